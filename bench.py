@@ -1,0 +1,278 @@
+"""Benchmark of the DSA layer on one MI355X: prefill tokens/s at L = 131072, k = 2048
+(lightning indexer + top-k + sparse MLA), plus decode microseconds per step for 64
+sequences of 131072 cached tokens.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_128k]
+                    [--decode-workload decode_64x128k | none] [--no-cpu-baseline]
+
+Prints ONE JSON line.  Inputs are seeded synthetic tensors from the generator shared with
+the tests, already resident in HBM when timing starts.  A step is one call of
+dsa_forward_prefill over the whole sequence.  The roofline object describes the slower of
+the two prefill stages, timed separately with HIP events on the stream they run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA prefill tokens/s at L=128K, k=2048 (indexer+top-k+sparse MLA); decode µs/step"
+PEAK_FP8 = 5.0e15      # MI355X dense FP8 MFMA, flop/s
+PEAK_BF16 = 2.5e15     # MI355X dense BF16 MFMA, flop/s
+PEAK_HBM = 8.0e12      # MI355X HBM3E, bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------ inputs
+
+def prefill_inputs_on_gpu(cfg, torch):
+    """Stream the generator's row blocks straight into device tensors."""
+    from sparse_attention_long_02_amd import synth as S
+    L = cfg.L
+    dev = "cuda"
+    qi = torch.empty((L, cfg.H_I, cfg.d_I), dtype=torch.uint8, device=dev)
+    qs = torch.empty((L, cfg.H_I), dtype=torch.float32, device=dev)
+    w = torch.empty((L, cfg.H_I), dtype=torch.float32, device=dev)
+    q = torch.empty((L, cfg.H, cfg.d_qk), dtype=torch.bfloat16, device=dev)
+    step = 8192
+    t0 = time.time()
+    for r0 in range(0, L, step):
+        rows = np.arange(r0, min(L, r0 + step))
+        a, b, c, d = S.query_rows(cfg, rows)
+        sl = slice(r0, r0 + len(rows))
+        qi[sl].copy_(torch.from_numpy(a))
+        qs[sl].copy_(torch.from_numpy(b))
+        w[sl].copy_(torch.from_numpy(c))
+        q[sl].copy_(torch.from_numpy(d.view(np.int16)).view(torch.bfloat16))
+    ki, ks, kv, _ = S.key_rows(cfg)
+    ki = torch.from_numpy(ki).to(dev)
+    ks = torch.from_numpy(ks).to(dev)
+    kv = torch.from_numpy(kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    torch.cuda.synchronize()
+    log(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s")
+    return qi, qs, ki, ks, w, q, kv
+
+
+def decode_inputs_on_gpu(cfg, torch):
+    from sparse_attention_long_02_amd import synth as S
+    dev = "cuda"
+    t0 = time.time()
+    inp = S.make_decode(cfg, with_keys=False)
+    kc = torch.empty((cfg.batch, cfg.L, cfg.d_I), dtype=torch.uint8, device=dev)
+    kcs = torch.empty((cfg.batch, cfg.L), dtype=torch.float32, device=dev)
+    kvc = torch.empty((cfg.batch, cfg.L, cfg.d_qk), dtype=torch.bfloat16, device=dev)
+    for b in range(cfg.batch):
+        ki, ks, kv, _ = S.key_rows(cfg, b)
+        kc[b].copy_(torch.from_numpy(ki))
+        kcs[b].copy_(torch.from_numpy(ks))
+        kvc[b].copy_(torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16))
+    qi = torch.from_numpy(inp.qi).to(dev)
+    qs = torch.from_numpy(inp.q_scale).to(dev)
+    w = torch.from_numpy(inp.w).to(dev)
+    q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    ctx = torch.full((cfg.batch,), cfg.L, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s")
+    return ctx, qi, qs, w, kc, kcs, q, kvc
+
+
+# ------------------------------------------------------------------------------ work model
+
+def indexer_flops(L, H_I, d_I):
+    """sum over tokens t of (t+1) * H_I * d_I * 2 (every causal pair, all heads)."""
+    return L * (L + 1) / 2 * H_I * d_I * 2
+
+
+def kept_keys(L, k):
+    """sum over tokens t of min(t+1, k)."""
+    m = min(L, k)
+    return m * (m + 1) / 2 + max(0, L - k) * k
+
+
+def gather_bytes(L, k, d_qk):
+    return kept_keys(L, k) * d_qk * 2
+
+
+def mla_flops(L, k, H, d_qk, d_v):
+    return kept_keys(L, k) * H * (d_qk + d_v) * 2
+
+
+# ------------------------------------------------------------------------------ timing
+
+def time_calls(torch, fn, reps):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / reps
+
+
+def cpu_baseline(cfg, budget_s=20.0):
+    """The float64 oracle on a bounded sample of query rows of the same workload."""
+    import oracle as O
+    from sparse_attention_long_02_amd import synth as S
+    rng = np.random.default_rng(1234)
+    L, k = cfg.L, cfg.k
+    fixed = [0, 1, k - 2, k - 1, k, L - 1]
+    t0 = time.time()
+    ki, ks, kv, v = S.key_rows(cfg)
+    khat = O.dequant(ki, ks)
+    kvf = O.bf16_to_f64(kv)
+    vf = kvf[:, : cfg.d_v]
+    setup = time.time() - t0
+    rows = np.array(sorted(set(fixed) | set(int(x) for x in rng.integers(0, L, 96))))
+    rand = set(int(x) for x in rng.integers(0, L, 96))
+    qi, qs, w, q = S.query_rows(cfg, rows)
+    qhat = O.dequant(qi, qs)
+    qf = O.bf16_to_f64(q)
+    order = [int(i) for i in rng.permutation(len(rows))]
+    spent, t_row = 0.0, []
+    for j in order:
+        t = int(rows[j])
+        if t in fixed and t not in rand:
+            continue
+        a = time.time()
+        O.dsa_rows(qhat[j:j + 1], w[j:j + 1].astype(np.float64), khat, qf[j:j + 1], kvf, vf,
+                   np.array([t]), k, cfg.sm_scale)
+        dt = time.time() - a
+        spent += dt
+        t_row.append(dt)
+        if spent >= budget_s:
+            break
+    mean = float(np.mean(t_row)) if t_row else float("nan")
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 1.0 / mean, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(t_row)} query rows drawn uniformly from the {L}-token sequence, "
+                      f"float64 numpy oracle, whole layer (indexer, top-k, attention) per row; "
+                      f"tokens/s = 1 / mean row time ({spent:.1f}s of CPU work, key setup {setup:.1f}s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill_128k")
+    ap.add_argument("--decode-workload", default="decode_64x128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the DSA layer on a single MI355X "
+              "(the multi-GPU sharding is described in the design notes, not implemented).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_long_02_amd import dsa
+    from sparse_attention_long_02_amd import synth as S
+
+    cfg = S.CONFIGS[args.workload]
+    assert not cfg.decode and not cfg.fp32
+    dsa.lib()
+    qi, qs, ki, ks, w, q, kv = prefill_inputs_on_gpu(cfg, torch)
+    L, k = cfg.L, cfg.k
+    idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((L, cfg.H, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((L, cfg.H), dtype=torch.float32, device="cuda")
+    ws_n = dsa.workspace_size(dsa.DSA_OP_PREFILL, 1, L, L, cfg.H, cfg.d_v, k, dsa.DSA_BF16)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
+
+    def step():
+        dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, k, cfg.sm_scale, cfg.d_v, idx=idx, out=out, lse=lse, ws=ws)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step (wall {wall:.2f}s)")
+
+    # the two stages alone (same stream, HIP events)
+    t_sel = time_calls(torch, lambda: dsa.select_prefill(qi, qs, ki, ks, w, k, idx=idx), args.stage_reps)
+    t_mla = time_calls(torch, lambda: dsa.sparse_mla(q, kv, idx, cfg.sm_scale, cfg.d_v), args.stage_reps)
+    log(f"[bench] stages: select {t_sel * 1e3:.3f} ms, sparse MLA {t_mla * 1e3:.3f} ms")
+    f_idx = indexer_flops(L, cfg.H_I, cfg.d_I)
+    g_bytes = gather_bytes(L, k, cfg.d_qk)
+    f_mla = mla_flops(L, k, cfg.H, cfg.d_qk, cfg.d_v)
+    stages = {
+        "select": {"ms": t_sel * 1e3, "fp8_flop": f_idx, "mfma_frac": f_idx / t_sel / PEAK_FP8},
+        "sparse_mla": {"ms": t_mla * 1e3, "gather_bytes": g_bytes, "hbm_frac": g_bytes / t_mla / PEAK_HBM,
+                       "bf16_flop": f_mla, "mfma_frac": f_mla / t_mla / PEAK_BF16},
+    }
+    if t_sel >= t_mla:
+        a = f_idx / t_sel
+        roof = {"kernel": "prefill_idx_topk_kernel (FP8 indexer + streaming top-k)", "bound": "mfma",
+                "achieved": a / 1e12, "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s", "frac": a / PEAK_FP8,
+                "traffic": None}
+    else:
+        a = g_bytes / t_mla
+        roof = {"kernel": "sparse_mla_bf16_kernel (gathered KV rows)", "bound": "hbm",
+                "achieved": a / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": a / PEAK_HBM,
+                "traffic": None}
+
+    decode = None
+    if args.decode_workload != "none":
+        del out, lse, q
+        torch.cuda.empty_cache()
+        dcfg = S.CONFIGS[args.decode_workload]
+        ctx, dqi, dqs, dw, kc, kcs, dq, kvc = decode_inputs_on_gpu(dcfg, torch)
+        ws_d = torch.empty(dsa.workspace_size(dsa.DSA_OP_DECODE, dcfg.batch, 1, dcfg.L, dcfg.H, dcfg.d_v, dcfg.k,
+                                              dsa.DSA_BF16), dtype=torch.uint8, device="cuda")
+        didx = torch.empty((dcfg.batch, dcfg.k), dtype=torch.int32, device="cuda")
+        dout = torch.empty((dcfg.batch, dcfg.H, dcfg.d_v), dtype=torch.bfloat16, device="cuda")
+        dlse = torch.empty((dcfg.batch, dcfg.H), dtype=torch.float32, device="cuda")
+
+        def dstep():
+            dsa.forward_decode(ctx, dqi, dqs, dw, kc, kcs, dq, kvc, dcfg.k, dcfg.sm_scale, dcfg.d_v, idx=didx,
+                               out=dout, lse=dlse, ws=ws_d)
+        for _ in range(args.warmup):
+            dstep()
+        t_dec = time_calls(torch, dstep, max(args.steps, 10))
+        icache = dcfg.batch * dcfg.L * (dcfg.d_I + 4)
+        log(f"[bench] decode {t_dec * 1e6:.1f} us/step")
+        decode = {"workload": dcfg.name, "us_per_step": t_dec * 1e6, "batch": dcfg.batch, "ctx": dcfg.L,
+                  "index_cache_bytes": icache, "index_cache_hbm_frac": icache / t_dec / PEAK_HBM}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} tokens/s on {cpu['cores']} cores")
+
+    value = L / (ms_step / 1e3)
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "seq_len": L, "batch": 1, "topk": k, "heads": cfg.H,
+                   "d_qk": cfg.d_qk, "d_v": cfg.d_v, "indexer_heads": cfg.H_I, "indexer_dim": cfg.d_I,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "stages": stages, "decode": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

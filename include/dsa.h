@@ -1,0 +1,208 @@
+/*
+ * dsa.h -- C ABI of libdsa: DeepSeek Sparse Attention (DSA) forward for one layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * DSA has three stages (described on the pages this library follows):
+ *   1. lightning indexer: a multi-head ReLU scorer, run in FP8, that gives every query a
+ *      score for each of its preceding tokens
+ *      ("DeepSeek-V3.2-Exp 技术报告解读" (53ai.com), section 创新架构; WeChat explainer on
+ *      juhe.plus, section 第一步：Lightning Indexer);
+ *   2. fine-grained token selection: keep the top-k keys per query, k = 2048
+ *      (juhe.plus explainer, section 第二步：Fine-grained Token Selection; paperbridge.wiki
+ *      summary, section DeepSeek Sparse Attention);
+ *   3. attention over the kept keys only, MLA in MQA mode: all query heads share one
+ *      latent key-value row (53ai.com, section 创新架构 and Figure 1).
+ *
+ * Definitions used by every entry point
+ * -------------------------------------
+ *   index score   I[t,s] = sum_j w[t,j] * ReLU( (q8[t,j,:]*q_scale[t,j]) . (k8[s,:]*k_scale[s]) )
+ *                 for keys s <= pos(t) ("preceding tokens" includes the token itself).
+ *   selection     S_t = the min(k, pos(t)+1) keys s <= pos(t) ranked highest by
+ *                 (I desc, s asc): ties go to the lower key index.  Written as int32 in
+ *                 ascending key order, padded with -1.
+ *   attention     z_s = sm_scale * q[t,h,:] . kv[s,:]      (s in S_t, every head h)
+ *                 O[t,h,:] = sum_s softmax(z)_s * V[s,:],  lse[t,h] = ln sum_s exp(z_s)
+ *                 V = kv[:, 0:d_v] (the latent part of the row) unless a separate v is
+ *                 given.  An empty S_t gives O = 0, lse = -inf.
+ *
+ * Conventions
+ * -----------
+ *   * Every pointer argument is a DEVICE pointer unless stated otherwise; all arrays
+ *     are dense row-major with the innermost dimension contiguous (no strides except
+ *     the documented ld_scores).  The caller owns every buffer, including the
+ *     workspace (size it with dsa_workspace_size); the library allocates nothing and
+ *     keeps no pointer after a call returns.
+ *   * All work is enqueued on `stream` (0 = the null stream); calls return before the
+ *     GPU finishes.  Buffers must stay alive until the stream has passed the work.
+ *   * Return value: DSA_OK (0) or a negative dsa_status.  Arguments are validated on
+ *     the host before anything is enqueued; a failing call enqueues nothing, except
+ *     DSA_ERR_HIP, which reports a launch failure.  dsa_last_error() gives a message
+ *     for the calling thread's last failure.  No exception or abort crosses the ABI.
+ *   * Device-side preconditions that are not checked: indices in idx are -1 or in
+ *     [0, n_k); positions fit the key arrays; no NaN in the inputs.
+ *   * dtype codes: DSA_F32 (fp32 everywhere), DSA_FP8_E4M3 (indexer operands are OCP
+ *     FP8 E4M3FN codes, one byte each, with fp32 scales), DSA_BF16 (attention operands
+ *     and output in bfloat16).
+ *   * Supported shapes.  dtype DSA_F32: any H_I <= 64, d_I <= 256, H <= 64,
+ *     d_qk <= 256, d_v <= 256, k <= 4096.  FP8 indexer: H_I = 64, d_I = 128.  BF16
+ *     attention: H = 128, d_qk = 576, d_v = 512 with V = kv[:, 0:512].  Top-k:
+ *     k <= 2048 (fp8/bf16 path) and n_k <= 262144.  Others: DSA_ERR_UNSUPPORTED.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
+
+#define DSA_ABI_VERSION 1
+
+enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1, /* null pointer, bad dimension, misaligned pointer */
+  DSA_ERR_UNSUPPORTED = -2, /* valid request without a kernel (dtype or shape) */
+  DSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than dsa_workspace_size() */
+  DSA_ERR_HIP = -4          /* the HIP runtime reported an error */
+};
+
+enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 };
+
+enum dsa_op { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2,
+              DSA_OP_PREFILL = 3, DSA_OP_DECODE = 4, DSA_OP_SELECT = 5 };
+
+/* DSA_ABI_VERSION of the loaded library. */
+int dsa_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* dsa_status_string(int status);
+
+/* Message of the calling thread's most recent failing call ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Workspace bytes an entry point needs (0 if none).  op is a dsa_op; the other
+ * arguments are the ones the entry point takes (unused ones may be 0).  For
+ * DSA_OP_PREFILL pass the attention dtype (DSA_F32 selects the fp32 path, whose
+ * selection ranks materialised scores); for DSA_OP_SELECT pass the indexer dtype.
+ */
+size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32_t H,
+                          int32_t d_v, int32_t k, int32_t dtype);
+
+/*
+ * dsa_indexer -- lightning-indexer scores for a range of query rows (stage 1).
+ *
+ *   q_idx   [B, n_q, H_I, d_I]  FP8 codes (DSA_FP8_E4M3) or float (DSA_F32)
+ *   q_scale [B, n_q, H_I]       fp32 scale of each query head row
+ *   k_idx   [B, n_k, d_I]       FP8 codes or float
+ *   k_scale [B, n_k]            fp32 scale of each key row
+ *   w       [B, n_q, H_I]       fp32 head weights
+ *   q_pos   [B] int32 or NULL   position of query row 0 of sequence b (NULL: all 0);
+ *                               row r of sequence b sits at pos = q_pos[b] + r
+ *   rows    row_begin .. row_begin + n_rows - 1 of each sequence are scored
+ *   scores  [B, n_rows, ld_scores] fp32 output, ld_scores >= n_k: scores[b][i][s] =
+ *           I[row_begin+i, s] for s <= pos, -inf for pos < s < n_k; columns >= n_k
+ *           are not written.
+ * Scores are bit-identical to the ones dsa_forward_prefill / dsa_forward_decode
+ * select from.  Needs no workspace.
+ */
+int dsa_indexer(const void* q_idx, const float* q_scale, const void* k_idx,
+                const float* k_scale, const float* w, int64_t B, int64_t n_q, int64_t n_k,
+                const int32_t* q_pos, int32_t H_I, int32_t d_I, int32_t dtype,
+                int64_t row_begin, int64_t n_rows, float* scores, int64_t ld_scores,
+                dsa_stream_t stream);
+
+/*
+ * dsa_topk -- fine-grained token selection over materialised scores (stage 2).
+ *
+ *   scores [B, n_rows, ld_scores] fp32; row i of sequence b belongs to the query at
+ *          pos = q_pos[b] + row_begin + i (q_pos NULL: 0) and only columns
+ *          s <= min(pos, n_k - 1) are read.
+ *   idx    [B, n_rows, k] int32 output: S_t in ascending order, -1 padded.
+ * The result depends only on the fp32 values (+0.0 and -0.0 are equal); it is
+ * bit-exact against a full sort by (score desc, index asc).  Workspace:
+ * dsa_workspace_size(DSA_OP_TOPK, ...) (currently 0; pass NULL, 0).
+ */
+int dsa_topk(const float* scores, int64_t ld_scores, int64_t B, int64_t n_rows, int64_t n_k,
+             const int32_t* q_pos, int64_t row_begin, int32_t k, int32_t* idx, void* ws,
+             size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_sparse_mla -- attention of every query head over its selected keys (stage 3).
+ *
+ *   q    [B, n_q, H, d_qk]   bf16 or fp32 (dtype)
+ *   kv   [B, n_k, d_qk]      shared key/latent rows (MQA)
+ *   v    [B, n_k, d_v] or NULL: NULL means V = kv[:, :, 0:d_v]
+ *   idx  [B, n_q, k] int32   selected keys (-1 entries are ignored, anywhere)
+ *   out  [B, n_q, H, d_v]    output, same dtype as q
+ *   lse  [B, n_q, H] fp32 or NULL: natural-log sum-exp of the scaled logits
+ * Workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA, B, n_q, n_k, H, d_v, k, dtype).
+ */
+int dsa_sparse_mla(const void* q, const void* kv, const void* v, const int32_t* idx,
+                   int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_qk, int32_t d_v,
+                   int32_t k, float sm_scale, int32_t dtype, void* out, float* lse, void* ws,
+                   size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_select_prefill -- stages 1 and 2 for one sequence of L tokens (query t at position
+ * t): lightning-indexer scores feed a per-row streaming top-k on chip, so the L x L
+ * score matrix is never stored (FP8 path).  The fp32 path ranks a materialised score
+ * matrix held in the workspace.
+ *
+ *   q_idx [L, H_I, d_I], q_scale [L, H_I], k_idx [L, d_I], k_scale [L], w [L, H_I]
+ *   idx   [L, k] int32 output, ascending, -1 padded
+ * idx_dtype: DSA_FP8_E4M3 (k <= 2048) or DSA_F32.  Workspace:
+ * dsa_workspace_size(DSA_OP_SELECT, 1, L, L, 0, 0, k, idx_dtype).
+ */
+int dsa_select_prefill(const void* q_idx, const float* q_scale, const void* k_idx,
+                       const float* k_scale, const float* w, int64_t L, int32_t H_I, int32_t d_I,
+                       int32_t k, int32_t idx_dtype, int32_t* idx, void* ws, size_t ws_bytes,
+                       dsa_stream_t stream);
+
+/*
+ * dsa_forward_prefill -- the whole layer for one sequence of L tokens, query t at
+ * position t: indexer -> top-k -> sparse attention.  The L x L score matrix is never
+ * stored: the indexer feeds a per-row streaming top-k on chip.
+ *
+ *   q_idx [L, H_I, d_I], q_scale [L, H_I], k_idx [L, d_I], k_scale [L], w [L, H_I]
+ *   q [L, H, d_qk], kv [L, d_qk], v [L, d_v] or NULL
+ *   idx [L, k] int32 (output: the selection), out [L, H, d_v], lse [L, H] or NULL
+ * idx_dtype: DSA_FP8_E4M3 or DSA_F32; attn_dtype: DSA_BF16 or DSA_F32.
+ * Workspace: dsa_workspace_size(DSA_OP_PREFILL, 1, L, L, H, d_v, k, attn_dtype).
+ */
+int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_idx,
+                        const float* k_scale, const float* w, const void* q, const void* kv,
+                        const void* v, int64_t L, int32_t H_I, int32_t d_I, int32_t H,
+                        int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
+                        int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out,
+                        float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_forward_decode -- the whole layer for B sequences with one new token each.
+ * Sequence b holds ctx_len[b] cached rows (1 <= ctx_len[b] <= n_k_max, device int32);
+ * its query sits at position ctx_len[b] - 1 (its own row is already in the caches)
+ * and sees every cached row.
+ *
+ *   q_idx [B, H_I, d_I], q_scale [B, H_I], w [B, H_I]
+ *   k_cache [B, n_k_max, d_I], k_cache_scale [B, n_k_max]
+ *   q [B, H, d_qk], kv_cache [B, n_k_max, d_qk], v_cache [B, n_k_max, d_v] or NULL
+ *   idx [B, k] int32 (output), out [B, H, d_v], lse [B, H] or NULL
+ * Workspace: dsa_workspace_size(DSA_OP_DECODE, B, 1, n_k_max, H, d_v, k, attn_dtype).
+ */
+int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx,
+                       const float* q_scale, const float* w, const void* k_cache,
+                       const float* k_cache_scale, const void* q, const void* kv_cache,
+                       const void* v_cache, int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk,
+                       int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype,
+                       int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                       size_t ws_bytes, dsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

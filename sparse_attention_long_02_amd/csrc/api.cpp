@@ -1,0 +1,259 @@
+// C ABI of libdsa: argument validation, workspace sizing and kernel dispatch.
+// Every check happens on the host before anything is enqueued; no exception leaves.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dsa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                   \
+  do {                                                       \
+    if (!(cond)) return fail(DSA_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+#define SUPPORT(cond, ...)                                   \
+  do {                                                       \
+    if (!(cond)) return fail(DSA_ERR_UNSUPPORTED, __VA_ARGS__); \
+  } while (0)
+
+int check_indexer_shape(int32_t H_I, int32_t d_I, int32_t dtype) {
+  REQUIRE(H_I > 0 && d_I > 0, "H_I and d_I must be positive (got %d, %d)", H_I, d_I);
+  if (dtype == DSA_FP8_E4M3) {
+    SUPPORT(H_I == 64 && d_I == 128, "FP8 indexer needs H_I=64, d_I=128 (got %d, %d)", H_I, d_I);
+  } else if (dtype == DSA_F32) {
+    SUPPORT(H_I <= 64 && d_I <= 256, "fp32 indexer needs H_I<=64, d_I<=256 (got %d, %d)", H_I, d_I);
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer dtype %d is not DSA_FP8_E4M3 or DSA_F32", dtype);
+  }
+  return DSA_OK;
+}
+
+int check_attn_shape(int32_t H, int32_t d_qk, int32_t d_v, int32_t k, int32_t dtype, bool has_v) {
+  REQUIRE(H > 0 && d_qk > 0 && d_v > 0 && k > 0, "H, d_qk, d_v, k must be positive");
+  REQUIRE(has_v || d_v <= d_qk, "d_v (%d) exceeds d_qk (%d) with V = kv[:, :d_v]", d_v, d_qk);
+  if (dtype == DSA_BF16) {
+    SUPPORT(H == 128 && d_qk == 576 && d_v == 512 && !has_v,
+            "bf16 attention needs H=128, d_qk=576, d_v=512, V = kv[:, :512]");
+    SUPPORT(k % 32 == 0 && k <= 2048, "bf16 attention needs k a multiple of 32, <= 2048 (got %d)", k);
+  } else if (dtype == DSA_F32) {
+    SUPPORT(H <= 64 && d_qk <= 256 && d_v <= 256 && k <= 4096,
+            "fp32 attention needs H<=64, d_qk<=256, d_v<=256, k<=4096");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "attention dtype %d is not DSA_BF16 or DSA_F32", dtype);
+  }
+  return DSA_OK;
+}
+
+size_t decode_scores_bytes(int64_t B, int64_t n_k) { return (size_t)B * n_k * sizeof(float); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: no kernel for this dtype or shape";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP runtime error";
+    default: return "unknown dsa status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_v,
+                          int32_t k, int32_t dtype) {
+  if (B <= 0 || n_q < 0 || n_k < 0 || H <= 0 || d_v <= 0 || k <= 0) return 0;
+  switch (op) {
+    case DSA_OP_SPARSE_MLA:
+      return dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, dtype);
+    case DSA_OP_PREFILL:
+      if (dtype == DSA_F32)  // fp32 path ranks materialised scores
+        return align256((size_t)n_q * n_k * sizeof(float)) + dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
+      return dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
+    case DSA_OP_SELECT:
+      return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : 0;
+    case DSA_OP_DECODE:
+      return align256(decode_scores_bytes(B, n_k)) + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
+    default:
+      return 0;
+  }
+}
+
+int dsa_indexer(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                const float* w, int64_t B, int64_t n_q, int64_t n_k, const int32_t* q_pos, int32_t H_I,
+                int32_t d_I, int32_t dtype, int64_t row_begin, int64_t n_rows, float* scores,
+                int64_t ld_scores, dsa_stream_t stream) {
+  REQUIRE(q_idx && q_scale && k_idx && k_scale && w && scores, "null pointer argument");
+  REQUIRE(B > 0 && n_q > 0 && n_k > 0, "B, n_q, n_k must be positive");
+  REQUIRE(B <= 65535, "B must be <= 65535");
+  REQUIRE(row_begin >= 0 && n_rows > 0 && row_begin + n_rows <= n_q, "row range outside [0, n_q)");
+  REQUIRE(n_rows <= 65535 || (n_rows + 3) / 4 <= 2147483647LL, "too many rows");
+  REQUIRE(ld_scores >= n_k, "ld_scores (%lld) < n_k (%lld)", (long long)ld_scores, (long long)n_k);
+  int st = check_indexer_shape(H_I, d_I, dtype);
+  if (st) return st;
+  if (dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_idx), "FP8 operands must be 16-byte aligned");
+  if (dtype == DSA_F32 || n_rows * B <= 512) REQUIRE(n_rows <= 65535, "n_rows must be <= 65535 here");
+  dsa::IndexerArgs a{q_idx, q_scale, k_idx, k_scale, w, B, n_q, n_k, q_pos, 0, H_I, d_I, dtype,
+                     row_begin, n_rows, scores, ld_scores};
+  return hip_status(dsa::launch_indexer(a, (hipStream_t)stream), "dsa_indexer launch");
+}
+
+int dsa_topk(const float* scores, int64_t ld_scores, int64_t B, int64_t n_rows, int64_t n_k,
+             const int32_t* q_pos, int64_t row_begin, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+             dsa_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  REQUIRE(scores && idx, "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_rows > 0 && n_k > 0 && k > 0, "B, n_rows, n_k, k must be positive");
+  REQUIRE(n_rows <= 2147483647LL, "too many rows");
+  REQUIRE(row_begin >= 0, "row_begin must be >= 0");
+  REQUIRE(ld_scores >= n_k, "ld_scores < n_k");
+  SUPPORT(n_k <= dsa::TOPK_MAX_N, "dsa_topk supports n_k <= %lld", (long long)dsa::TOPK_MAX_N);
+  SUPPORT(k <= 65536, "dsa_topk supports k <= 65536");
+  dsa::TopkArgs a{scores, ld_scores, B, n_rows, n_k, q_pos, 0, row_begin, k, idx};
+  return hip_status(dsa::launch_topk(a, (hipStream_t)stream), "dsa_topk launch");
+}
+
+int dsa_sparse_mla(const void* q, const void* kv, const void* v, const int32_t* idx, int64_t B, int64_t n_q,
+                   int64_t n_k, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t dtype,
+                   void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(q && kv && idx && out, "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k > 0, "B, n_q, n_k must be positive");
+  int st = check_attn_shape(H, d_qk, d_v, k, dtype, v != nullptr);
+  if (st) return st;
+  if (dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out), "bf16 operands must be 16-byte aligned");
+  REQUIRE(n_q * H <= 2147483647LL, "n_q * H too large");
+  const size_t need = dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, dtype);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_sparse_mla needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  dsa::MlaArgs a{q, kv, v, idx, B, n_q, n_k, H, d_qk, d_v, k, sm_scale, dtype, out, lse, ws, ws_bytes};
+  return hip_status(dsa::launch_sparse_mla(a, (hipStream_t)stream), "dsa_sparse_mla launch");
+}
+
+static int select_prefill(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                          const float* w, int64_t L, int32_t H_I, int32_t d_I, int32_t k, int32_t idx_dtype,
+                          int32_t* idx, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (idx_dtype == DSA_FP8_E4M3) {
+    SUPPORT(k <= 2048, "fused selection keeps at most 2048 keys (k = %d)", k);
+    dsa::PrefillTopkArgs pa{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, L, k, idx};
+    return hip_status(dsa::launch_prefill_topk(pa, s), "prefill indexer/top-k launch");
+  }
+  SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
+  const size_t need = align256((size_t)L * L * sizeof(float));
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "fp32 selection needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  float* scores = (float*)ws;
+  dsa::IndexerArgs ia{q_idx, q_scale, k_idx, k_scale, w, 1, L, L, nullptr, 0, H_I, d_I, idx_dtype, 0, L, scores, L};
+  int st = hip_status(dsa::launch_indexer(ia, s), "prefill indexer launch");
+  if (st) return st;
+  dsa::TopkArgs ta{scores, L, 1, L, L, nullptr, 0, 0, k, idx};
+  return hip_status(dsa::launch_topk(ta, s), "prefill top-k launch");
+}
+
+int dsa_select_prefill(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                       const float* w, int64_t L, int32_t H_I, int32_t d_I, int32_t k, int32_t idx_dtype,
+                       int32_t* idx, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(q_idx && q_scale && k_idx && k_scale && w && idx, "null pointer argument");
+  REQUIRE(L > 0 && L <= 2147483647LL, "L must be in [1, 2^31)");
+  REQUIRE(k > 0, "k must be positive");
+  int st = check_indexer_shape(H_I, d_I, idx_dtype);
+  if (st) return st;
+  if (idx_dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_idx), "FP8 operands must be 16-byte aligned");
+  return select_prefill(q_idx, q_scale, k_idx, k_scale, w, L, H_I, d_I, k, idx_dtype, idx, ws, ws_bytes,
+                        (hipStream_t)stream);
+}
+
+int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                        const float* w, const void* q, const void* kv, const void* v, int64_t L, int32_t H_I,
+                        int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
+                        int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                        size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(q_idx && q_scale && k_idx && k_scale && w && q && kv && idx && out, "null pointer argument");
+  REQUIRE(L > 0 && L <= 2147483647LL, "L must be in [1, 2^31)");
+  int st = check_indexer_shape(H_I, d_I, idx_dtype);
+  if (st) return st;
+  st = check_attn_shape(H, d_qk, d_v, k, attn_dtype, v != nullptr);
+  if (st) return st;
+  if (idx_dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_idx), "FP8 operands must be 16-byte aligned");
+  if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out), "bf16 operands must be 16-byte aligned");
+  SUPPORT(idx_dtype == attn_dtype || (idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16),
+          "prefill pairs an FP8 indexer with bf16 attention, or fp32 with fp32");
+  SUPPORT(idx_dtype != DSA_FP8_E4M3 || k <= 2048, "fused selection keeps at most 2048 keys");
+  const bool f32 = idx_dtype == DSA_F32;
+  if (f32) SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
+  const size_t s_bytes = f32 ? align256((size_t)L * L * sizeof(float)) : 0;
+  const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(1, L, H, d_v, k, attn_dtype);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_forward_prefill needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  st = select_prefill(q_idx, q_scale, k_idx, k_scale, w, L, H_I, d_I, k, idx_dtype, idx, ws, s_bytes, s);
+  if (st) return st;
+  dsa::MlaArgs a{q, kv, v, idx, 1, L, L, H, d_qk, d_v, k, sm_scale, attn_dtype, out, lse,
+                 (char*)ws + s_bytes, ws_bytes - s_bytes};
+  return hip_status(dsa::launch_sparse_mla(a, s), "prefill sparse attention launch");
+}
+
+int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx, const float* q_scale,
+                       const float* w, const void* k_cache, const float* k_cache_scale, const void* q,
+                       const void* kv_cache, const void* v_cache, int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk,
+                       int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype, int32_t* idx,
+                       void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(ctx_len && q_idx && q_scale && w && k_cache && k_cache_scale && q && kv_cache && idx && out,
+          "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_k_max > 0, "B in [1, 65535] and n_k_max > 0 required");
+  int st = check_indexer_shape(H_I, d_I, idx_dtype);
+  if (st) return st;
+  st = check_attn_shape(H, d_qk, d_v, k, attn_dtype, v_cache != nullptr);
+  if (st) return st;
+  SUPPORT(n_k_max <= dsa::TOPK_MAX_N, "decode supports n_k_max <= %lld", (long long)dsa::TOPK_MAX_N);
+  if (idx_dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_cache), "FP8 operands must be 16-byte aligned");
+  if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv_cache) && aligned16(out), "bf16 operands must be 16-byte aligned");
+  const size_t s_bytes = align256(decode_scores_bytes(B, n_k_max));
+  const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, attn_dtype);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "dsa_forward_decode needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  float* scores = (float*)ws;
+  // the query of sequence b is its row 0, at position ctx_len[b] - 1
+  dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, H_I, d_I,
+                      idx_dtype, 0, 1, scores, n_k_max};
+  st = hip_status(dsa::launch_indexer(ia, s), "decode indexer launch");
+  if (st) return st;
+  dsa::TopkArgs ta{scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx};
+  st = hip_status(dsa::launch_topk(ta, s), "decode top-k launch");
+  if (st) return st;
+  dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, 1, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
+                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes};
+  return hip_status(dsa::launch_sparse_mla(a, s), "decode sparse attention launch");
+}
+
+}  // extern "C"

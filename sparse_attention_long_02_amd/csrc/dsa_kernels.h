@@ -1,0 +1,71 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+struct IndexerArgs {
+  const void* q_idx;
+  const float* q_scale;
+  const void* k_idx;
+  const float* k_scale;
+  const float* w;
+  int64_t B, n_q, n_k;
+  const int32_t* q_pos;     // [B] or null; position of row r = q_pos[b] + pos_offset + r
+  int64_t pos_offset;
+  int32_t H_I, d_I, dtype;
+  int64_t row_begin, n_rows;
+  float* scores;
+  int64_t ld_scores;
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
+
+struct TopkArgs {
+  const float* scores;
+  int64_t ld_scores, B, n_rows, n_k;
+  const int32_t* q_pos;     // position of row i = q_pos[b] + pos_offset + row_begin + i
+  int64_t pos_offset;
+  int64_t row_begin;
+  int32_t k;
+  int32_t* idx;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+constexpr int64_t TOPK_MAX_N = 262144;
+
+struct MlaArgs {
+  const void* q;
+  const void* kv;
+  const void* v;  // may be null (V = kv[:, :d_v])
+  const int32_t* idx;
+  int64_t B, n_q, n_k;
+  int32_t H, d_qk, d_v, k;
+  float sm_scale;
+  int32_t dtype;
+  void* out;
+  float* lse;
+  void* ws;
+  size_t ws_bytes;
+};
+hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
+// workspace of the bf16 kernel when it splits each query's keys over several blocks
+size_t sparse_mla_ws_bytes(int64_t B, int64_t n_q, int32_t H, int32_t d_v, int32_t k, int32_t dtype);
+int sparse_mla_splits(int64_t B, int64_t n_q, int32_t k, int32_t dtype);
+
+// fused FP8 indexer + streaming top-k for the prefill rows of one sequence (q_pos = 0)
+struct PrefillTopkArgs {
+  const uint8_t* q8;
+  const float* qs;
+  const uint8_t* k8;
+  const float* ks;
+  const float* w;
+  int64_t L;
+  int32_t k;
+  int32_t* idx;
+};
+hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,211 @@
+"""Python binding of libdsa (the C ABI in include/dsa.h): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, passes their device
+pointers, sizes and torch's current HIP stream to the library, and returns the output
+tensors it allocated.  All arithmetic runs in the library's HIP kernels; there is no
+fallback of any kind: if libdsa.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_PREFILL, DSA_OP_DECODE, DSA_OP_SELECT = range(6)
+
+_i64, _i32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "dsa_abi_version": (ctypes.c_int, []),
+    "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32, _i32, _i32, _i32]),
+    "dsa_indexer": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i32, _i32,
+                                   _i64, _i64, _vp, _i64, _vp]),
+    "dsa_topk": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i32, _vp, _vp, _sz, _vp]),
+    "dsa_sparse_mla": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
+                                      _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "dsa_select_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+                                          _sz, _vp]),
+    "dsa_forward_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                           _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp,
+                                           _vp, _sz, _vp]),
+    "dsa_forward_decode": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
+                                          _vp, _vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_long_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != DSA_OK:
+        raise DSAError(status, lib().dsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libdsa takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libdsa takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _idx_dtype(t: torch.Tensor) -> int:
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_FP8_E4M3
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"indexer operands must be FP8 codes (uint8 / float8_e4m3fn) or float32, got {t.dtype}")
+
+
+def _attn_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"attention operands must be bfloat16 or float32, got {t.dtype}")
+
+
+def workspace_size(op: int, B: int, n_q: int, n_k: int, H: int, d_v: int, k: int, dtype: int) -> int:
+    return int(lib().dsa_workspace_size(op, B, n_q, n_k, H, d_v, k, dtype))
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def indexer(q_idx, q_scale, k_idx, k_scale, w, q_pos=None, row_begin: int = 0,
+            n_rows: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index scores [B, n_rows, n_k] (fp32).  Shapes: q_idx [B, n_q, H_I, d_I] (or without
+    the leading B), q_scale/w [B, n_q, H_I], k_idx [B, n_k, d_I], k_scale [B, n_k]."""
+    squeeze = q_idx.dim() == 3
+    if squeeze:
+        q_idx, q_scale, w, k_idx, k_scale = (x.unsqueeze(0) for x in (q_idx, q_scale, w, k_idx, k_scale))
+    B, n_q, H_I, d_I = q_idx.shape
+    n_k = k_idx.shape[1]
+    n_rows = n_q - row_begin if n_rows is None else n_rows
+    if out is None:
+        out = torch.empty((B, n_rows, n_k), dtype=torch.float32, device=q_idx.device)
+    _check(lib().dsa_indexer(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), B, n_q, n_k,
+                             _ptr(q_pos), H_I, d_I, _idx_dtype(q_idx), row_begin, n_rows, _ptr(out),
+                             out.shape[-1], _stream()))
+    return out[0] if squeeze else out
+
+
+def topk(scores, k: int, q_pos=None, row_begin: int = 0, n_k: Optional[int] = None) -> torch.Tensor:
+    """Top-k selection of scores [B, n_rows, ld] (or [n_rows, ld]) -> idx int32 [.., n_rows, k]."""
+    squeeze = scores.dim() == 2
+    if squeeze:
+        scores = scores.unsqueeze(0)
+    B, n_rows, ld = scores.shape
+    n_k = ld if n_k is None else n_k
+    idx = torch.empty((B, n_rows, k), dtype=torch.int32, device=scores.device)
+    _check(lib().dsa_topk(_ptr(scores), ld, B, n_rows, n_k, _ptr(q_pos), row_begin, k, _ptr(idx), None, 0,
+                          _stream()))
+    return idx[0] if squeeze else idx
+
+
+def sparse_mla(q, kv, idx, sm_scale: float, d_v: int, v=None):
+    """Sparse MQA attention.  q [B, n_q, H, d_qk] (or without B), kv [B, n_k, d_qk],
+    idx [B, n_q, k] int32, v [B, n_k, d_v] or None (V = kv[..., :d_v]) -> (out, lse)."""
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, kv, idx = q.unsqueeze(0), kv.unsqueeze(0), idx.unsqueeze(0)
+        v = v.unsqueeze(0) if v is not None else None
+    B, n_q, H, d_qk = q.shape
+    n_k, k = kv.shape[1], idx.shape[-1]
+    dt = _attn_dtype(q)
+    out = torch.empty((B, n_q, H, d_v), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
+    ws = _workspace(workspace_size(DSA_OP_SPARSE_MLA, B, n_q, n_k, H, d_v, k, dt), q.device)
+    _check(lib().dsa_sparse_mla(_ptr(q), _ptr(kv), _ptr(v), _ptr(idx), B, n_q, n_k, H, d_qk, d_v, k,
+                                float(sm_scale), dt, _ptr(out), _ptr(lse), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream()))
+    return (out[0], lse[0]) if squeeze else (out, lse)
+
+
+def select_prefill(q_idx, q_scale, k_idx, k_scale, w, k: int, idx=None, ws=None) -> torch.Tensor:
+    """Stages 1-2 over one sequence: idx [L, k] int32 (scores never stored on the FP8 path)."""
+    L, H_I, d_I = q_idx.shape
+    it = _idx_dtype(q_idx)
+    idx = torch.empty((L, k), dtype=torch.int32, device=q_idx.device) if idx is None else idx
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_SELECT, 1, L, L, 1, 1, k, it), q_idx.device)
+    _check(lib().dsa_select_prefill(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), L, H_I,
+                                    d_I, k, it, _ptr(idx), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return idx
+
+
+def forward_prefill(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int, sm_scale: float, d_v: int, v=None,
+                    idx=None, out=None, lse=None, ws=None):
+    """Whole DSA layer over one sequence of L tokens -> (idx [L, k], out [L, H, d_v], lse [L, H])."""
+    L, H_I, d_I = q_idx.shape
+    _, H, d_qk = q.shape
+    it, at = _idx_dtype(q_idx), _attn_dtype(q)
+    dev = q.device
+    idx = torch.empty((L, k), dtype=torch.int32, device=dev) if idx is None else idx
+    out = torch.empty((L, H, d_v), dtype=q.dtype, device=dev) if out is None else out
+    lse = torch.empty((L, H), dtype=torch.float32, device=dev) if lse is None else lse
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_PREFILL, 1, L, L, H, d_v, k, at), dev)
+    _check(lib().dsa_forward_prefill(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w),
+                                     _ptr(q), _ptr(kv), _ptr(v), L, H_I, d_I, H, d_qk, d_v, k,
+                                     float(sm_scale), it, at, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream()))
+    return idx, out, lse
+
+
+def forward_decode(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cache, k: int, sm_scale: float,
+                   d_v: int, v_cache=None, idx=None, out=None, lse=None, ws=None):
+    """Whole DSA layer for B sequences with one new token each -> (idx [B, k], out, lse)."""
+    B, H_I, d_I = q_idx.shape
+    n_k_max = k_cache.shape[1]
+    _, H, d_qk = q.shape
+    it, at = _idx_dtype(q_idx), _attn_dtype(q)
+    dev = q.device
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev) if idx is None else idx
+    out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if lse is None else lse
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_DECODE, B, 1, n_k_max, H, d_v, k, at), dev)
+    _check(lib().dsa_forward_decode(B, _ptr(ctx_len), n_k_max, _ptr(q_idx), _ptr(q_scale), _ptr(w),
+                                    _ptr(k_cache), _ptr(k_cache_scale), _ptr(q), _ptr(kv_cache),
+                                    _ptr(v_cache), H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
+                                    _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream()))
+    return idx, out, lse

@@ -1,0 +1,53 @@
+"""Shared test helpers: move generator outputs to the GPU, tolerance checks."""
+import numpy as np
+import torch
+
+import oracle as O
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_attn(a, fp32):
+    return dev_f32(a) if fp32 else dev_bf16(a)
+
+
+def bf16_dev_to_f64(t):
+    return O.bf16_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def out_to_f64(t):
+    if t.dtype == torch.bfloat16:
+        return bf16_dev_to_f64(t)
+    return t.double().cpu().numpy()
+
+
+def indexer_inputs_dev(inp):
+    c = inp.cfg
+    if c.fp32:
+        return dev_f32(inp.qi), dev_f32(inp.q_scale), dev_f32(inp.ki), dev_f32(inp.k_scale), dev_f32(inp.w)
+    return dev_u8(inp.qi), dev_f32(inp.q_scale), dev_u8(inp.ki), dev_f32(inp.k_scale), dev_f32(inp.w)
+
+
+def overlap(idx_a, idx_b):
+    """sum_t |A_t & B_t| / sum_t |B_t| over rows, and the per-row minimum."""
+    tot = inter = 0
+    worst = 1.0
+    for a, b in zip(idx_a, idx_b):
+        sa = set(int(x) for x in a if x >= 0)
+        sb = set(int(x) for x in b if x >= 0)
+        i = len(sa & sb)
+        inter += i
+        tot += len(sb)
+        if sb:
+            worst = min(worst, i / len(sb))
+    return inter / max(tot, 1), worst

@@ -1,0 +1,120 @@
+"""The C ABI library: it builds, loads, exports every declared symbol and validates its
+arguments on the host (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_long_02_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(dsa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.LIB_PATH):
+        from sparse_attention_long_02_amd import build
+        build.build()
+    return dsa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert len(syms) == 10
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(dsa._SIGNATURES)
+
+
+def test_version_and_status_strings(L):
+    assert L.dsa_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert L.dsa_status_string(st)
+    assert b"unknown" in L.dsa_status_string(7)
+
+
+FAKE = 1 << 20   # a non-null, 16-byte-aligned address that is never dereferenced
+
+
+def test_indexer_validation(L):
+    call = lambda **kw: L.dsa_indexer(*[kw.get(n, d) for n, d in [
+        ("q", FAKE), ("qs", FAKE), ("k", FAKE), ("ks", FAKE), ("w", FAKE), ("B", 1), ("nq", 16),
+        ("nk", 16), ("qpos", None), ("H_I", 64), ("d_I", 128), ("dt", dsa.DSA_FP8_E4M3), ("rb", 0),
+        ("nr", 16), ("sc", FAKE), ("ld", 16), ("st", None)]])
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
+    assert b"null" in L.dsa_last_error()
+    assert call(nq=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(nr=17) == dsa.DSA_ERR_INVALID_ARG
+    assert call(rb=-1) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ld=15) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H_I=32) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(d_I=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(dt=dsa.DSA_BF16) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(dt=dsa.DSA_F32, H_I=65) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(q=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG     # misaligned FP8 operand
+    assert b"aligned" in L.dsa_last_error()
+
+
+def test_topk_validation(L):
+    assert L.dsa_topk(None, 16, 1, 4, 16, None, 0, 8, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(FAKE, 15, 1, 4, 16, None, 0, 8, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(FAKE, 16, 1, 4, 16, None, 0, 0, FAKE, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(FAKE, 1 << 19, 1, 4, 1 << 19, None, 0, 8, FAKE, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_sparse_mla_validation(L):
+    args = dict(q=FAKE, kv=FAKE, v=None, idx=FAKE, B=1, nq=4, nk=64, H=128, dqk=576, dv=512, k=2048,
+                sm=0.04, dt=dsa.DSA_BF16, out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    order = list(args)
+    call = lambda **kw: L.dsa_sparse_mla(*[kw.get(n, args[n]) for n in order])
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(v=FAKE) == dsa.DSA_ERR_UNSUPPORTED            # bf16 path reads V from kv
+    assert call(k=100) == dsa.DSA_ERR_UNSUPPORTED             # k must be a multiple of 32
+    assert call(dt=dsa.DSA_FP8_E4M3) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(dt=dsa.DSA_F32, H=4, dqk=64, dv=600) == dsa.DSA_ERR_INVALID_ARG
+    # few queries -> split keys -> needs workspace
+    need = L.dsa_workspace_size(dsa.DSA_OP_SPARSE_MLA, 1, 4, 64, 128, 512, 2048, dsa.DSA_BF16)
+    assert need > 0
+    assert call() == dsa.DSA_ERR_WORKSPACE
+    assert call(ws=FAKE, wsb=need - 1) == dsa.DSA_ERR_WORKSPACE
+
+
+def test_forward_validation(L):
+    pre = dict(qi=FAKE, qs=FAKE, ki=FAKE, ks=FAKE, w=FAKE, q=FAKE, kv=FAKE, v=None, L=1024, H_I=64, d_I=128,
+               H=128, dqk=576, dv=512, k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, idx=FAKE,
+               out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    order = list(pre)
+    call = lambda **kw: L.dsa_forward_prefill(*[kw.get(n, pre[n]) for n in order])
+    assert call(idx=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(L=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(it=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED     # fp32 indexer with bf16 attention
+    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED
+    f32 = dict(it=dsa.DSA_F32, at=dsa.DSA_F32, H_I=2, d_I=32, H=4, dqk=64, dv=64, v=FAKE, k=64, L=512)
+    need = L.dsa_workspace_size(dsa.DSA_OP_PREFILL, 1, 512, 512, 4, 64, 64, dsa.DSA_F32)
+    assert need >= 512 * 512 * 4
+    assert call(**f32) == dsa.DSA_ERR_WORKSPACE
+    dec = dict(B=64, ctx=FAKE, nkm=131072, qi=FAKE, qs=FAKE, w=FAKE, kc=FAKE, kcs=FAKE, q=FAKE, kv=FAKE,
+               v=None, H_I=64, d_I=128, H=128, dqk=576, dv=512, k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3,
+               at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    order = list(dec)
+    call = lambda **kw: L.dsa_forward_decode(*[kw.get(n, dec[n]) for n in order])
+    assert call(ctx=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call() == dsa.DSA_ERR_WORKSPACE
+    need = L.dsa_workspace_size(dsa.DSA_OP_DECODE, 64, 1, 131072, 128, 512, 2048, dsa.DSA_BF16)
+    assert need >= 64 * 131072 * 4
+    assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG   # misaligned workspace
+    assert call(nkm=1 << 19, ws=FAKE, wsb=1 << 40) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        dsa._ptr(torch.zeros(4))

@@ -1,0 +1,262 @@
+"""GPU parity of each stage against the float64 oracle, at sizes the oracle finishes in
+seconds that still span several tiles and a ragged tail."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_long_02_amd import dsa
+from sparse_attention_long_02_amd import synth as S
+from tests.helpers import (dev_attn, dev_bf16, dev_f32, dev_u8, indexer_inputs_dev, out_to_f64, overlap)
+
+pytestmark = pytest.mark.gpu
+
+ATOL_BF16 = 2e-2   # attention output, bf16 path (max-abs)
+ATOL_F32 = 1e-5    # attention output, fp32 path (max-abs)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def indexer_tolerance_ok(gpu_row, ref_row, mag_row, cond_row, d_I):
+    """|I_gpu - I_ref| <= 1e-2 * A + eps * M on the visible keys.
+
+    A = sum_j |w_j| ReLU(qhat_j . khat) is the size of the score; M = sum_j |w_j| sum_d
+    |qhat_jd khat_d| is what the fp32 dot products round against (their error bound is
+    about d_I * 2^-24 * M, which can exceed 1e-2 * A when a head's dot product nearly
+    cancels); eps = 2 * d_I * 2^-24.
+    """
+    eps = 2.0 * d_I * 2.0 ** -24
+    err = np.abs(gpu_row - ref_row)
+    bound = 1e-2 * mag_row + eps * cond_row
+    return bool(np.all(err <= bound)), float((err / (bound + 1e-300)).max())
+
+
+@pytest.fixture(scope="module")
+def c2_small():
+    cfg = S.CONFIGS["prefill_8k"].with_(L=1000)
+    return cfg, S.make_prefill(cfg)
+
+
+@pytest.fixture(scope="module")
+def c1():
+    cfg = S.CONFIGS["tiny_fp32_512"]
+    return cfg, S.make_prefill(cfg)
+
+
+# ------------------------------------------------------------------ indexer
+
+@pytest.mark.parametrize("which", ["c2_small", "c1"])
+def test_indexer_parity(which, request):
+    cfg, inp = request.getfixturevalue(which)
+    _say(f"[indexer parity] {cfg.name} L={cfg.L}")
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    torch.cuda.synchronize()
+    g = scores.cpu().numpy().astype(np.float64)
+    W = O.widen_inputs(inp)
+    worst = 0.0
+    for t in range(cfg.L):
+        ref = O.indexer_row(W["qhat"][t], W["w"][t], W["khat"], t)
+        mag = O.indexer_magnitude_row(W["qhat"][t], W["w"][t], W["khat"], t)
+        cond = np.abs(W["w"][t]) @ (np.abs(W["qhat"][t]) @ np.abs(W["khat"][: t + 1]).T)
+        ok, rel = indexer_tolerance_ok(g[t, : t + 1], ref, mag, cond, cfg.d_I)
+        worst = max(worst, rel)
+        assert ok, (t, rel)
+        assert np.all(np.isneginf(g[t, t + 1:])), t
+    _say(f"  worst error / bound = {worst:.3e}")
+
+
+def test_indexer_row_ranges_and_kernels_agree(c2_small):
+    """Scores of a row range, of single rows (the per-row split kernel) and of the whole
+    matrix are bit-identical; q_pos shifts positions."""
+    cfg, inp = c2_small
+    _say("[indexer kernels agree]")
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    full = dsa.indexer(qi, qs, ki, ks, w)
+    part = dsa.indexer(qi, qs, ki, ks, w, row_begin=300, n_rows=600)       # rows kernel
+    few = dsa.indexer(qi, qs, ki, ks, w, row_begin=997, n_rows=3)          # split kernel
+    one = dsa.indexer(qi, qs, ki, ks, w, row_begin=5, n_rows=1)
+    torch.cuda.synchronize()
+    assert torch.equal(part, full[300:900])
+    assert torch.equal(few, full[997:1000])
+    assert torch.equal(one, full[5:6])
+    # q_pos: row r of a sequence sits at q_pos + r
+    qpos = torch.tensor([100], dtype=torch.int32, device="cuda")
+    shifted = dsa.indexer(qi[None, 200:260], qs[None, 200:260], ki[None], ks[None], w[None, 200:260],
+                          q_pos=qpos)
+    torch.cuda.synchronize()
+    for r in (0, 17, 59):
+        p = 100 + r
+        # same query row, different position: visible prefix equals the full row's scores
+        ref_row = dsa.indexer(qi, qs, ki, ks, w, row_begin=200 + r, n_rows=1)[0]
+        assert torch.equal(shifted[0, r, : p + 1], ref_row[: p + 1])
+        assert torch.all(torch.isneginf(shifted[0, r, p + 1:]))
+
+
+# ------------------------------------------------------------------ top-k
+
+def _check_topk_exact(scores_dev, idx_dev, k, pos_of_row):
+    s = scores_dev.cpu().numpy().astype(np.float64)
+    got = idx_dev.cpu().numpy()
+    for i in range(s.shape[0]):
+        want = O.topk_row(s[i], pos_of_row(i), k)
+        assert np.array_equal(got[i], want), (i, got[i][:8], want[:8])
+
+
+@pytest.mark.parametrize("k", [64, 256, 2048])
+def test_topk_exact_on_gpu_scores(c2_small, k):
+    cfg, inp = c2_small
+    _say(f"[topk exact] k={k}")
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    idx = dsa.topk(scores, k)
+    torch.cuda.synchronize()
+    _check_topk_exact(scores, idx, k, lambda i: i)
+
+
+def test_topk_ties_zeros_and_positions():
+    _say("[topk ties]")
+    rng = np.random.default_rng(11)
+    levels = np.array([-1.0, -0.0, 0.0, 0.5, 2.0, -np.inf], dtype=np.float32)
+    B, R, n = 2, 24, 5000
+    s = levels[rng.integers(0, len(levels), size=(B, R, n))]
+    scores = torch.from_numpy(s).cuda()
+    qpos = torch.tensor([0, 3000], dtype=torch.int32, device="cuda")
+    for k in (1, 7, 64, 1000, 2048, 4999, 6000):
+        idx = dsa.topk(scores, k, q_pos=qpos, row_begin=10)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for b in range(B):
+            for i in range(R):
+                pos = int(qpos[b]) + 10 + i
+                want = O.topk_row(s[b, i].astype(np.float64), pos, k)
+                assert np.array_equal(got[b, i], want), (k, b, i)
+
+
+def test_topk_long_rows():
+    """Rows of 131072 keys (the decode length) with a continuous distribution and ties."""
+    _say("[topk long rows]")
+    rng = np.random.default_rng(12)
+    n = 131072
+    s = rng.standard_normal((3, n)).astype(np.float32)
+    s[1, rng.integers(0, n, 5000)] = s[1, 77]          # many exact copies of one value
+    s[2] = np.round(s[2] * 4) / 4                       # heavy ties everywhere
+    scores = torch.from_numpy(s).cuda()
+    # rows at positions n-1, n, n+1: every key is visible
+    idx = dsa.topk(scores, 2048, q_pos=torch.tensor([n - 1], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    _check_topk_exact(scores, idx, 2048, lambda i: n - 1)
+
+
+# ------------------------------------------------------------------ sparse MLA
+
+def _random_idx(rng, n_q, n_k, k, pos):
+    out = np.full((n_q, k), -1, dtype=np.int32)
+    for i in range(n_q):
+        cnt = min(k, pos[i] + 1)
+        if i % 11 == 3:
+            cnt = 0                        # empty selection
+        elif i % 11 == 5:
+            cnt = 1
+        sel = np.sort(rng.choice(pos[i] + 1, size=cnt, replace=False))
+        out[i, :cnt] = sel
+    # -1 entries in the middle are ignored too
+    out[7, 1::3] = -1
+    return out
+
+
+@pytest.mark.parametrize("n_q", [40, 1100])
+def test_sparse_mla_bf16_parity(n_q):
+    _say(f"[sparse mla bf16] n_q={n_q}")
+    rng = np.random.default_rng(13)
+    n_k, k = 3000, 2048 if n_q < 100 else 256
+    cfg = S.CONFIGS["prefill_8k"].with_(L=n_k)
+    q = S.bf16_bits(rng.standard_normal((n_q, 128, 576)).astype(np.float32))
+    kv = S.bf16_bits(rng.standard_normal((n_k, 576)).astype(np.float32))
+    pos = rng.integers(0, n_k, size=n_q)
+    pos[:3] = [0, n_k - 1, 2047]
+    idx = _random_idx(rng, n_q, n_k, k, pos)
+    out, lse = dsa.sparse_mla(dev_bf16(q), dev_bf16(kv), torch.from_numpy(idx).cuda(), cfg.sm_scale, 512)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    qf, kvf = O.bf16_to_f64(q), O.bf16_to_f64(kv)
+    rows = range(n_q) if n_q < 100 else rng.choice(n_q, 48, replace=False)
+    worst = 0.0
+    for i in rows:
+        o, l = O.sparse_mqa_row(qf[i], kvf, kvf[:, :512], idx[i], cfg.sm_scale)
+        err = np.abs(got[i] - o).max()
+        worst = max(worst, err)
+        assert err <= ATOL_BF16, (i, err)
+        fin = np.isfinite(l)
+        assert np.array_equal(fin, np.isfinite(got_lse[i]))
+        assert np.allclose(got_lse[i][fin], l[fin], atol=1e-3, rtol=1e-4)
+    _say(f"  worst max-abs {worst:.3e}")
+
+
+def test_sparse_mla_closed_forms():
+    """q = 0: O = mean of V over the kept keys, lse = ln |S|; a single kept key returns its row."""
+    _say("[sparse mla closed forms]")
+    rng = np.random.default_rng(14)
+    n_k, n_q, k = 700, 6, 2048
+    kv = S.bf16_bits(rng.standard_normal((n_k, 576)).astype(np.float32))
+    q = np.zeros((n_q, 128, 576), dtype=np.uint16)
+    idx = np.full((n_q, k), -1, dtype=np.int32)
+    idx[0, :1] = [0]
+    idx[1, :5] = [3, 9, 100, 101, 699]
+    idx[2, :700] = np.arange(700)
+    idx[3, :2] = [650, 12]
+    idx[5, :1] = [444]
+    out, lse = dsa.sparse_mla(dev_bf16(q), dev_bf16(kv), torch.from_numpy(idx).cuda(), 1 / 24, 512)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    kvf = O.bf16_to_f64(kv)
+    for i in range(n_q):
+        sel = idx[i][idx[i] >= 0]
+        if len(sel) == 0:
+            assert np.all(got[i] == 0) and torch.all(torch.isneginf(lse[i]))
+            continue
+        assert np.abs(got[i] - kvf[sel, :512].mean(0)[None]).max() <= 4e-3
+        assert np.allclose(lse[i].cpu().numpy(), np.log(len(sel)), atol=1e-5)
+
+
+def test_sparse_mla_fp32_parity(c1):
+    cfg, inp = c1
+    _say("[sparse mla fp32]")
+    rng = np.random.default_rng(15)
+    idx = _random_idx(rng, cfg.L, cfg.L, cfg.k, np.arange(cfg.L))
+    out, lse = dsa.sparse_mla(dev_f32(inp.q), dev_f32(inp.kv), torch.from_numpy(idx).cuda(), cfg.sm_scale,
+                              cfg.d_v, v=dev_f32(inp.v))
+    torch.cuda.synchronize()
+    W = O.widen_inputs(inp)
+    o, l = O.sparse_mqa(W["q"], W["kv"], W["v"], idx, cfg.sm_scale)
+    assert np.abs(out.double().cpu().numpy() - o).max() <= ATOL_F32
+    fin = np.isfinite(l)
+    assert np.allclose(lse.double().cpu().numpy()[fin], l[fin], atol=1e-5)
+
+
+# ------------------------------------------------------------------ whole layer, small
+
+def test_prefill_fp32_tiny_end_to_end(c1):
+    cfg, inp = c1
+    _say("[prefill fp32 tiny]")
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    idx, out, lse = dsa.forward_prefill(qi, qs, ki, ks, w, dev_f32(inp.q), dev_f32(inp.kv), cfg.k, cfg.sm_scale,
+                                        cfg.d_v, v=dev_f32(inp.v))
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    torch.cuda.synchronize()
+    # the selection is exactly the top-k of the library's own fp32 scores
+    _check_topk_exact(scores, idx, cfg.k, lambda i: i)
+    W = O.widen_inputs(inp)
+    ref = O.dsa_rows(W["qhat"], W["w"], W["khat"], W["q"], W["kv"], W["v"], np.arange(cfg.L), cfg.k, cfg.sm_scale)
+    ov, worst = overlap(idx.cpu().numpy(), ref["idx"])
+    _say(f"  overlap vs float64 selection {ov:.5f} (worst row {worst:.4f})")
+    assert ov >= 0.995
+    g = idx.cpu().numpy()
+    o, l = O.sparse_mqa(W["q"], W["kv"], W["v"], g, cfg.sm_scale)
+    assert np.abs(out.double().cpu().numpy() - o).max() <= ATOL_F32
