@@ -36,10 +36,10 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
   const int64_t row = row_begin + i;
   const uint8_t* kb8 = k8 + (int64_t)b * n_k * IDX_DIM;
   const float* ksb = ks + (int64_t)b * n_k;
-  IdxQuery Q;
+  IdxRow Q;
   if (active) {
     const int64_t qrow = (int64_t)b * n_q + row;
-    load_idx_query(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
+    load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
   }
   float* srow = scores + ((int64_t)b * n_rows + (active ? i : 0)) * ld;
 
@@ -55,8 +55,9 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
     if (active) {
       const int64_t key = (int64_t)t * KEY_TILE + lane;
       const float ksc = ksb[key < n_k ? key : n_k - 1];
-      const float s = score_tile64(Q, lds_key_fragment(tiles[cur], 0), lds_key_fragment(tiles[cur], 1),
-                                   lds_key_fragment(tiles[cur], 2), lds_key_fragment(tiles[cur], 3), ksc);
+      const v8i bf[4] = {lds_key_fragment(tiles[cur], 0), lds_key_fragment(tiles[cur], 1),
+                         lds_key_fragment(tiles[cur], 2), lds_key_fragment(tiles[cur], 3)};
+      const float s = score_tile64(Q, bf, ksc);
       if (key < n_k) srow[key] = key <= pos ? s : -INFINITY;
     }
     if (t + 1 < ntiles) store_key_tile_lds(R, tiles[cur ^ 1], tid);
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
   n_vis = n_vis > 0 ? n_vis : 0;
   const int64_t vis_tiles = (n_vis + KEY_TILE - 1) / KEY_TILE;
 
-  IdxQuery Q;
+  IdxRow Q;
   bool loaded = false;
   for (int64_t t = t0 + wv; t < t0 + SPLIT_TILES; t += 4) {
     const int64_t key0 = t * KEY_TILE;
@@ -99,12 +100,13 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
       continue;
     }
     if (!loaded) {
-      load_idx_query(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
+      load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
       loaded = true;
     }
     const float ksc = ksb[key < n_k ? key : n_k - 1];
-    const float s = score_tile64(Q, global_key_fragment(kb8, key0, 0, n_k), global_key_fragment(kb8, key0, 1, n_k),
-                                 global_key_fragment(kb8, key0, 2, n_k), global_key_fragment(kb8, key0, 3, n_k), ksc);
+    const v8i bf[4] = {global_key_fragment(kb8, key0, 0, n_k), global_key_fragment(kb8, key0, 1, n_k),
+                       global_key_fragment(kb8, key0, 2, n_k), global_key_fragment(kb8, key0, 3, n_k)};
+    const float s = score_tile64(Q, bf, ksc);
     if (key < n_k) srow[key] = key <= pos ? s : -INFINITY;
   }
 }

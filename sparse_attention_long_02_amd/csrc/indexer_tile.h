@@ -2,20 +2,27 @@
 //
 // The index score of query t and key s is
 //     I[t,s] = k_scale[s] * sum_j c[t,j] * ReLU(q8[t,j,:] . k8[s,:]),  c = w * q_scale
-// i.e. the weighted sum over indexer heads of ReLU'd FP8 dot products (the indexer is
+// the weighted sum over indexer heads of ReLU'd FP8 dot products (the indexer is
 // multi-head, uses ReLU and runs in FP8: 53ai.com V3.2-Exp report summary, section
 // 创新架构; juhe.plus explainer, section 第一步：Lightning Indexer).  Pulling the positive
 // per-row scales out of the ReLU is exact in real arithmetic.
 //
-// One wave scores one query against 64 keys at a time:
-//   * the 64 heads are the M dimension of four 16x16x128 FP8 MFMAs (A = the query's head
-//     rows, loaded once), the keys are N (B = 16 keys x 128 bytes per fragment);
-//   * each lane then holds 4 heads x 1 key per MFMA and folds ReLU and c into a running
-//     fp32 sum over its 16 heads;
-//   * a reduce-scatter over the four 16-lane groups (two permlane swaps) leaves lane l
-//     with the full head sum for key l of the 64-key tile.
-// Every kernel that produces scores goes through score_tile64(), so scores are
-// bit-identical whichever kernel computes them.
+// How the terms are formed (the same in every kernel, so scores are bit-identical
+// whichever kernel produces them):
+//   * the 64 heads are the M dimension of four 16x16x128 FP8 MFMAs (A = a query's head
+//     rows), the keys are N (B = 16 keys x 128 bytes).  The MFMA's block scales multiply
+//     every product by 2^-25, exactly (powers of two), so each head dot x lies in
+//     (-0.77, 0.77) whatever the FP8 codes (|x| <= 448^2 * 128 * 2^-25);
+//   * ReLU and the head weights then cost 1.5 VALU ops per head: pairs of heads are packed
+//     to f16 (round toward zero), ReLU'd with one packed max, and dotted with the pair of
+//     normalised weights c' = c / max|c| (f16) into an fp32 sum (v_dot2_f32_f16);
+//   * per lane the sum covers 8 heads of one "head half" (two 16-head blocks); the four
+//     16-lane groups of a wave are combined as (g0 + g2) + (g1 + g3) by two permlane
+//     swaps; the two head halves are added; the result is scaled by max|c| * 2^25 and by
+//     k_scale.
+// Relative error of a term: <= 2^-10 (f16 truncation) + 2^-11 (f16 weight); f16
+// subnormals below 2^-14 (head dots below 2^11 in code units) carry an absolute error of
+// at most 2 code units.
 #pragma once
 
 #include "dsa_device.h"
@@ -24,63 +31,107 @@ namespace dsa {
 
 constexpr int IDX_HEADS = 64;
 constexpr int IDX_DIM = 128;
-constexpr int KEY_TILE = 64;  // keys scored per wave step
+constexpr int KEY_TILE = 64;  // keys per tile
 
-// per-wave query state: A operands of the 4 head blocks and the 16 head weights c this
-// lane folds (heads 16*hb + 4*(lane/16) + i)
-struct IdxQuery {
-  v8i a[4];
-  float c[16];
+typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+
+// E8M0 block scales: 2^-13 on the query side, 2^-12 on the key side
+constexpr uint32_t SCALE_Q = 0x72727272u, SCALE_K = 0x73737373u;
+constexpr float UNSCALE = 33554432.0f;  // 2^25
+
+__device__ __forceinline__ v4f mfma_fp8_scaled(v8i a, v8i b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, SCALE_Q, 0,
+                                                          SCALE_K);
+}
+
+// One query row's operands for one head half (head blocks 2hh, 2hh+1): the A operands and
+// the f16 weight pairs this lane folds (heads 16hb + 4g + {0,1} and {2,3}).
+struct IdxHalf {
+  v8i a[2];
+  h2 c[4];
 };
 
-// q8: the query's [64][128] FP8 codes; qs, w: its 64 scales and weights.
-__device__ __forceinline__ void load_idx_query(IdxQuery& Q, const uint8_t* __restrict__ q8,
-                                               const float* __restrict__ qs,
-                                               const float* __restrict__ w) {
+// Per-row weight normaliser: cs = max_j |w_j q_scale_j| * 2^25 (0 if all weights vanish).
+__device__ __forceinline__ float row_cmax(const float* __restrict__ qs, const float* __restrict__ w) {
+  const int l = lane_id();
+  float m = fabsf(__fmul_rn(w[l], qs[l]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
+  return m;
+}
+
+__device__ __forceinline__ void load_idx_half(IdxHalf& Q, const uint8_t* __restrict__ q8,
+                                              const float* __restrict__ qs, const float* __restrict__ w,
+                                              int hh, float cmax) {
   const int l = lane_id();
   const int g = l >> 4;
+  const float inv = cmax > 0.f ? 1.f / cmax : 0.f;
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
+  for (int k = 0; k < 2; ++k) {
+    const int hb = 2 * hh + k;
     const int head = 16 * hb + (l & 15);
     const v4i* p = reinterpret_cast<const v4i*>(q8 + head * IDX_DIM + 32 * g);
-    v4i lo = p[0], hi = p[1];
-    Q.a[hb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const v4i lo = p[0], hi = p[1];
+    Q.a[k] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h2 = 16 * hb + 4 * g + i;
-      Q.c[4 * hb + i] = __fmul_rn(w[h2], qs[h2]);
+    for (int pr = 0; pr < 2; ++pr) {
+      const int h0 = 16 * hb + 4 * g + 2 * pr;
+      const float c0 = __fmul_rn(__fmul_rn(w[h0], qs[h0]), inv);
+      const float c1 = __fmul_rn(__fmul_rn(w[h0 + 1], qs[h0 + 1]), inv);
+      Q.c[2 * k + pr] = h2{(__fp16)c0, (__fp16)c1};
     }
   }
 }
 
-// Partial head sum (this lane's 16 heads) for the key this lane holds in fragment b.
-__device__ __forceinline__ float fold_fragment(const IdxQuery& Q, v8i b) {
-  v4f acc[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) acc[hb] = mfma_fp8_16x16x128(Q.a[hb], b, v4f{0.f, 0.f, 0.f, 0.f});
+// Fold the two MFMA results of a head half: sum over this lane's 8 heads of c' ReLU(x).
+__device__ __forceinline__ float fold_half(const IdxHalf& Q, v4f x0, v4f x1) {
+  const h2 zero = h2{(__fp16)0.f, (__fp16)0.f};
   float p = 0.f;
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p = __fmaf_rn(Q.c[4 * hb + i], fmaxf(acc[hb][i], 0.f), p);
+  h2 r;
+  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x0[0], x0[1]), zero);
+  p = __builtin_amdgcn_fdot2(Q.c[0], r, p, false);
+  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x0[2], x0[3]), zero);
+  p = __builtin_amdgcn_fdot2(Q.c[1], r, p, false);
+  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x1[0], x1[1]), zero);
+  p = __builtin_amdgcn_fdot2(Q.c[2], r, p, false);
+  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x1[2], x1[3]), zero);
+  p = __builtin_amdgcn_fdot2(Q.c[3], r, p, false);
   return p;
 }
 
-// Given the partial sums of 4 consecutive 16-key fragments, return the full head sum
-// of key (lane) of the 64-key tile.
+// Combine four per-lane partial vectors across the four 16-lane groups: lane l returns
+// the total of vector l/16 at column l%16, summed as (g0 + g2) + (g1 + g3).
 __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
-  // lanes 0-31 collect fragments 0,1 and lanes 32-63 fragments 2,3 (pairs g, g+2)
   auto r02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
   auto r13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
   const float qa = __fadd_rn(__uint_as_float(r02[0]), __uint_as_float(r02[1]));
   const float qb = __fadd_rn(__uint_as_float(r13[0]), __uint_as_float(r13[1]));
-  // rows (16-lane groups) 0..3 end with fragments 0..3 (pairs g, g+1)
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(qa), __float_as_uint(qb), false, false);
   return __fadd_rn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// B operand of fragment f (keys 16f .. 16f+15) from a 64-key LDS tile stored as
-// 64 rows of 128 bytes whose 16-byte chunks are XOR-swizzled by (row & 7).
+// Final score from the two head-half totals.
+__device__ __forceinline__ float finish_score(float t0, float t1, float cmax, float kscale) {
+  return __fmul_rn(__fmul_rn(__fadd_rn(t0, t1), __fmul_rn(cmax, UNSCALE)), kscale);
+}
+
+// ---------------------------------------------------------------------------------------
+// single-wave scoring of one query row against 64 keys (the score-writing kernels)
+// ---------------------------------------------------------------------------------------
+struct IdxRow {
+  IdxHalf h[2];
+  float cmax;
+};
+
+__device__ __forceinline__ void load_idx_row(IdxRow& R, const uint8_t* __restrict__ q8,
+                                             const float* __restrict__ qs, const float* __restrict__ w) {
+  R.cmax = row_cmax(qs, w);
+  load_idx_half(R.h[0], q8, qs, w, 0, R.cmax);
+  load_idx_half(R.h[1], q8, qs, w, 1, R.cmax);
+}
+
+// B operand of fragment f (keys 16f .. 16f+15) from a 64-key LDS tile stored as 64 rows of
+// 128 bytes whose 16-byte units are XOR-swizzled by (row & 7).
 __device__ __forceinline__ v8i lds_key_fragment(const uint8_t* tile, int f) {
   const int l = lane_id();
   const int row = 16 * f + (l & 15);
@@ -104,18 +155,29 @@ __device__ __forceinline__ v8i global_key_fragment(const uint8_t* __restrict__ k
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Score of key (key0 + lane) given the four fragments' B operands and that key's scale.
-__device__ __forceinline__ float score_tile64(const IdxQuery& Q, v8i b0, v8i b1, v8i b2, v8i b3,
-                                             float kscale) {
-  const float p0 = fold_fragment(Q, b0);
-  const float p1 = fold_fragment(Q, b1);
-  const float p2 = fold_fragment(Q, b2);
-  const float p3 = fold_fragment(Q, b3);
-  return __fmul_rn(reduce_scatter4(p0, p1, p2, p3), kscale);
+// Score of key (key0 + lane) of a 64-key tile given the four fragments' B operands.
+__device__ __forceinline__ float score_tile64(const IdxRow& R, const v8i* b, float kscale) {
+  v4f x[4][2][2];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      x[f][hh][0] = mfma_fp8_scaled(R.h[hh].a[0], b[f]);
+      x[f][hh][1] = mfma_fp8_scaled(R.h[hh].a[1], b[f]);
+    }
+  __builtin_amdgcn_sched_barrier(0);  // all 16 MFMAs issue back to back, then the folds
+  float p[2][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) p[hh][f] = fold_half(R.h[hh], x[f][hh][0], x[f][hh][1]);
+  const float t0 = reduce_scatter4(p[0][0], p[0][1], p[0][2], p[0][3]);
+  const float t1 = reduce_scatter4(p[1][0], p[1][1], p[1][2], p[1][3]);
+  return finish_score(t0, t1, R.cmax, kscale);
 }
 
 // Cooperative copy of one 64-key tile (8 KB) into LDS by a 256-thread block:
-// two 16-byte chunks per thread, swizzled as lds_key_fragment() expects.
+// two 16-byte units per thread, swizzled as lds_key_fragment() expects.
 struct KeyTileRegs {
   v4i c[2];
 };

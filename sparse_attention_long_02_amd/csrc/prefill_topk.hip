@@ -1,16 +1,16 @@
 // Fused lightning indexer + streaming top-k for prefill (query t at position t).
 //
-// The indexer's L x L score matrix is never stored.  Each wave owns one query row and
-// scores its visible keys 64 at a time (indexer_tile.h); every score immediately meets
-// the row's streaming selection state in LDS:
+// The indexer's L x L score matrix is never stored.  Rows are scored 64 keys at a time
+// (indexer_tile.h); every score immediately meets the row's streaming selection state in
+// LDS:
 //   * a candidate buffer (order-preserving key + index) that stays sorted by key index,
 //     because keys arrive in ascending order and appends keep lane order;
 //   * a threshold thr: once the buffer has been cut to exactly k entries, v* = the k-th
 //     largest key so far, and a later key can only enter with a strictly larger key
 //     (on a tie it has the larger index, and the lower index wins);
-//   * when the buffer is nearly full, a wave-local radix select (4 x 8-bit digits over
-//     an LDS histogram) finds v* and an in-place stable compaction keeps exactly the
-//     top-k so far.
+//   * when the buffer is nearly full, a wave-local radix select (8-bit digits over an LDS
+//     histogram, starting at the highest bit where the candidates differ) finds v* and an
+//     in-place stable compaction keeps exactly the top-k so far.
 // At the end the buffer holds the row's selection in ascending key order.  Rows whose
 // position is below k keep every key and are written by a separate fill kernel.
 //
@@ -22,152 +22,359 @@
 
 namespace dsa {
 
-constexpr int CAND = 4096;  // candidate slots per row
+constexpr int CAND = 3584;  // candidate slots per row
 
-struct RowSelect {
-  uint32_t* key;  // [CAND]
-  int32_t* idx;   // [CAND]
-  uint32_t* hist; // [256]
-};
+// Per-row selection state of the fused kernel, at file scope so the compiler can tell it
+// apart from the key tiles that direct loads are still writing (accesses to these arrays
+// then never wait for the tile loads).
+__shared__ uint32_t s_ckey[4][CAND];
+__shared__ int32_t s_cidx[4][CAND];
+__shared__ uint32_t s_hist[4][256];
 
-// Radix select of the k-th largest key among key[0..n) (n > k), then stable in-place
-// compaction to exactly k entries.  Wave-local; returns v*.
-__device__ uint32_t select_compact(const RowSelect& R, int n, int k) {
+// LDS increment without a return value, written as the instruction itself: the compiler
+// would otherwise drain every in-flight direct load before each atomic (it cannot tell that
+// the histogram and the tile buffers do not overlap).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)p);
+}
+__device__ __forceinline__ void lds_inc(uint32_t* p) {
+  asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(p)), "v"(1u) : "memory");
+}
+// 4-byte LDS store written as the instruction itself (same reason as lds_inc).  Completion
+// is left to the s_waitcnt lgkmcnt(0) that precedes every block barrier; a later LDS read
+// by the same wave is ordered after it by the LDS queue.
+__device__ __forceinline__ void lds_store(void* p, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+// 16-byte LDS read that completes inside the same asm block (same reason as lds_inc).
+__device__ __forceinline__ v4i lds_read16_sync(const void* p) {
+  v4i r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr(p)) : "memory");
+  return r;
+}
+
+constexpr int SEL_BATCH = 8;  // entries per lane in flight per pass step
+
+// Radix select of the k-th largest key among s_ckey[r][0..n) (n > k), then stable in-place
+// compaction to exactly k entries.  Wave-local.  The digits start at the highest bit where
+// the candidates differ (they share their top bits, which would pile every candidate into
+// one histogram bin).  Every pass reads SEL_BATCH entries per lane before using them.
+// Returns v*.
+__device__ uint32_t select_compact(int r, int n, int k) {
   const int lane = lane_id();
-  uint32_t prefix = 0, pmask = 0;
+  uint32_t* key = s_ckey[r];
+  int32_t* id = s_cidx[r];
+  uint32_t* hist = s_hist[r];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
+    uint32_t u[SEL_BATCH];
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m) {
+      const int i = base + WAVE * m + lane;
+      u[m] = key[i < n ? i : 0];
+    }
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m) {
+      const bool in = base + WAVE * m + lane < n;
+      mn = in ? min(mn, u[m]) : mn;
+      mx = in ? max(mx, u[m]) : mx;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, WAVE));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
+  }
   uint32_t rem = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  uint32_t prefix = mx, pmask = 0xFFFFFFFFu;
+  if (mn != mx) {
+    int hi = 31 - __clz((int)(mn ^ mx));  // highest differing bit
+    pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+    prefix = mx & pmask;
+    while (true) {
+      const int shift = hi >= 7 ? hi - 7 : 0;
+      const uint32_t dmask = (2u << (hi - shift)) - 1u;
+      *reinterpret_cast<v4i*>(hist + 4 * lane) = v4i{0, 0, 0, 0};
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
+        uint32_t u[SEL_BATCH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) R.hist[lane + 64 * j] = 0;
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-    for (int i = lane; i < n; i += WAVE) {
-      const uint32_t u = R.key[i];
-      if ((u & pmask) == prefix) atomicAdd(&R.hist[(u >> shift) & 255u], 1u);
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    // lane owns bins 255-4*lane .. 252-4*lane (descending)
-    uint32_t h[4], local = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h[j] = R.hist[255 - 4 * lane - j];
-      local += h[j];
-    }
-    uint32_t c = wave_incl_scan(local) - local;
-    uint32_t digit = 0, above = 0;
-    bool found = false;
-    if (c < rem && c + local >= rem) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (!found && c + h[j] >= rem) {
-          found = true;
-          digit = 255u - 4u * lane - j;
-          above = c;
+        for (int m = 0; m < SEL_BATCH; ++m) {
+          const int i = base + WAVE * m + lane;
+          u[m] = key[i < n ? i : 0];
         }
-        c += h[j];
+#pragma unroll
+        for (int m = 0; m < SEL_BATCH; ++m)
+          if (base + WAVE * m + lane < n && (u[m] & pmask) == prefix) lds_inc(&hist[(u[m] >> shift) & dmask]);
       }
+      __builtin_amdgcn_wave_barrier();
+      // lane owns bins 255-4*lane .. 252-4*lane (descending)
+      const v4i hv = lds_read16_sync(hist + 252 - 4 * lane);
+      const uint32_t h[4] = {(uint32_t)hv[3], (uint32_t)hv[2], (uint32_t)hv[1], (uint32_t)hv[0]};
+      const uint32_t local = h[0] + h[1] + h[2] + h[3];
+      uint32_t c = wave_incl_scan(local) - local;
+      uint32_t digit = 0, above = 0;
+      bool found = false;
+      if (c < rem && c + local >= rem) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!found && c + h[j] >= rem) {
+            found = true;
+            digit = 255u - 4u * lane - j;
+            above = c;
+          }
+          c += h[j];
+        }
+      }
+      const uint64_t fm = ballot(found);
+      const int src = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
+      digit = __shfl(digit, src, WAVE);
+      above = __shfl(above, src, WAVE);
+      rem -= above;
+      prefix |= digit << shift;
+      pmask |= dmask << shift;
+      if (shift == 0) break;
+      hi = shift - 1;
     }
-    const uint64_t fm = ballot(found);
-    const int src = __ffsll((unsigned long long)fm) - 1;
-    digit = __shfl(digit, src, WAVE);
-    above = __shfl(above, src, WAVE);
-    rem -= above;
-    prefix |= digit << shift;
-    pmask |= 0xFFu << shift;
   }
-  // keep key > v*, and the first `rem` keys equal to v* (lowest indices)
+  // keep key > v*, and the first `rem` keys equal to v* (lowest indices).  All entries of a
+  // batch are read before any is written, and an entry only moves down, so the in-place
+  // stable compaction never overwrites an unread entry.
   uint32_t kept = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += WAVE) {
-    const int i = base + lane;
-    const bool in = i < n;
-    const uint32_t u = in ? R.key[i] : 0u;
-    const int32_t id = in ? R.idx[i] : -1;
-    const bool eq = in && u == prefix;
-    const uint64_t me = ballot(eq);
-    const bool keep = (in && u > prefix) || (eq && eq_seen + lanes_below(me) < rem);
-    const uint64_t mk = ballot(keep);
-    if (keep) {
-      const uint32_t dst = kept + lanes_below(mk);
-      R.key[dst] = u;
-      R.idx[dst] = id;
+  for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
+    uint32_t u[SEL_BATCH];
+    int32_t ix[SEL_BATCH];
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m) {
+      const int i = base + WAVE * m + lane;
+      u[m] = key[i < n ? i : 0];
+      ix[m] = id[i < n ? i : 0];
     }
-    kept += (uint32_t)__popcll((unsigned long long)mk);
-    eq_seen += (uint32_t)__popcll((unsigned long long)me);
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m) {
+      const bool in = base + WAVE * m + lane < n;
+      const bool eq = in && u[m] == prefix;
+      const uint64_t me = ballot(eq);
+      const bool keep = (in && u[m] > prefix) || (eq && eq_seen + lanes_below(me) < rem);
+      const uint64_t mk = ballot(keep);
+      if (keep) {
+        const uint32_t dst = kept + lanes_below(mk);
+        key[dst] = u[m];
+        id[dst] = ix[m];
+      }
+      kept += (uint32_t)__popcll((unsigned long long)mk);
+      eq_seen += (uint32_t)__popcll((unsigned long long)me);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
   return prefix;
 }
 
-// grid.x = row groups of 4 over rows [row_lo, L), last rows first
-__global__ __launch_bounds__(256, 1) void prefill_idx_topk_kernel(
+// ---------------------------------------------------------------------------------------
+// Persistent fused kernel.  A block of 8 waves owns groups of 4 consecutive rows; blocks
+// take groups longest-first in lockstep (group G = block + round * blocks), so the blocks
+// on one XCD sweep the same key tiles at about the same time and the tiles stay in L2.
+// Wave w scores key fragment f = w/2 (16 keys of each 64-key tile) for head half hh = w%2
+// of all 4 rows and writes its half-totals to LDS; wave j < 4 also owns row j's selection.
+// Key tiles arrive by direct global->LDS loads in a ring of 4 buffers (three in flight).
+//
+// The two waves sharing a SIMD (w and w+4) run out of phase, so one's VALU work covers the
+// other's MFMAs: waves 0-3 issue tile i's MFMAs then fold them; waves 4-7 first fold the
+// MFMA results of tile i-1 kept in registers, then issue tile i's MFMAs.  Tile t's half
+// totals are therefore complete after step t+1, and the owners take tile t at step t+2.
+// When any owner's buffer nears full, all four owners compact at the same step (one stall
+// of the block instead of four).
+// ---------------------------------------------------------------------------------------
+constexpr int PF_WAVES = 8;
+constexpr int TILE_BYTES = KEY_TILE * IDX_DIM;
+constexpr int XSLOTS = 3;                       // tile score exchange ring
+constexpr int COMPACT_AT = CAND - 3 * KEY_TILE;  // collective compaction trigger
+
+#define WAIT_VM_LGKM0(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0x0 << 8))
+
+// wave w copies LDS units 64w .. 64w+63 of a tile (key 8w + lane/8 of the tile, 16-byte
+// unit lane%8 XOR-swizzled by the key's row); wave 0 also copies the tile's 64 key scales.
+struct TileDma {
+  int krow;          // key row within the tile
+  uint32_t koff;     // byte offset of this lane's unit within a key row
+};
+__device__ __forceinline__ TileDma tile_dma_lane(int wv, int lane) {
+  const int U = 64 * wv + lane;
+  const int row = U >> 3, cp = U & 7;
+  return TileDma{row, (uint32_t)(16 * (cp ^ (row & 7)))};
+}
+__device__ __forceinline__ void dma_key_tile(uint8_t* tk, float* ts, const uint8_t* __restrict__ k8,
+                                             const float* __restrict__ ks, int key0, int L, const TileDma& d,
+                                             int wv, int lane) {
+  const int key = min(key0 + d.krow, L - 1);
+  __builtin_amdgcn_global_load_lds(k8 + (size_t)key * IDX_DIM + d.koff, tk + 1024 * wv, 16, 0, 0);
+  if (wv == 0) __builtin_amdgcn_global_load_lds(ks + min(key0 + lane, L - 1), ts, 4, 0, 0);
+}
+
+// wait until tile i has landed: tiles i+1, i+2 (if they exist) may still be in flight;
+// wave 0 issues two loads per tile, the others one.  Also drains this wave's LDS ops.
+__device__ __forceinline__ void wait_tile(int i, int ntiles, int wv) {
+  const int after = min(2, ntiles - 1 - i);
+  if (wv == 0) {
+    if (after >= 2) WAIT_VM_LGKM0(4);
+    else if (after == 1) WAIT_VM_LGKM0(2);
+    else WAIT_VM_LGKM0(0);
+  } else {
+    if (after >= 2) WAIT_VM_LGKM0(2);
+    else if (after == 1) WAIT_VM_LGKM0(1);
+    else WAIT_VM_LGKM0(0);
+  }
+}
+
+struct OwnerState {
+  int cnt;
+  uint32_t thr;
+  float cmax;
+  float ksc[2];  // key scales of the two tiles not yet taken
+};
+
+__shared__ int s_cnt[4];  // owners' published candidate counts
+// Half-totals of tile scores exchanged between the scoring waves and the owners
+// ([tile % 3][head half][row][key]).
+__shared__ float xbuf[XSLOTS][2][4][KEY_TILE];
+
+// Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer; compact
+// when this buffer is full or when any owner's buffer nears full (all compact together).
+__device__ __forceinline__ void owner_take(OwnerState& S, int r, float s, int key0, int row, int k) {
+  const int lane = lane_id();
+  const int key = key0 + lane;
+  const uint32_t u = score_key(s);
+  const bool pass = key <= row && u > S.thr;
+  const uint64_t m = ballot(pass);
+  if (m) {
+    if (pass) {
+      const int off = S.cnt + (int)lanes_below(m);
+      s_ckey[r][off] = u;
+      s_cidx[r][off] = key;
+    }
+    S.cnt += __popcll((unsigned long long)m);
+  }
+  const int most = max(max(s_cnt[0], s_cnt[1]), max(s_cnt[2], s_cnt[3]));
+  if (S.cnt > CAND - KEY_TILE || (most > COMPACT_AT && S.cnt > k)) {
+    __builtin_amdgcn_wave_barrier();
+    S.thr = select_compact(r, S.cnt, k);
+    S.cnt = k;
+  }
+}
+
+__global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
-    const float* __restrict__ ks, const float* __restrict__ w, int64_t L, int64_t row_lo, int k,
-    int32_t* __restrict__ idx) {
-  __shared__ __align__(16) uint8_t tiles[2][KEY_TILE * IDX_DIM];
-  __shared__ uint32_t ckey[4][CAND];
-  __shared__ int32_t cidx[4][CAND];
-  __shared__ uint32_t hist[4][256];
+    const float* __restrict__ ks, const float* __restrict__ w, int L, int row_lo, int k,
+    int n_groups, int32_t* __restrict__ idx) {
+  __shared__ __align__(16) uint8_t tk0[TILE_BYTES];
+  __shared__ __align__(16) uint8_t tk1[TILE_BYTES];
+  __shared__ __align__(16) uint8_t tk2[TILE_BYTES];
+  __shared__ __align__(16) uint8_t tk3[TILE_BYTES];
+  __shared__ __align__(16) float ts0[KEY_TILE];
+  __shared__ __align__(16) float ts1[KEY_TILE];
+  __shared__ __align__(16) float ts2[KEY_TILE];
+  __shared__ __align__(16) float ts3[KEY_TILE];
 
+  uint8_t* const tks[4] = {tk0, tk1, tk2, tk3};
+  float* const tss[4] = {ts0, ts1, ts2, ts3};
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int64_t n_rows = L - row_lo;
-  const int64_t grp = (int64_t)gridDim.x - 1 - blockIdx.x;
-  const int64_t i = grp * 4 + wv;
-  const bool active = i < n_rows;
-  const int64_t row = row_lo + i;  // == its position
-  const int64_t i_last = (grp * 4 + 3 < n_rows) ? grp * 4 + 3 : n_rows - 1;
-  const int64_t n_vis = row_lo + i_last + 1;  // <= L
-  const int ntiles = (int)((n_vis + KEY_TILE - 1) / KEY_TILE);
+  const int f = wv >> 1, hh = wv & 1;
+  const bool lead = wv < 4;  // MFMA-then-fold role; also the row owners
+  const TileDma dl = tile_dma_lane(wv, lane);
 
-  IdxQuery Q;
-  if (active) load_idx_query(Q, q8 + row * IDX_HEADS * IDX_DIM, qs + row * IDX_HEADS, w + row * IDX_HEADS);
-  RowSelect R{ckey[wv], cidx[wv], hist[wv]};
-  int cnt = 0;
-  uint32_t thr = 0;
+  for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
+    const int row_hi = L - 4 * G;  // rows row_hi-4 .. row_hi-1
+    const int row0 = row_hi - 4;
+    IdxHalf Qh[4];
+    float cm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = max(row0 + j, row_lo);  // rows below row_lo are not this kernel's: score a valid row
+      cm[j] = row_cmax(qs + (size_t)r * IDX_HEADS, w + (size_t)r * IDX_HEADS);
+      load_idx_half(Qh[j], q8 + (size_t)r * IDX_HEADS * IDX_DIM, qs + (size_t)r * IDX_HEADS,
+                    w + (size_t)r * IDX_HEADS, hh, cm[j]);
+    }
+    const int my_row = row0 + (wv & 3);
+    const bool my_valid = lead && my_row >= row_lo;
+    OwnerState S{0, 0u, cm[wv & 3], {0.f, 0.f}};
+    if (lead && lane == 0) s_cnt[wv] = 0;
+    const int ntiles = (row_hi + KEY_TILE - 1) / KEY_TILE;
+    v4f xprev[4][2];  // trailing waves: MFMA results of the previous tile
 
-  KeyTileRegs TR;
-  load_key_tile_regs(TR, k8, 0, L, tid);
-  store_key_tile_lds(TR, tiles[0], tid);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < ntiles) load_key_tile_regs(TR, k8, (int64_t)(t + 1) * KEY_TILE, L, tid);
-    if (active) {
-      const int64_t key = (int64_t)t * KEY_TILE + lane;
-      const float ksc = ks[key < L ? key : L - 1];
-      const float s = score_tile64(Q, lds_key_fragment(tiles[cur], 0), lds_key_fragment(tiles[cur], 1),
-                                   lds_key_fragment(tiles[cur], 2), lds_key_fragment(tiles[cur], 3), ksc);
-      const uint32_t u = score_key(s);
-      const bool pass = key <= row && u > thr;
-      const uint64_t m = ballot(pass);
-      if (m) {
-        if (pass) {
-          const int off = cnt + (int)lanes_below(m);
-          R.key[off] = u;
-          R.idx[off] = (int32_t)key;
-        }
-        cnt += __popcll((unsigned long long)m);
-        if (cnt > CAND - KEY_TILE) {
-          __builtin_amdgcn_s_waitcnt(0xc07f);
-          __builtin_amdgcn_wave_barrier();
-          thr = select_compact(R, cnt, k);
-          cnt = k;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < ntiles) dma_key_tile(tks[j], tss[j], k8, ks, j * KEY_TILE, L, dl, wv, lane);
+
+    for (int base = 0; base < ntiles + 2; base += 4) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = base + jj;
+        if (i < ntiles + 2) {
+          if (i < ntiles) wait_tile(i, ntiles, wv);
+          else WAIT_VM_LGKM0(0);
+          __builtin_amdgcn_s_barrier();
+          if (i + 3 < ntiles) dma_key_tile(tks[(jj + 3) & 3], tss[(jj + 3) & 3], k8, ks, (i + 3) * KEY_TILE, L, dl, wv, lane);
+          if (lead) {
+            v4f x[4][2];
+            float ksc_i = 0.f;
+            if (i < ntiles) {
+              ksc_i = tss[jj][lane];
+              const v8i b = lds_key_fragment(tks[jj], f);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                x[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
+                x[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // take tile i-2 (its key scales sit in ring slot i%2), then keep tile i's scales there
+            if (i >= 2 && my_valid) {
+              const int t = i - 2, slot = t % XSLOTS;
+              const float x0 = xbuf[slot][0][wv][lane], x1 = xbuf[slot][1][wv][lane];
+              owner_take(S, wv, finish_score(x0, x1, S.cmax, S.ksc[i & 1]), t * KEY_TILE, my_row, k);
+              if (lane == 0) s_cnt[wv] = S.cnt;
+            }
+            S.ksc[i & 1] = ksc_i;
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < ntiles) {
+              float p[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], x[j][0], x[j][1]);
+              lds_store(&xbuf[i % XSLOTS][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
+            }
+          } else {
+            if (i >= 1 && i <= ntiles) {
+              float p[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], xprev[j][0], xprev[j][1]);
+              lds_store(&xbuf[(i - 1) % XSLOTS][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < ntiles) {
+              const v8i b = lds_key_fragment(tks[jj], f);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                xprev[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
+                xprev[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
+              }
+            }
+          }
         }
       }
     }
-    if (t + 1 < ntiles) store_key_tile_lds(TR, tiles[cur ^ 1], tid);
-    __syncthreads();
-  }
-  if (active) {
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    if (cnt > k) {
-      select_compact(R, cnt, k);
-      cnt = k;
+    if (my_valid) {
+      __builtin_amdgcn_wave_barrier();
+      if (S.cnt > k) {
+        select_compact(wv, S.cnt, k);
+        S.cnt = k;
+      }
+      int32_t* out = idx + (size_t)my_row * k;
+      for (int j = lane; j < k; j += WAVE) out[j] = j < S.cnt ? s_cidx[wv][j] : -1;
     }
-    int32_t* out = idx + row * (int64_t)k;
-    for (int j = lane; j < k; j += WAVE) out[j] = j < cnt ? R.idx[j] : -1;
+    WAIT_VM_LGKM0(0);
+    __builtin_amdgcn_s_barrier();
   }
 }
 
@@ -185,9 +392,17 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(prefill_fill_kernel, dim3((unsigned)row_lo), dim3(256), 0, st, row_lo, a.k, a.idx);
   const int64_t n_rows = a.L - row_lo;
   if (n_rows > 0) {
-    dim3 grid((unsigned)((n_rows + 3) / 4));
-    hipLaunchKernelGGL(prefill_idx_topk_kernel, grid, dim3(256), 0, st, a.q8, a.qs, a.k8, a.ks, a.w, a.L,
-                       row_lo, a.k, a.idx);
+    static int n_cu = 0;
+    if (n_cu == 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+        n_cu = 256;
+    }
+    const int64_t n_groups = (n_rows + 3) / 4;
+    const int64_t blocks = n_groups < n_cu ? n_groups : n_cu;
+    hipLaunchKernelGGL(prefill_idx_topk_kernel, dim3((unsigned)blocks), dim3(PF_WAVES * 64), 0, st, a.q8, a.qs,
+                       a.k8, a.ks, a.w, (int)a.L, (int)row_lo, a.k, (int)n_groups, a.idx);
   }
   return hipGetLastError();
 }

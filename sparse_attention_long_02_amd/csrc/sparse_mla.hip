@@ -7,14 +7,19 @@
 // so its cost per query is O(k) (same sections).
 //
 // bf16 kernel (H = 128, d_qk = 576, d_v = 512), one block of 4 waves per query:
-//   * wave w owns heads 32w .. 32w+31 (two 16-head MFMA column blocks);
-//   * keys are processed in chunks of 32 gathered rows, double-buffered in LDS in two
-//     layouts: row-major K (1152 B/row + pad) and a transposed copy of the 512 latent
-//     values (V^T, 32 keys contiguous per value);
+//   * wave w owns heads 32w .. 32w+31 (two 16-head MFMA column blocks); its Q^T operands
+//     (144 registers) and O^T accumulators (256 fp32 registers) stay in registers;
+//   * keys are processed in chunks of 32 gathered rows.  The rows go straight from HBM to
+//     LDS with 16-byte direct loads (no staging registers; the latent half of a row is one
+//     wave-wide 1 KB load from a scalar address) into a ring of four buffers, so three
+//     chunks are in flight while one is computed;
 //   * logits are formed as S^T = K Q^T (keys = MFMA rows, heads = columns), so after the
 //     softmax each lane already holds P^T in the B-operand layout of the PV product
-//     O^T = V^T P^T: no register transpose of P is needed;
-//   * fp32 online softmax in base 2; O^T stays in 256 fp32 registers per lane.
+//     O^T = V^T P^T; V^T is read from the same row-major rows with the gfx950 transposing
+//     LDS read, so no transposed copy is stored;
+//   * fp32 online softmax in base 2 whose reference max moves only when a logit exceeds
+//     it by 8 (P then stays <= 256, exact enough in bf16), which keeps the 256-register
+//     rescale off the common path.
 // Keys may be split over several blocks (decode): each writes a normalised partial O and
 // its lse, and a combine kernel merges them.
 #include "dsa_device.h"
@@ -23,77 +28,163 @@
 namespace dsa {
 
 constexpr int MH = 128, MDQK = 576, MDV = 512, KC = 32;
-constexpr int KROW_STRIDE = MDQK * 2 + 16;        // bytes per key row in LDS
-constexpr int VT_STRIDE = KC * 2 + 16;            // bytes per latent value row of V^T
-constexpr int KROW_BYTES = KC * KROW_STRIDE;      // 37376
-constexpr int VT_BYTES = MDV * VT_STRIDE;         // 40960
-constexpr int BUF_BYTES = KROW_BYTES + VT_BYTES;  // 78336
+// LDS image of one chunk of 32 gathered rows, in two regions whose row pitches sit 4 banks
+// past a multiple of the bank count (so 8 consecutive rows read at one column hit distinct
+// banks, and every LDS read is a per-lane base plus an immediate offset):
+//   latent: values 0..511 of each row, 1040 B apart (1024 B + one unused 16-byte unit);
+//   rope:   values 512..575 of each row, 144 B apart (128 B + one unused unit).
+constexpr int LAT_PITCH = 1040, ROPE_PITCH = 144;
+constexpr int LAT_BYTES = KC * LAT_PITCH;                      // 33280
+constexpr int ROPE_UNITS = KC * ROPE_PITCH / 16;               // 288
+constexpr int ROPE_INSTR = (ROPE_UNITS + 63) / 64;             // 5
+constexpr int CHUNK_BYTES = LAT_BYTES + ROPE_INSTR * 64 * 16;  // 33280 + 5120 = 38400
+constexpr int MAX_K = 2048;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_SLACK = 8.f;              // log2 units the running max may lag
 
-// one chunk's worth of gathered 16-byte units held by a thread between load and store
-struct ChunkRegs {
-  v4i lat[8];  // keys 8*o .. 8*o+7, latent values 8*u .. 8*u+7
-  v4i rope;    // key t/8, rope values 512 + 8*(t%8) ..
-};
+#define VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
-__device__ __forceinline__ int64_t clamp_key(int32_t s, int64_t n_k) {
+__device__ __forceinline__ int64_t safe_row(int32_t s, int64_t n_k) {
   return (s >= 0 && s < n_k) ? (int64_t)s : 0;
 }
 
-__device__ __forceinline__ void load_chunk(ChunkRegs& R, const uint16_t* __restrict__ kvb,
-                                           const int32_t* __restrict__ keys, int tid, int64_t n_k) {
-  const int o = tid >> 6, u = tid & 63;
+// Issue this wave's direct global->LDS loads for chunk c (rows ids[32c .. 32c+31]):
+// the latent halves of rows 8w .. 8w+7 (one wave-wide 1 KB load each, scalar row
+// address) and rope instruction w (wave 0 also instruction 4).  Wave 0 issues 10 loads,
+// the others 9.
+__device__ __forceinline__ void gather_chunk(uint8_t* buf, const uint16_t* __restrict__ kvb,
+                                             const int32_t* ids, int c, int64_t n_k, int wv, int lane) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t s = clamp_key(keys[8 * o + j], n_k);
-    R.lat[j] = *reinterpret_cast<const v4i*>(kvb + s * MDQK + 8 * u);
+    const int r = 8 * wv + j;
+    const int64_t row = safe_row(__builtin_amdgcn_readfirstlane(ids[c * KC + r]), n_k);
+    __builtin_amdgcn_global_load_lds(kvb + row * MDQK + 8 * lane, buf + r * LAT_PITCH, 16, 0, 0);
   }
-  const int64_t s = clamp_key(keys[tid >> 3], n_k);
-  R.rope = *reinterpret_cast<const v4i*>(kvb + s * MDQK + 512 + 8 * (tid & 7));
-}
-
-__device__ __forceinline__ void store_chunk(const ChunkRegs& R, uint8_t* buf, int tid) {
-  const int o = tid >> 6, u = tid & 63;
-  uint8_t* krow = buf;
-  uint8_t* vt = buf + KROW_BYTES;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<v4i*>(krow + (8 * o + j) * KROW_STRIDE + 16 * u) = R.lat[j];
-  *reinterpret_cast<v4i*>(krow + (tid >> 3) * KROW_STRIDE + 1024 + 16 * (tid & 7)) = R.rope;
-  // 8x8 transpose of 16-bit values: row i of the output = value 8u+i of keys 8o..8o+7
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    v4i t;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      t[m] = (int)__builtin_amdgcn_perm((uint32_t)R.lat[2 * m + 1][i >> 1], (uint32_t)R.lat[2 * m][i >> 1], sel);
-    *reinterpret_cast<v4i*>(vt + (8 * u + i) * VT_STRIDE + 16 * o) = t;
+  for (int i = 0; i < 2; ++i) {
+    const int ins = wv + 4 * i;
+    if (ins < ROPE_INSTR) {
+      const int u = ins * 64 + lane;               // rope unit: row u / 9, unit u % 9 (8 = pad)
+      const int r = min(u / 9, KC - 1);
+      const int cu = u - (u / 9) * 9;
+      const int64_t row = safe_row(ids[c * KC + r], n_k);
+      __builtin_amdgcn_global_load_lds(kvb + row * MDQK + 512 + 8 * (cu & 7), buf + LAT_BYTES + ins * 1024, 16, 0, 0);
+    }
   }
 }
 
-// A operand of S^T: key block kb holds keys sigma(r) = 8*(r/4) + 4*kb + r%4 for MFMA row r,
-// so the four rows a lane group sees in the output are keys 8g+4kb .. 8g+4kb+3.
+// A operand of S^T for key block kb and d-step ds (values 32ds .. 32ds+31): MFMA row p is
+// key 16kb + p, so the output rows a lane group g sees are keys 16kb+4g .. 16kb+4g+3.
 __device__ __forceinline__ v8bf krow_frag(const uint8_t* buf, int kb, int ds) {
   const int l = lane_id();
-  const int r = l & 15, g = l >> 4;
-  const int key = 8 * (r >> 2) + 4 * kb + (r & 3);
-  return *reinterpret_cast<const v8bf*>(buf + key * KROW_STRIDE + 64 * ds + 16 * g);
+  const int r = 16 * kb + (l & 15);
+  const uint8_t* p = ds < 16 ? buf + r * LAT_PITCH + 64 * ds + 16 * (l >> 4)
+                             : buf + LAT_BYTES + r * ROPE_PITCH + 64 * (ds - 16) + 16 * (l >> 4);
+  return *reinterpret_cast<const v8bf*>(p);
 }
 
-// A operand of O^T = V^T P^T for latent values 16*db .. +15: row = value, 8 keys 8g..8g+7
+// A operand of O^T = V^T P^T for latent values 16*db .. +15 (rows); the contraction slots
+// of lane group g are keys 4g..4g+3 (first read) and 16+4g..16+4g+3 (second read), the
+// same keys in the same order as that lane's P^T slots.  The gfx950 transposing LDS read
+// does the transpose: in a 16-lane group, lanes 4rr..4rr+3 supply 16 values of one key
+// and lane p receives value 16db + p of the four keys.
+typedef short v4s __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v8bf vt_frag(const uint8_t* buf, int db) {
   const int l = lane_id();
-  return *reinterpret_cast<const v8bf*>(buf + KROW_BYTES + (16 * db + (l & 15)) * VT_STRIDE + 16 * (l >> 4));
+  const int p = l & 15, g = l >> 4;
+  const int rr = p >> 2, qq = p & 3;
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  const uint8_t* a0 = buf + (4 * g + rr) * LAT_PITCH + 32 * db + 8 * qq;
+  const uint8_t* a1 = a0 + 16 * LAT_PITCH;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(__attribute__((address_space(3))) uint8_t*)a0);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(__attribute__((address_space(3))) uint8_t*)a1);
+  const v8s v = v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(v8bf, v);
 }
 
-// grid.x = n_q * n_split, grid.y = B
+struct MlaState {
+  v8bf Qt[2][18];
+  v4f O[32][2];
+  float m_ref[2], l_run[2];
+};
+
+// One chunk: S^T = K Q^T, online softmax (base 2, lazily rescaled), O^T += V^T P^T.
+__device__ __forceinline__ void mla_chunk(MlaState& st, const uint8_t* buf, uint32_t vmask, float scale_log2) {
+  const int l = lane_id(), g = l >> 4;
+  v4f S[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) S[kb][0] = S[kb][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ds = 0; ds < 18; ++ds)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const v8bf a = krow_frag(buf, kb, ds);
+      S[kb][0] = mfma_bf16_16x16x32(a, st.Qt[0][ds], S[kb][0]);
+      S[kb][1] = mfma_bf16_16x16x32(a, st.Qt[1][ds], S[kb][1]);
+    }
+  v8bf P[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float z[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = (vmask >> (16 * (j >> 2) + 4 * g + (j & 3))) & 1u;
+      z[j] = ok ? S[j >> 2][hb][j & 3] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, z[j]);
+    }
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    // move the reference max only when a logit exceeds it by more than the slack
+    if (ballot(mx > st.m_ref[hb] + RESCALE_SLACK)) {
+      const float m_new = fmaxf(st.m_ref[hb], mx);
+      const float alpha = st.m_ref[hb] == -INFINITY ? 0.f : exp2f(st.m_ref[hb] - m_new);
+      st.l_run[hb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 32; ++db) st.O[db][hb] *= alpha;
+      st.m_ref[hb] = m_new;
+    }
+    const float m = st.m_ref[hb];
+    float ps = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float p0 = z[j] == -INFINITY ? 0.f : exp2f(z[j] - m);
+      const float p1 = z[j + 1] == -INFINITY ? 0.f : exp2f(z[j + 1] - m);
+      ps += p0 + p1;
+      pk[j >> 1] = pack_bf16x2(p0, p1);
+    }
+    ps += xor16(ps);
+    ps += xor32(ps);
+    st.l_run[hb] += ps;
+    const v4i pv = v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+    P[hb] = __builtin_bit_cast(v8bf, pv);
+  }
+#pragma unroll
+  for (int db = 0; db < 32; ++db) {
+    const v8bf a = vt_frag(buf, db);
+    st.O[db][0] = mfma_bf16_16x16x32(a, P[0], st.O[db][0]);
+    st.O[db][1] = mfma_bf16_16x16x32(a, P[1], st.O[db][1]);
+  }
+}
+
+__device__ __forceinline__ uint32_t chunk_mask(const int32_t* ids, int c, int64_t n_k) {
+  const int32_t s = ids[c * KC + (lane_id() & 31)];
+  return (uint32_t)ballot(s >= 0 && s < n_k);
+}
+
+// grid.x = n_q * n_split, grid.y = B.  Pipeline: chunk c+3 is in flight while chunk c is
+// computed (4 LDS buffers, loop unrolled by 4 so each buffer is a distinct static array).
 __global__ __launch_bounds__(256, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int64_t n_q, int64_t n_k, int k, float scale_log2, int n_split, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __align__(16) uint8_t smem[2 * BUF_BYTES];
+  __shared__ __align__(16) uint8_t buf0[CHUNK_BYTES];
+  __shared__ __align__(16) uint8_t buf1[CHUNK_BYTES];
+  __shared__ __align__(16) uint8_t buf2[CHUNK_BYTES];
+  __shared__ __align__(16) uint8_t buf3[CHUNK_BYTES];
+  __shared__ int32_t ids[MAX_K];
   __shared__ int32_t s_last[4];
 
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, g = l >> 4;
@@ -104,122 +195,74 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16_kernel(
   const int32_t* irow = idx + qrow * k;
   const uint16_t* kvb = kv + (int64_t)b * n_k * MDQK;
 
-  // number of chunks up to the last valid index of the row
-  int last = -1;
-  for (int j = tid; j < k; j += 256)
-    if (irow[j] >= 0 && irow[j] < n_k) last = j;
-  last = (int)wave_max((float)last);
-  if (l == 0) s_last[wv] = last;
-  __syncthreads();
-  last = max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3]));
-  const int nchunks = (last + KC) / KC;  // 0 if no valid key
-  const int c_lo = (int)((int64_t)nchunks * split / n_split);
-  const int c_hi = (int)((int64_t)nchunks * (split + 1) / n_split);
-
-  // Q^T B operands: head 32w + 16hb + l%16, values 32ds + 8g .. +7
-  v8bf Qt[2][18];
+  MlaState st;
   const uint16_t* qb = q + qrow * MH * MDQK;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
     for (int ds = 0; ds < 18; ++ds)
-      Qt[hb][ds] = *reinterpret_cast<const v8bf*>(qb + (32 * wv + 16 * hb + (l & 15)) * MDQK + 32 * ds + 8 * g);
+      st.Qt[hb][ds] = *reinterpret_cast<const v8bf*>(qb + (32 * wv + 16 * hb + (l & 15)) * MDQK + 32 * ds + 8 * g);
 
-  v4f O[32][2];
-#pragma unroll
-  for (int db = 0; db < 32; ++db) O[db][0] = O[db][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-  ChunkRegs CR;
-  if (c_lo < c_hi) {
-    load_chunk(CR, kvb, irow + c_lo * KC, tid, n_k);
-    store_chunk(CR, smem, tid);
+  // the row's selected ids -> LDS; chunks up to the last valid id
+  int last = -1;
+  for (int j = tid; j < k; j += 256) {
+    const int32_t s = irow[j];
+    ids[j] = s;
+    if (s >= 0 && s < n_k) last = j;
   }
+  last = (int)wave_max((float)last);
+  if (l == 0) s_last[wv] = last;
   __syncthreads();
-  for (int c = c_lo; c < c_hi; ++c) {
-    uint8_t* buf = smem + ((c - c_lo) & 1) * BUF_BYTES;
-    const bool more = c + 1 < c_hi;
-    // validity of the chunk's 32 keys (bit j = key j), wave-uniform
-    const int32_t my = irow[c * KC + (l & 31)];
-    const uint32_t vmask = (uint32_t)ballot(c * KC + (l & 31) < k && my >= 0 && my < n_k);
+  last = max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3]));
+  const int nchunks = (last + KC) / KC;
+  const int c_lo = (int)((int64_t)nchunks * split / n_split);
+  const int c_hi = (int)((int64_t)nchunks * (split + 1) / n_split);
 
-    // ---- S^T = K Q^T
-    v4f S[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) S[kb][0] = S[kb][1] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ds = 0; ds < 18; ++ds)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const v8bf a = krow_frag(buf, kb, ds);
-        S[kb][0] = mfma_bf16_16x16x32(a, Qt[0][ds], S[kb][0]);
-        S[kb][1] = mfma_bf16_16x16x32(a, Qt[1][ds], S[kb][1]);
-      }
+  for (int db = 0; db < 32; ++db) st.O[db][0] = st.O[db][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  st.m_ref[0] = st.m_ref[1] = -INFINITY;
+  st.l_run[0] = st.l_run[1] = 0.f;
 
-    // ---- online softmax per head (lane: head l%16 of block hb, keys 8g .. 8g+7)
-    v8bf P[2];
+  uint8_t* bufs[4] = {buf0, buf1, buf2, buf3};
+  const int n = c_hi - c_lo;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float z[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool ok = (vmask >> (8 * g + j)) & 1u;
-        z[j] = ok ? S[j >> 2][hb][j & 3] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, z[j]);
-      }
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run[hb], mx);
-      const bool any = m_new != -INFINITY;
-      const float alpha = any ? exp2f(m_run[hb] - m_new) : 1.f;
-      float ps = 0.f;
-      uint32_t pk[4];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float p0 = any ? exp2f(z[j] - m_new) : 0.f;
-        const float p1 = any ? exp2f(z[j + 1] - m_new) : 0.f;
-        ps += p0 + p1;
-        pk[j >> 1] = pack_bf16x2(p0, p1);
-      }
-      ps += xor16(ps);
-      ps += xor32(ps);
-      l_run[hb] = l_run[hb] * alpha + ps;
-      m_run[hb] = m_new;
-      if (ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < 32; ++db) O[db][hb] *= alpha;
-      }
-      v4i pv = v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-      P[hb] = __builtin_bit_cast(v8bf, pv);
-    }
+  for (int j = 0; j < 3; ++j)
+    if (j < n) gather_chunk(bufs[j], kvb, ids, c_lo + j, n_k, wv, l);
 
-    // ---- O^T += V^T P^T
+  for (int base = 0; base < n; base += 4) {
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const v8bf a = vt_frag(buf, db);
-      O[db][0] = mfma_bf16_16x16x32(a, P[0], O[db][0]);
-      O[db][1] = mfma_bf16_16x16x32(a, P[1], O[db][1]);
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j;  // chunk ordinal within this split
+      if (i < n) {
+        // chunk i must have landed (chunks i+1, i+2 may still be in flight), in every wave
+        if (wv == 0) {
+          if (i + 2 < n) VMCNT(20);
+          else if (i + 1 < n) VMCNT(10);
+          else VMCNT(0);
+        } else {
+          if (i + 2 < n) VMCNT(18);
+          else if (i + 1 < n) VMCNT(9);
+          else VMCNT(0);
+        }
+        __builtin_amdgcn_s_barrier();
+        if (i + 3 < n) gather_chunk(bufs[(j + 3) & 3], kvb, ids, c_lo + i + 3, n_k, wv, l);
+        mla_chunk(st, bufs[j], chunk_mask(ids, c_lo + i, n_k), scale_log2);
+      }
     }
-    if (more) {
-      load_chunk(CR, kvb, irow + (c + 1) * KC, tid, n_k);
-      store_chunk(CR, smem + ((c + 1 - c_lo) & 1) * BUF_BYTES, tid);
-    }
-    __syncthreads();
   }
 
   // ---- epilogue: lane holds head 32w+16hb+l%16, values 16db + 4g + i
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int head = 32 * wv + 16 * hb + (l & 15);
-    const bool nonempty = l_run[hb] > 0.f;
-    const float inv = nonempty ? 1.f / l_run[hb] : 0.f;
-    const float lse_v = nonempty ? (m_run[hb] + log2f(l_run[hb])) * LN2 : -INFINITY;
+    const bool nonempty = st.l_run[hb] > 0.f;
+    const float inv = nonempty ? 1.f / st.l_run[hb] : 0.f;
+    const float lse_v = nonempty ? (st.m_ref[hb] + log2f(st.l_run[hb])) * LN2 : -INFINITY;
     if (n_split == 1) {
       uint16_t* orow = out + (qrow * MH + head) * MDV;
 #pragma unroll
       for (int db = 0; db < 32; ++db) {
-        const v4f o = O[db][hb] * inv;
+        const v4f o = st.O[db][hb] * inv;
         uint2 pkd;
         pkd.x = pack_bf16x2(o[0], o[1]);
         pkd.y = pack_bf16x2(o[2], o[3]);
@@ -229,7 +272,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_bf16_kernel(
     } else {
       float* prow = part_o + ((qrow * n_split + split) * MH + head) * MDV;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) *reinterpret_cast<v4f*>(prow + 16 * db + 4 * g) = O[db][hb] * inv;
+      for (int db = 0; db < 32; ++db) *reinterpret_cast<v4f*>(prow + 16 * db + 4 * g) = st.O[db][hb] * inv;
       if (g == 0) part_lse[(qrow * n_split + split) * MH + head] = lse_v;
     }
   }

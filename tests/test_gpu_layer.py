@@ -1,0 +1,157 @@
+"""GPU parity of the whole layer (FP8 indexer -> top-k -> bf16 sparse MLA), prefill and
+decode, against the float64 oracle and against the library's own materialised scores."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_long_02_amd import dsa
+from sparse_attention_long_02_amd import synth as S
+from tests.helpers import dev_bf16, dev_f32, dev_u8, indexer_inputs_dev, out_to_f64, overlap
+
+pytestmark = pytest.mark.gpu
+
+ATOL_BF16 = 2e-2
+OVERLAP_MIN = 0.995
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _tol_ok(gpu_row, W, j, t, d_I):
+    """Row j of the widened operands is the query at position t."""
+    ref = O.indexer_row(W["qhat"][j], W["w"][j], W["khat"], t)
+    A = O.indexer_magnitude_row(W["qhat"][j], W["w"][j], W["khat"], t)
+    M = np.abs(W["w"][j]) @ (np.abs(W["qhat"][j]) @ np.abs(W["khat"][: t + 1]).T)
+    bound = 1e-2 * A + 2.0 * d_I * 2.0 ** -24 * M
+    err = np.abs(gpu_row[: t + 1] - ref)
+    return bool(np.all(err <= bound)), float((err / (bound + 1e-300)).max())
+
+
+@pytest.fixture(scope="module")
+def c2():
+    cfg = S.CONFIGS["prefill_8k"]
+    inp = S.make_prefill(cfg)
+    return cfg, inp
+
+
+def test_fused_selection_equals_topk_of_scores(c2):
+    """The fused indexer + streaming top-k selects exactly the top-k of the scores that
+    dsa_indexer writes (bit-identical scores, same tie rule), on every row of L = 8192."""
+    cfg, inp = c2
+    _say("[fused == topk(indexer)] L=8192")
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    fused = dsa.select_prefill(qi, qs, ki, ks, w, cfg.k)
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    ref = dsa.topk(scores, cfg.k)
+    torch.cuda.synchronize()
+    diff = (fused != ref).any(dim=1).nonzero().flatten().tolist()
+    assert not diff, f"{len(diff)} rows differ, first {diff[:5]}"
+    del scores
+
+
+@pytest.mark.parametrize("case", ["repeated_keys", "zero_rows", "small_k"])
+def test_fused_selection_ties(case):
+    """Heavy ties: repeated key rows (identical scores), all-zero query rows (every score
+    0), and a small k (many compactions)."""
+    _say(f"[fused ties] {case}")
+    cfg = S.CONFIGS["prefill_8k"].with_(L=6000)
+    inp = S.make_prefill(cfg)
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    k = cfg.k
+    if case == "repeated_keys":
+        ki = ki[torch.arange(cfg.L, device="cuda") % 37].contiguous()
+        ks = ks[torch.arange(cfg.L, device="cuda") % 37].contiguous()
+    elif case == "zero_rows":
+        qi = qi.clone()
+        qi[3000:3100] = 0
+        ki = ki.clone()
+        ki[100:2500] = 0
+    else:
+        k = 96
+    fused = dsa.select_prefill(qi, qs, ki, ks, w, k)
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    ref = dsa.topk(scores, k)
+    torch.cuda.synchronize()
+    diff = (fused != ref).any(dim=1).nonzero().flatten().tolist()
+    assert not diff, f"{len(diff)} rows differ, first {diff[:5]}"
+    if case == "zero_rows":   # an all-zero query row scores 0 everywhere: the first k keys win
+        row = fused[3050].cpu().numpy()
+        assert np.array_equal(row, np.arange(k))
+
+
+def test_prefill_end_to_end_vs_oracle(c2):
+    cfg, inp = c2
+    _say("[prefill e2e vs oracle] L=8192")
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    q, kv = dev_bf16(inp.q), dev_bf16(inp.kv)
+    idx, out, lse = dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, cfg.k, cfg.sm_scale, cfg.d_v)
+    idx2, out2, lse2 = dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, cfg.k, cfg.sm_scale, cfg.d_v)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(out, out2) and torch.equal(lse, lse2), "not deterministic"
+    rng = np.random.default_rng(21)
+    rows = np.array(sorted(set([0, 1, cfg.k - 2, cfg.k - 1, cfg.k, cfg.k + 1, cfg.L - 1]) |
+                           set(int(x) for x in rng.integers(0, cfg.L, 41))))
+    W = O.widen_inputs(inp, rows)
+    Wk = {"qhat": W["qhat"], "w": W["w"], "khat": W["khat"]}
+    ref = O.dsa_rows(W["qhat"], W["w"], W["khat"], W["q"], W["kv"], W["v"], rows, cfg.k, cfg.sm_scale)
+    g_idx = idx.cpu().numpy()[rows]
+    ov, worst = overlap(g_idx, ref["idx"])
+    _say(f"  selected-set overlap {ov:.5f} (worst row {worst:.4f})")
+    assert ov >= OVERLAP_MIN
+    o_ref, l_ref = O.sparse_mqa(W["q"], W["kv"], W["v"], g_idx, cfg.sm_scale)
+    got = out_to_f64(out)[rows]
+    err = float(np.abs(got - o_ref).max())
+    _say(f"  attention max-abs on the GPU's selection {err:.3e}")
+    assert err <= ATOL_BF16
+    e2e = float(np.abs(got - ref["out"]).max())
+    _say(f"  end-to-end max-abs vs the oracle's own selection {e2e:.3e} (reported)")
+    gl = lse.cpu().numpy()[rows]
+    assert np.allclose(gl, l_ref, atol=1e-3, rtol=1e-4)
+    # the library's scores of these rows, against the oracle's
+    worst_rel = 0.0
+    for j, t in enumerate(rows):
+        g = dsa.indexer(qi, qs, ki, ks, w, row_begin=int(t), n_rows=1)[0].cpu().numpy().astype(np.float64)
+        ok, rel = _tol_ok(g, Wk, j, int(t), cfg.d_I)
+        worst_rel = max(worst_rel, rel)
+        assert ok, (t, rel)
+    _say(f"  indexer worst error / bound {worst_rel:.3e}")
+
+
+def test_decode_small_batch():
+    """Decode over caches of different lengths: selection == top-k of the library's scores,
+    overlap with the oracle, attention on the GPU's selection."""
+    cfg = S.CONFIGS["decode_64x128k"].with_(L=6000, batch=4)
+    _say("[decode] B=4, n_k_max=6000")
+    inp = S.make_decode(cfg)
+    ctx_l = [1, 2048, 2049, 6000]
+    ctx = torch.tensor(ctx_l, dtype=torch.int32, device="cuda")
+    qi, qs, w = dev_u8(inp.qi), dev_f32(inp.q_scale), dev_f32(inp.w)
+    kc, kcs = dev_u8(inp.ki), dev_f32(inp.k_scale)
+    q, kvc = dev_bf16(inp.q), dev_bf16(inp.kv)
+    idx, out, lse = dsa.forward_decode(ctx, qi, qs, w, kc, kcs, q, kvc, cfg.k, cfg.sm_scale, cfg.d_v)
+    # the same through the stage entry points
+    qpos = ctx - 1
+    scores = dsa.indexer(qi[:, None], qs[:, None], kc, kcs, w[:, None], q_pos=qpos)
+    ref_idx = dsa.topk(scores, cfg.k, q_pos=qpos)[:, 0]
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref_idx)
+    g_idx = idx.cpu().numpy()
+    got = out_to_f64(out)
+    for b in range(cfg.batch):
+        pos = ctx_l[b] - 1
+        qhat = O.dequant(inp.qi[b][None], inp.q_scale[b][None])
+        khat = O.dequant(inp.ki[b], inp.k_scale[b])
+        kvf = O.bf16_to_f64(inp.kv[b])
+        qf = O.bf16_to_f64(inp.q[b])[None]
+        r = O.dsa_rows(qhat, inp.w[b][None].astype(np.float64), khat, qf, kvf, kvf[:, :512], np.array([pos]),
+                       cfg.k, cfg.sm_scale)
+        ov, _ = overlap(g_idx[b][None], r["idx"])
+        assert ov >= OVERLAP_MIN, (b, ov)
+        o, l = O.sparse_mqa(qf, kvf, kvf[:, :512], g_idx[b][None], cfg.sm_scale)
+        assert np.abs(got[b] - o[0]).max() <= ATOL_BF16, b
+        assert np.allclose(lse[b].cpu().numpy(), l[0], atol=1e-3, rtol=1e-4)
