@@ -5,14 +5,16 @@
 // LDS:
 //   * a candidate buffer (order-preserving key + index) that stays sorted by key index,
 //     because keys arrive in ascending order and appends keep lane order;
-//   * a threshold thr: once the buffer has been cut to exactly k entries, v* = the k-th
-//     largest key so far, and a later key can only enter with a strictly larger key
-//     (on a tie it has the larger index, and the lower index wins);
-//   * when the buffer is nearly full, a wave-local radix select (8-bit digits over an LDS
-//     histogram, starting at the highest bit where the candidates differ) finds v* and an
-//     in-place stable compaction keeps exactly the top-k so far.
-// At the end the buffer holds the row's selection in ascending key order.  Rows whose
-// position is below k keep every key and are written by a separate fill kernel.
+//   * a threshold thr: a later key enters only if its key is > thr;
+//   * when the buffer is nearly full it is cut: a wave-local radix descent (8-bit digits
+//     over an LDS histogram, starting at the highest bit where the candidates can differ)
+//     finds the bin holding the k-th largest key, and an in-place stable compaction keeps
+//     the keys >= that bin's lower edge, which becomes the new bound (thr = edge - 1).  If
+//     that would free too little room (many equal keys), the exact selection runs instead:
+//     v* = the k-th largest key exactly, keep exactly the top k so far, thr = v* (a later
+//     key equal to v* has a larger index, and on a tie the lower index wins).
+// At the end an exact selection leaves the row's top k, in ascending key order.
+// Rows whose position is below k keep every key and are written by a separate fill kernel.
 //
 // Selection rule: top-k by index score with ties to the lower key index (juhe.plus
 // explainer, section 第二步：Fine-grained Token Selection; 53ai.com V3.2-Exp summary,
@@ -46,25 +48,123 @@ __device__ __forceinline__ void lds_inc(uint32_t* p) {
 __device__ __forceinline__ void lds_store(void* p, float v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
 }
-// 16-byte LDS read that completes inside the same asm block (same reason as lds_inc).
+// LDS reads that complete inside the same asm block (same reason as lds_inc: a plain read
+// of the tile ring or of the exchange buffers would first wait for every tile load in flight).
 __device__ __forceinline__ v4i lds_read16_sync(const void* p) {
   v4i r;
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr(p)) : "memory");
   return r;
 }
+__device__ __forceinline__ float lds_read4_sync(const void* p) {
+  float r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr(p)) : "memory");
+  return r;
+}
+__device__ __forceinline__ void lds_read4x2_sync(const void* p0, const void* p1, float& a, float& b) {
+  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b)
+               : "v"(lds_addr(p0)), "v"(lds_addr(p1))
+               : "memory");
+}
 
-constexpr int SEL_BATCH = 8;  // entries per lane in flight per pass step
+constexpr int SEL_BATCH = 8;   // entries per lane in flight per pass step
+constexpr int CUT_SLACK = 256; // a cut may keep at most this many keys below the k-th largest
 
-// Radix select of the k-th largest key among s_ckey[r][0..n) (n > k), then stable in-place
-// compaction to exactly k entries.  Wave-local.  The digits start at the highest bit where
-// the candidates differ (they share their top bits, which would pile every candidate into
-// one histogram bin).  Every pass reads SEL_BATCH entries per lane before using them.
-// Returns v*.
-__device__ uint32_t select_compact(int r, int n, int k) {
+// One radix digit of the k-th largest key among s_ckey[r][0..n): histogram (8-bit digits
+// at `shift`) of the keys whose bits under `pmask` equal `prefix`, then the digit d where
+// the count from the top reaches `rem`.  Returns d; `above` = keys in higher bins, `binc` =
+// keys in bin d.
+__device__ __forceinline__ uint32_t digit_step(int r, int n, int shift, uint32_t dmask, uint32_t pmask,
+                                               uint32_t prefix, uint32_t rem, uint32_t& above, uint32_t& binc) {
+  const int lane = lane_id();
+  const uint32_t* key = s_ckey[r];
+  uint32_t* hist = s_hist[r];
+  *reinterpret_cast<v4i*>(hist + 4 * lane) = v4i{0, 0, 0, 0};
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
+    uint32_t u[SEL_BATCH];
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m) {
+      const int i = base + WAVE * m + lane;
+      u[m] = key[i < n ? i : 0];
+    }
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m)
+      if ((base + WAVE * m + lane < n) & ((u[m] & pmask) == prefix)) lds_inc(&hist[(u[m] >> shift) & dmask]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane owns bins 255-4*lane .. 252-4*lane (descending)
+  const v4i hv = lds_read16_sync(hist + 252 - 4 * lane);
+  const uint32_t h[4] = {(uint32_t)hv[3], (uint32_t)hv[2], (uint32_t)hv[1], (uint32_t)hv[0]};
+  const uint32_t local = h[0] + h[1] + h[2] + h[3];
+  uint32_t c = wave_incl_scan(local) - local;
+  uint32_t digit = 0, ab = 0, bc = 0;
+  bool found = false;
+  if (c < rem && c + local >= rem) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && c + h[j] >= rem) {
+        found = true;
+        digit = 255u - 4u * lane - j;
+        ab = c;
+        bc = h[j];
+      }
+      c += h[j];
+    }
+  }
+  const uint64_t fm = ballot(found);
+  const int src = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
+  above = __shfl(ab, src, WAVE);
+  binc = __shfl(bc, src, WAVE);
+  return __shfl(digit, src, WAVE);
+}
+
+// Stable in-place compaction of s_ckey/s_cidx[r][0..n): keeps the keys > gt and the first
+// `rem_eq` keys equal to `eq` (in buffer order, i.e. lowest key index first).  All entries
+// of a batch are read before any is written, and an entry only moves down, so no unread
+// entry is overwritten.  Returns the number kept.
+__device__ __forceinline__ int compact_keep(int r, int n, uint32_t gt, uint32_t eq, uint32_t rem_eq) {
   const int lane = lane_id();
   uint32_t* key = s_ckey[r];
   int32_t* id = s_cidx[r];
-  uint32_t* hist = s_hist[r];
+  uint32_t kept = 0, eq_seen = 0;
+  for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
+    uint32_t u[SEL_BATCH];
+    int32_t ix[SEL_BATCH];
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m) {
+      const int i = base + WAVE * m + lane;
+      u[m] = key[i < n ? i : 0];
+      ix[m] = id[i < n ? i : 0];
+    }
+#pragma unroll
+    for (int m = 0; m < SEL_BATCH; ++m) {
+      const bool in = base + WAVE * m + lane < n;
+      const bool is_eq = in & (u[m] == eq);
+      const uint64_t me = ballot(is_eq);
+      const bool keep = (in & (u[m] > gt)) | (is_eq & (eq_seen + lanes_below(me) < rem_eq));
+      const uint64_t mk = ballot(keep);
+      if (keep) {
+        const uint32_t dst = kept + lanes_below(mk);
+        key[dst] = u[m];
+        id[dst] = ix[m];
+      }
+      kept += (uint32_t)__popcll((unsigned long long)mk);
+      eq_seen += (uint32_t)__popcll((unsigned long long)me);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  return (int)kept;
+}
+
+// Exact selection: radix select of v* = the k-th largest key among s_ckey[r][0..n) (n > k),
+// then stable compaction to exactly k entries (keys > v*, then the lowest-index keys equal
+// to v*).  Wave-local.  The digits start at the highest bit where the keys differ (they
+// share their top bits, which would pile every key into one histogram bin).  Returns v*.
+__device__ uint32_t select_compact(int r, int n, int k) {
+  const int lane = lane_id();
+  const uint32_t* key = s_ckey[r];
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
     uint32_t u[SEL_BATCH];
@@ -86,51 +186,16 @@ __device__ uint32_t select_compact(int r, int n, int k) {
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
   }
   uint32_t rem = (uint32_t)k;
-  uint32_t prefix = mx, pmask = 0xFFFFFFFFu;
+  uint32_t prefix = mx;
   if (mn != mx) {
     int hi = 31 - __clz((int)(mn ^ mx));  // highest differing bit
-    pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+    uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
     prefix = mx & pmask;
     while (true) {
       const int shift = hi >= 7 ? hi - 7 : 0;
       const uint32_t dmask = (2u << (hi - shift)) - 1u;
-      *reinterpret_cast<v4i*>(hist + 4 * lane) = v4i{0, 0, 0, 0};
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-      for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
-        uint32_t u[SEL_BATCH];
-#pragma unroll
-        for (int m = 0; m < SEL_BATCH; ++m) {
-          const int i = base + WAVE * m + lane;
-          u[m] = key[i < n ? i : 0];
-        }
-#pragma unroll
-        for (int m = 0; m < SEL_BATCH; ++m)
-          if (base + WAVE * m + lane < n && (u[m] & pmask) == prefix) lds_inc(&hist[(u[m] >> shift) & dmask]);
-      }
-      __builtin_amdgcn_wave_barrier();
-      // lane owns bins 255-4*lane .. 252-4*lane (descending)
-      const v4i hv = lds_read16_sync(hist + 252 - 4 * lane);
-      const uint32_t h[4] = {(uint32_t)hv[3], (uint32_t)hv[2], (uint32_t)hv[1], (uint32_t)hv[0]};
-      const uint32_t local = h[0] + h[1] + h[2] + h[3];
-      uint32_t c = wave_incl_scan(local) - local;
-      uint32_t digit = 0, above = 0;
-      bool found = false;
-      if (c < rem && c + local >= rem) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!found && c + h[j] >= rem) {
-            found = true;
-            digit = 255u - 4u * lane - j;
-            above = c;
-          }
-          c += h[j];
-        }
-      }
-      const uint64_t fm = ballot(found);
-      const int src = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
-      digit = __shfl(digit, src, WAVE);
-      above = __shfl(above, src, WAVE);
+      uint32_t above, binc;
+      const uint32_t digit = digit_step(r, n, shift, dmask, pmask, prefix, rem, above, binc);
       rem -= above;
       prefix |= digit << shift;
       pmask |= dmask << shift;
@@ -138,36 +203,39 @@ __device__ uint32_t select_compact(int r, int n, int k) {
       hi = shift - 1;
     }
   }
-  // keep key > v*, and the first `rem` keys equal to v* (lowest indices).  All entries of a
-  // batch are read before any is written, and an entry only moves down, so the in-place
-  // stable compaction never overwrites an unread entry.
-  uint32_t kept = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += WAVE * SEL_BATCH) {
-    uint32_t u[SEL_BATCH];
-    int32_t ix[SEL_BATCH];
-#pragma unroll
-    for (int m = 0; m < SEL_BATCH; ++m) {
-      const int i = base + WAVE * m + lane;
-      u[m] = key[i < n ? i : 0];
-      ix[m] = id[i < n ? i : 0];
+  compact_keep(r, n, prefix, prefix, rem);
+  return prefix;
+}
+
+// Cut: keeps every key that can still be among the row's k best, without finding v*
+// exactly.  Descends the radix digits of the k-th largest key only until its bin holds at
+// most CUT_SLACK keys below it; the keys >= that bin's lower edge e are then kept (at least
+// k keys are >= e, so no key below e can reach the top k).  `lo` <= every key <= `mx`.
+// The buffer is compacted only if at most `max_keep` keys would remain.  Returns e, or 0
+// (buffer untouched) if no such cut exists; `kept` = entries left.
+__device__ uint32_t cut_candidates(int r, int n, int k, uint32_t lo, uint32_t mx, int max_keep, int& kept) {
+  kept = n;
+  if (lo >= mx) return 0u;
+  int hi = 31 - __clz((int)(lo ^ mx));
+  uint32_t pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+  uint32_t prefix = mx & pmask;
+  uint32_t rem = (uint32_t)k;
+  while (true) {
+    const int shift = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (2u << (hi - shift)) - 1u;
+    uint32_t above, binc;
+    const uint32_t digit = digit_step(r, n, shift, dmask, pmask, prefix, rem, above, binc);
+    rem -= above;
+    prefix |= digit << shift;
+    pmask |= dmask << shift;
+    if (binc - rem <= (uint32_t)CUT_SLACK || shift == 0) {
+      // keys >= the bin's lower edge: those in higher bins at every level, plus the bin
+      if (prefix == 0u || (int)((uint32_t)k - rem + binc) > max_keep) return 0u;
+      break;
     }
-#pragma unroll
-    for (int m = 0; m < SEL_BATCH; ++m) {
-      const bool in = base + WAVE * m + lane < n;
-      const bool eq = in && u[m] == prefix;
-      const uint64_t me = ballot(eq);
-      const bool keep = (in && u[m] > prefix) || (eq && eq_seen + lanes_below(me) < rem);
-      const uint64_t mk = ballot(keep);
-      if (keep) {
-        const uint32_t dst = kept + lanes_below(mk);
-        key[dst] = u[m];
-        id[dst] = ix[m];
-      }
-      kept += (uint32_t)__popcll((unsigned long long)mk);
-      eq_seen += (uint32_t)__popcll((unsigned long long)me);
-    }
+    hi = shift - 1;
   }
-  __builtin_amdgcn_wave_barrier();
+  kept = compact_keep(r, n, prefix - 1u, 0u, 0u);
   return prefix;
 }
 
@@ -179,16 +247,14 @@ __device__ uint32_t select_compact(int r, int n, int k) {
 // of all 4 rows and writes its half-totals to LDS; wave j < 4 also owns row j's selection.
 // Key tiles arrive by direct global->LDS loads in a ring of 4 buffers (three in flight).
 //
-// The two waves sharing a SIMD (w and w+4) run out of phase, so one's VALU work covers the
-// other's MFMAs: waves 0-3 issue tile i's MFMAs then fold them; waves 4-7 first fold the
-// MFMA results of tile i-1 kept in registers, then issue tile i's MFMAs.  Tile t's half
-// totals are therefore complete after step t+1, and the owners take tile t at step t+2.
+// Every wave issues its 8 MFMAs of tile i, then folds them; an owner takes tile i-1 (whose
+// half-totals were completed before this step's barrier) between the two, while the other
+// wave on its SIMD keeps the matrix core busy.
 // When any owner's buffer nears full, all four owners compact at the same step (one stall
 // of the block instead of four).
 // ---------------------------------------------------------------------------------------
 constexpr int PF_WAVES = 8;
 constexpr int TILE_BYTES = KEY_TILE * IDX_DIM;
-constexpr int XSLOTS = 3;                       // tile score exchange ring
 constexpr int COMPACT_AT = CAND - 3 * KEY_TILE;  // collective compaction trigger
 
 #define WAIT_VM_LGKM0(n) \
@@ -208,9 +274,10 @@ __device__ __forceinline__ TileDma tile_dma_lane(int wv, int lane) {
 __device__ __forceinline__ void dma_key_tile(uint8_t* tk, float* ts, const uint8_t* __restrict__ k8,
                                              const float* __restrict__ ks, int key0, int L, const TileDma& d,
                                              int wv, int lane) {
-  const int key = min(key0 + d.krow, L - 1);
-  __builtin_amdgcn_global_load_lds(k8 + (size_t)key * IDX_DIM + d.koff, tk + 1024 * wv, 16, 0, 0);
-  if (wv == 0) __builtin_amdgcn_global_load_lds(ks + min(key0 + lane, L - 1), ts, 4, 0, 0);
+  // 32-bit offsets from the uniform bases (L * 128 < 2^32 for every supported L)
+  const uint32_t key = (uint32_t)min(key0 + d.krow, L - 1);
+  __builtin_amdgcn_global_load_lds(k8 + (key * IDX_DIM + d.koff), tk + 1024 * wv, 16, 0, 0);
+  if (wv == 0) __builtin_amdgcn_global_load_lds(ks + (uint32_t)min(key0 + lane, L - 1), ts, 4, 0, 0);
 }
 
 // wait until tile i has landed: tiles i+1, i+2 (if they exist) may still be in flight;
@@ -228,17 +295,33 @@ __device__ __forceinline__ void wait_tile(int i, int ntiles, int wv) {
   }
 }
 
+// B operand of fragment f of a tile in the ring (the layout lds_key_fragment reads),
+// fetched with both reads completing inside one asm block.
+__device__ __forceinline__ v8i ring_key_fragment(const uint8_t* tile, int f, int lane) {
+  const int row = 16 * f + (lane & 15);
+  const int c0 = (2 * (lane >> 4)) ^ (row & 7);
+  const int c1 = (2 * (lane >> 4) + 1) ^ (row & 7);
+  v4i lo, hi;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(lo), "=&v"(hi)
+               : "v"(lds_addr(tile + row * IDX_DIM + 16 * c0)), "v"(lds_addr(tile + row * IDX_DIM + 16 * c1))
+               : "memory");
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 struct OwnerState {
   int cnt;
-  uint32_t thr;
+  uint32_t thr;  // a key enters only if it is > thr
+  uint32_t lo;   // every buffered key is >= lo
+  uint32_t mx;   // this lane's largest key appended so far
   float cmax;
-  float ksc[2];  // key scales of the two tiles not yet taken
+  float ksc;  // key scales (this lane's key) of the tile not yet taken
 };
 
-__shared__ int s_cnt[4];  // owners' published candidate counts
+__shared__ __align__(16) int s_cnt[4];  // owners' published candidate counts
 // Half-totals of tile scores exchanged between the scoring waves and the owners
-// ([tile % 3][head half][row][key]).
-__shared__ float xbuf[XSLOTS][2][4][KEY_TILE];
+// ([tile % 2][head half][row][key]).
+__shared__ float xbuf[2][2][4][KEY_TILE];
 
 // Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer; compact
 // when this buffer is full or when any owner's buffer nears full (all compact together).
@@ -253,14 +336,28 @@ __device__ __forceinline__ void owner_take(OwnerState& S, int r, float s, int ke
       const int off = S.cnt + (int)lanes_below(m);
       s_ckey[r][off] = u;
       s_cidx[r][off] = key;
+      S.mx = max(S.mx, u);
     }
     S.cnt += __popcll((unsigned long long)m);
   }
-  const int most = max(max(s_cnt[0], s_cnt[1]), max(s_cnt[2], s_cnt[3]));
-  if (S.cnt > CAND - KEY_TILE || (most > COMPACT_AT && S.cnt > k)) {
+  const v4i c = lds_read16_sync(s_cnt);
+  const int most = max(max(c[0], c[1]), max(c[2], c[3]));
+  if (S.cnt > CAND - KEY_TILE || (most > COMPACT_AT && S.cnt > k + 4 * KEY_TILE)) {
     __builtin_amdgcn_wave_barrier();
-    S.thr = select_compact(r, S.cnt, k);
-    S.cnt = k;
+    uint32_t mx = S.mx;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
+    int kept;
+    const uint32_t e = cut_candidates(r, S.cnt, k, S.lo, mx, CAND - 4 * KEY_TILE, kept);
+    if (e != 0u) {
+      S.thr = e - 1u;
+      S.lo = e;
+      S.cnt = kept;
+    } else {  // the cut freed too little (many equal keys): select exactly
+      S.thr = select_compact(r, S.cnt, k);
+      S.lo = S.thr;
+      S.cnt = k;
+    }
   }
 }
 
@@ -281,7 +378,7 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
   float* const tss[4] = {ts0, ts1, ts2, ts3};
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int f = wv >> 1, hh = wv & 1;
-  const bool lead = wv < 4;  // MFMA-then-fold role; also the row owners
+  const bool lead = wv < 4;  // waves 0-3 also own one row each
   const TileDma dl = tile_dma_lane(wv, lane);
 
   for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
@@ -298,68 +395,50 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     }
     const int my_row = row0 + (wv & 3);
     const bool my_valid = lead && my_row >= row_lo;
-    OwnerState S{0, 0u, cm[wv & 3], {0.f, 0.f}};
-    if (lead && lane == 0) s_cnt[wv] = 0;
+    OwnerState S{0, 0u, 0u, 0u, cm[wv & 3], 0.f};
+    if (lead && lane == 0) lds_store(&s_cnt[wv], __int_as_float(0));
     const int ntiles = (row_hi + KEY_TILE - 1) / KEY_TILE;
-    v4f xprev[4][2];  // trailing waves: MFMA results of the previous tile
+    v4f xr[4][2];  // this tile's MFMA results
 
 #pragma unroll
     for (int j = 0; j < 3; ++j)
       if (j < ntiles) dma_key_tile(tks[j], tss[j], k8, ks, j * KEY_TILE, L, dl, wv, lane);
 
-    for (int base = 0; base < ntiles + 2; base += 4) {
+    for (int base = 0; base <= ntiles; base += 4) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int i = base + jj;
-        if (i < ntiles + 2) {
+        if (i <= ntiles) {
           if (i < ntiles) wait_tile(i, ntiles, wv);
           else WAIT_VM_LGKM0(0);
           __builtin_amdgcn_s_barrier();
           if (i + 3 < ntiles) dma_key_tile(tks[(jj + 3) & 3], tss[(jj + 3) & 3], k8, ks, (i + 3) * KEY_TILE, L, dl, wv, lane);
-          if (lead) {
-            v4f x[4][2];
-            float ksc_i = 0.f;
-            if (i < ntiles) {
-              ksc_i = tss[jj][lane];
-              const v8i b = lds_key_fragment(tks[jj], f);
+          float ksc_i = 0.f;
+          if (i < ntiles) {
+            if (lead) ksc_i = lds_read4_sync(tss[jj] + lane);
+            const v8i b = ring_key_fragment(tks[jj], f, lane);
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                x[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
-                x[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
-              }
+            for (int j = 0; j < 4; ++j) {
+              xr[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
+              xr[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            // take tile i-2 (its key scales sit in ring slot i%2), then keep tile i's scales there
-            if (i >= 2 && my_valid) {
-              const int t = i - 2, slot = t % XSLOTS;
-              const float x0 = xbuf[slot][0][wv][lane], x1 = xbuf[slot][1][wv][lane];
-              owner_take(S, wv, finish_score(x0, x1, S.cmax, S.ksc[i & 1]), t * KEY_TILE, my_row, k);
-              if (lane == 0) s_cnt[wv] = S.cnt;
-            }
-            S.ksc[i & 1] = ksc_i;
-            __builtin_amdgcn_sched_barrier(0);
-            if (i < ntiles) {
-              float p[4];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // an owner takes tile i-1 while tile i's MFMAs run
+          if (i >= 1 && my_valid) {
+            const int t = i - 1, slot = t & 1;
+            float x0, x1;
+            lds_read4x2_sync(&xbuf[slot][0][wv][lane], &xbuf[slot][1][wv][lane], x0, x1);
+            owner_take(S, wv, finish_score(x0, x1, S.cmax, S.ksc), t * KEY_TILE, my_row, k);
+            if (lane == 0) lds_store(&s_cnt[wv], __int_as_float(S.cnt));
+          }
+          S.ksc = ksc_i;
+          __builtin_amdgcn_sched_barrier(0);
+          if (i < ntiles) {
+            float p[4];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], x[j][0], x[j][1]);
-              lds_store(&xbuf[i % XSLOTS][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
-            }
-          } else {
-            if (i >= 1 && i <= ntiles) {
-              float p[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], xprev[j][0], xprev[j][1]);
-              lds_store(&xbuf[(i - 1) % XSLOTS][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (i < ntiles) {
-              const v8i b = lds_key_fragment(tks[jj], f);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                xprev[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
-                xprev[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
-              }
-            }
+            for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], xr[j][0], xr[j][1]);
+            lds_store(&xbuf[i & 1][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
           }
         }
       }

@@ -54,10 +54,11 @@ def test_fused_selection_equals_topk_of_scores(c2):
     del scores
 
 
-@pytest.mark.parametrize("case", ["repeated_keys", "zero_rows", "small_k"])
+@pytest.mark.parametrize("case", ["repeated_keys", "zero_rows", "zero_prefix", "small_k"])
 def test_fused_selection_ties(case):
     """Heavy ties: repeated key rows (identical scores), all-zero query rows (every score
-    0), and a small k (many compactions)."""
+    0), a run of all-zero keys longer than the candidate buffer (every buffer cut ends in
+    the exact tie-breaking selection), and a small k (many compactions)."""
     _say(f"[fused ties] {case}")
     cfg = S.CONFIGS["prefill_8k"].with_(L=6000)
     inp = S.make_prefill(cfg)
@@ -71,6 +72,9 @@ def test_fused_selection_ties(case):
         qi[3000:3100] = 0
         ki = ki.clone()
         ki[100:2500] = 0
+    elif case == "zero_prefix":
+        ki = ki.clone()
+        ki[:5000] = 0
     else:
         k = 96
     fused = dsa.select_prefill(qi, qs, ki, ks, w, k)
