@@ -240,20 +240,21 @@ __device__ uint32_t cut_candidates(int r, int n, int k, uint32_t lo, uint32_t mx
 }
 
 // ---------------------------------------------------------------------------------------
-// Persistent fused kernel.  A block of 8 waves owns groups of 4 consecutive rows; blocks
-// take groups longest-first in lockstep (group G = block + round * blocks), so the blocks
-// on one XCD sweep the same key tiles at about the same time and the tiles stay in L2.
-// Wave w scores key fragment f = w/2 (16 keys of each 64-key tile) for head half hh = w%2
-// of all 4 rows and writes its half-totals to LDS; wave j < 4 also owns row j's selection.
+// Persistent fused kernel.  A block owns groups of 4 consecutive rows; blocks take groups
+// longest-first in lockstep (group G = block + round * blocks), so the blocks on one XCD
+// sweep the same key tiles at about the same time and the tiles stay in L2.
+//   * scoring waves 0-7: wave w scores key fragment f = w/2 (16 keys of each 64-key tile)
+//     for head half hh = w%2 of all 4 rows: 8 MFMAs, then the fold, then its half-totals
+//     go to LDS.  The two scoring waves of a SIMD keep its matrix core busy.
+//   * owner waves 8-11: wave 8+j owns row j's selection.  At step i it takes tile i-1
+//     (whose half-totals were completed before the step's barrier), in the VALU and LDS
+//     issue slots the scoring waves leave free.
 // Key tiles arrive by direct global->LDS loads in a ring of 4 buffers (three in flight).
-//
-// Every wave issues its 8 MFMAs of tile i, then folds them; an owner takes tile i-1 (whose
-// half-totals were completed before this step's barrier) between the two, while the other
-// wave on its SIMD keeps the matrix core busy.
-// When any owner's buffer nears full, all four owners compact at the same step (one stall
-// of the block instead of four).
+// When any owner's buffer nears full, all four owners cut at the same step (one stall of
+// the block instead of four).
 // ---------------------------------------------------------------------------------------
-constexpr int PF_WAVES = 8;
+constexpr int PF_SCORE_WAVES = 8;
+constexpr int PF_WAVES = PF_SCORE_WAVES + 4;
 constexpr int TILE_BYTES = KEY_TILE * IDX_DIM;
 constexpr int COMPACT_AT = CAND - 3 * KEY_TILE;  // collective compaction trigger
 
@@ -281,7 +282,8 @@ __device__ __forceinline__ void dma_key_tile(uint8_t* tk, float* ts, const uint8
 }
 
 // wait until tile i has landed: tiles i+1, i+2 (if they exist) may still be in flight;
-// wave 0 issues two loads per tile, the others one.  Also drains this wave's LDS ops.
+// wave 0 issues two loads per tile, the other scoring waves one.  Also drains this wave's
+// LDS ops.
 __device__ __forceinline__ void wait_tile(int i, int ntiles, int wv) {
   const int after = min(2, ntiles - 1 - i);
   if (wv == 0) {
@@ -315,7 +317,7 @@ struct OwnerState {
   uint32_t lo;   // every buffered key is >= lo
   uint32_t mx;   // this lane's largest key appended so far
   float cmax;
-  float ksc;  // key scales (this lane's key) of the tile not yet taken
+  float ksc;  // key scale (this lane's key) of the tile not yet taken
 };
 
 __shared__ __align__(16) int s_cnt[4];  // owners' published candidate counts
@@ -323,9 +325,21 @@ __shared__ __align__(16) int s_cnt[4];  // owners' published candidate counts
 // ([tile % 2][head half][row][key]).
 __shared__ float xbuf[2][2][4][KEY_TILE];
 
-// Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer; compact
-// when this buffer is full or when any owner's buffer nears full (all compact together).
-__device__ __forceinline__ void owner_take(OwnerState& S, int r, float s, int key0, int row, int k) {
+// An owner's reads for one step, completing together: the two half-totals of its row's
+// scores of the previous tile, this tile's key scale, and the published counts.
+__device__ __forceinline__ void owner_reads(const float* x0p, const float* x1p, const float* ksp, float& x0,
+                                            float& x1, float& ksc, v4i& cnts) {
+  asm volatile(
+      "ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(ksc), "=&v"(cnts)
+      : "v"(lds_addr(x0p)), "v"(lds_addr(x1p)), "v"(lds_addr(ksp)), "v"(lds_addr(s_cnt))
+      : "memory");
+}
+
+// Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer; cut when
+// this buffer is full or when any owner's buffer nears full (all cut together).
+__device__ __forceinline__ void owner_take(OwnerState& S, int r, float s, int key0, int row, int k, int most) {
   const int lane = lane_id();
   const int key = key0 + lane;
   const uint32_t u = score_key(s);
@@ -340,8 +354,6 @@ __device__ __forceinline__ void owner_take(OwnerState& S, int r, float s, int ke
     }
     S.cnt += __popcll((unsigned long long)m);
   }
-  const v4i c = lds_read16_sync(s_cnt);
-  const int most = max(max(c[0], c[1]), max(c[2], c[3]));
   if (S.cnt > CAND - KEY_TILE || (most > COMPACT_AT && S.cnt > k + 4 * KEY_TILE)) {
     __builtin_amdgcn_wave_barrier();
     uint32_t mx = S.mx;
@@ -377,83 +389,102 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
   uint8_t* const tks[4] = {tk0, tk1, tk2, tk3};
   float* const tss[4] = {ts0, ts1, ts2, ts3};
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int f = wv >> 1, hh = wv & 1;
-  const bool lead = wv < 4;  // waves 0-3 also own one row each
-  const TileDma dl = tile_dma_lane(wv, lane);
 
-  for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
-    const int row_hi = L - 4 * G;  // rows row_hi-4 .. row_hi-1
-    const int row0 = row_hi - 4;
-    IdxHalf Qh[4];
-    float cm[4];
+  if (wv < PF_SCORE_WAVES) {
+    // ---------------- scoring waves ----------------
+    const int f = wv >> 1, hh = wv & 1;
+    const TileDma dl = tile_dma_lane(wv, lane);
+    for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
+      const int row_hi = L - 4 * G;  // rows row_hi-4 .. row_hi-1
+      const int row0 = row_hi - 4;
+      IdxHalf Qh[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = max(row0 + j, row_lo);  // rows below row_lo are not this kernel's: score a valid row
-      cm[j] = row_cmax(qs + (size_t)r * IDX_HEADS, w + (size_t)r * IDX_HEADS);
-      load_idx_half(Qh[j], q8 + (size_t)r * IDX_HEADS * IDX_DIM, qs + (size_t)r * IDX_HEADS,
-                    w + (size_t)r * IDX_HEADS, hh, cm[j]);
-    }
-    const int my_row = row0 + (wv & 3);
-    const bool my_valid = lead && my_row >= row_lo;
-    OwnerState S{0, 0u, 0u, 0u, cm[wv & 3], 0.f};
-    if (lead && lane == 0) lds_store(&s_cnt[wv], __int_as_float(0));
-    const int ntiles = (row_hi + KEY_TILE - 1) / KEY_TILE;
-    v4f xr[4][2];  // this tile's MFMA results
+      for (int j = 0; j < 4; ++j) {
+        const int r = max(row0 + j, row_lo);  // rows below row_lo are not this kernel's: score a valid row
+        const float cmax = row_cmax(qs + (size_t)r * IDX_HEADS, w + (size_t)r * IDX_HEADS);
+        load_idx_half(Qh[j], q8 + (size_t)r * IDX_HEADS * IDX_DIM, qs + (size_t)r * IDX_HEADS,
+                      w + (size_t)r * IDX_HEADS, hh, cmax);
+      }
+      const int ntiles = (row_hi + KEY_TILE - 1) / KEY_TILE;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < ntiles) dma_key_tile(tks[j], tss[j], k8, ks, j * KEY_TILE, L, dl, wv, lane);
 
+      for (int base = 0; base <= ntiles; base += 4) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < ntiles) dma_key_tile(tks[j], tss[j], k8, ks, j * KEY_TILE, L, dl, wv, lane);
-
-    for (int base = 0; base <= ntiles; base += 4) {
+        for (int jj = 0; jj < 4; ++jj) {
+          const int i = base + jj;
+          if (i <= ntiles) {
+            if (i < ntiles) wait_tile(i, ntiles, wv);
+            else WAIT_VM_LGKM0(0);
+            __builtin_amdgcn_s_barrier();
+            if (i < ntiles) {
+              if (i + 3 < ntiles)
+                dma_key_tile(tks[(jj + 3) & 3], tss[(jj + 3) & 3], k8, ks, (i + 3) * KEY_TILE, L, dl, wv, lane);
+              const v8i b = ring_key_fragment(tks[jj], f, lane);
+              v4f x[4][2];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int i = base + jj;
-        if (i <= ntiles) {
-          if (i < ntiles) wait_tile(i, ntiles, wv);
-          else WAIT_VM_LGKM0(0);
-          __builtin_amdgcn_s_barrier();
-          if (i + 3 < ntiles) dma_key_tile(tks[(jj + 3) & 3], tss[(jj + 3) & 3], k8, ks, (i + 3) * KEY_TILE, L, dl, wv, lane);
-          float ksc_i = 0.f;
-          if (i < ntiles) {
-            if (lead) ksc_i = lds_read4_sync(tss[jj] + lane);
-            const v8i b = ring_key_fragment(tks[jj], f, lane);
+              for (int j = 0; j < 4; ++j) {
+                x[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
+                x[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+              float p[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              xr[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
-              xr[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
+              for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], x[j][0], x[j][1]);
+              lds_store(&xbuf[i & 1][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
             }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          // an owner takes tile i-1 while tile i's MFMAs run
-          if (i >= 1 && my_valid) {
-            const int t = i - 1, slot = t & 1;
-            float x0, x1;
-            lds_read4x2_sync(&xbuf[slot][0][wv][lane], &xbuf[slot][1][wv][lane], x0, x1);
-            owner_take(S, wv, finish_score(x0, x1, S.cmax, S.ksc), t * KEY_TILE, my_row, k);
-            if (lane == 0) lds_store(&s_cnt[wv], __int_as_float(S.cnt));
-          }
-          S.ksc = ksc_i;
-          __builtin_amdgcn_sched_barrier(0);
-          if (i < ntiles) {
-            float p[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], xr[j][0], xr[j][1]);
-            lds_store(&xbuf[i & 1][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
           }
         }
       }
+      WAIT_VM_LGKM0(0);
+      __builtin_amdgcn_s_barrier();  // end of group: ring and exchange buffers free
     }
-    if (my_valid) {
-      __builtin_amdgcn_wave_barrier();
-      if (S.cnt > k) {
-        select_compact(wv, S.cnt, k);
-        S.cnt = k;
+  } else {
+    // ---------------- owner waves ----------------
+    const int r = wv - PF_SCORE_WAVES;
+    for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
+      const int row_hi = L - 4 * G;
+      const int my_row = row_hi - 4 + r;
+      const bool valid = my_row >= row_lo;
+      const int rq = max(my_row, row_lo);
+      OwnerState S{0, 0u, 0u, 0u, row_cmax(qs + (size_t)rq * IDX_HEADS, w + (size_t)rq * IDX_HEADS), 0.f};
+      if (lane == 0) lds_store(&s_cnt[r], __int_as_float(0));
+      const int ntiles = (row_hi + KEY_TILE - 1) / KEY_TILE;
+      for (int base = 0; base <= ntiles; base += 4) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int i = base + jj;
+          if (i <= ntiles) {
+            WAIT_VM_LGKM0(0);
+            __builtin_amdgcn_s_barrier();
+            // tile i's key scales are read now (their ring slot is reloaded at step i+1)
+            float x0, x1, ksc;
+            v4i c;
+            const int slot = (i - 1) & 1;
+            owner_reads(&xbuf[slot][0][r][lane], &xbuf[slot][1][r][lane], tss[jj] + lane, x0, x1, ksc, c);
+            if (i >= 1 && valid) {
+              const int most = max(max(c[0], c[1]), max(c[2], c[3]));
+              owner_take(S, r, finish_score(x0, x1, S.cmax, S.ksc), (i - 1) * KEY_TILE, my_row, k, most);
+              if (lane == 0) lds_store(&s_cnt[r], __int_as_float(S.cnt));
+            }
+            S.ksc = ksc;
+          }
+        }
       }
-      int32_t* out = idx + (size_t)my_row * k;
-      for (int j = lane; j < k; j += WAVE) out[j] = j < S.cnt ? s_cidx[wv][j] : -1;
+      WAIT_VM_LGKM0(0);
+      __builtin_amdgcn_s_barrier();  // end of group
+      // the final selection overlaps the scoring waves' start of the next group
+      if (valid) {
+        __builtin_amdgcn_wave_barrier();
+        if (S.cnt > k) {
+          select_compact(r, S.cnt, k);
+          S.cnt = k;
+        }
+        int32_t* out = idx + (size_t)my_row * k;
+        for (int j = lane; j < k; j += WAVE) out[j] = j < S.cnt ? s_cidx[r][j] : -1;
+      }
     }
-    WAIT_VM_LGKM0(0);
-    __builtin_amdgcn_s_barrier();
   }
 }
 
