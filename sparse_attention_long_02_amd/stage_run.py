@@ -1,0 +1,54 @@
+"""Runs each prefill stage once, at a benchmark workload, for hardware-counter profiling.
+
+    python -m sparse_attention_long_02_amd.stage_run [--workload prefill_128k] [--copy-mib 4096]
+
+Order of the dispatches: one device-to-device copy of --copy-mib MiB (its FETCH_SIZE and
+WRITE_SIZE readings calibrate the counters against a known byte count), then
+dsa_select_prefill (fill kernel + fused indexer/top-k kernel), then dsa_sparse_mla on that
+selection.  Inputs are the seeded synthetic tensors the benchmark uses.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="prefill_128k")
+    ap.add_argument("--copy-mib", type=int, default=4096)
+    args = ap.parse_args()
+
+    import torch
+    import bench
+    from sparse_attention_long_02_amd import dsa
+    from sparse_attention_long_02_amd import synth as S
+
+    cfg = S.CONFIGS[args.workload]
+    dsa.lib()
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[stage_run] copy of {n} bytes done", flush=True)
+    del src, dst
+
+    qi, qs, ki, ks, w, q, kv = bench.prefill_inputs_on_gpu(cfg, torch)
+    idx = torch.empty((cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    dsa.select_prefill(qi, qs, ki, ks, w, cfg.k, idx=idx)
+    torch.cuda.synchronize()
+    print("[stage_run] select_prefill done", flush=True)
+    dsa.sparse_mla(q, kv, idx, cfg.sm_scale, cfg.d_v)
+    torch.cuda.synchronize()
+    print("[stage_run] sparse_mla done", flush=True)
+
+
+if __name__ == "__main__":
+    main()
