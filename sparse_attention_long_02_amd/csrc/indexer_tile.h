@@ -13,13 +13,13 @@
 //     rows), the keys are N (B = 16 keys x 128 bytes).  The MFMA's block scales multiply
 //     every product by 2^-25, exactly (powers of two), so each head dot x lies in
 //     (-0.77, 0.77) whatever the FP8 codes (|x| <= 448^2 * 128 * 2^-25);
-//   * ReLU and the head weights then cost 1.5 VALU ops per head: pairs of heads are packed
-//     to f16 (round toward zero), ReLU'd with one packed max, and dotted with the pair of
-//     normalised weights c' = c / max|c| (f16) into an fp32 sum (v_dot2_f32_f16);
-//   * per lane the sum covers 8 heads of one "head half" (two 16-head blocks); the four
-//     16-lane groups of a wave are combined as (g0 + g2) + (g1 + g3) by two permlane
-//     swaps; the two head halves are added; the result is scaled by max|c| * 2^25 and by
-//     k_scale.
+//   * ReLU: pairs of head dots are packed to f16 (round toward zero) and clamped at 0 with
+//     one packed max (one VALU op per head value);
+//   * the weighted head sum runs on the matrix core: per "head half" (32 heads) a
+//     16x16x32 f16 MFMA whose A operand holds the half's normalised weights
+//     c' = c / max|c| (f16) in every row and whose B operand is the ReLU'd values, so every
+//     lane receives the half's sum for its key (l % 16) in fp32;
+//   * the two head halves are added; the result is scaled by max|c| * 2^25 and by k_scale.
 // Relative error of a term: <= 2^-10 (f16 truncation) + 2^-11 (f16 weight); f16
 // subnormals below 2^-14 (head dots below 2^11 in code units) carry an absolute error of
 // at most 2 code units.
@@ -33,7 +33,6 @@ constexpr int IDX_HEADS = 64;
 constexpr int IDX_DIM = 128;
 constexpr int KEY_TILE = 64;  // keys per tile
 
-typedef __fp16 h2 __attribute__((ext_vector_type(2)));
 
 // E8M0 block scales: 2^-13 on the query side, 2^-12 on the key side
 constexpr uint32_t SCALE_Q = 0x72727272u, SCALE_K = 0x73737373u;
@@ -44,11 +43,14 @@ __device__ __forceinline__ v4f mfma_fp8_scaled(v8i a, v8i b) {
                                                           SCALE_K);
 }
 
-// One query row's operands for one head half (head blocks 2hh, 2hh+1): the A operands and
-// the f16 weight pairs this lane folds (heads 16hb + 4g + {0,1} and {2,3}).
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// One query row's operands for one head half (head blocks 2hh, 2hh+1): the FP8 A operands
+// and the A operand of the head-sum MFMA (contraction slot e of lane group g = head
+// 32hh + 16(e/4) + 4g + e%4, the head whose ReLU'd value that lane packs in slot e).
 struct IdxHalf {
   v8i a[2];
-  h2 c[4];
+  v8h wa;
 };
 
 // Per-row weight normaliser: cs = max_j |w_j q_scale_j| * 2^25 (0 if all weights vanish).
@@ -73,41 +75,30 @@ __device__ __forceinline__ void load_idx_half(IdxHalf& Q, const uint8_t* __restr
     const v4i* p = reinterpret_cast<const v4i*>(q8 + head * IDX_DIM + 32 * g);
     const v4i lo = p[0], hi = p[1];
     Q.a[k] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const int h0 = 16 * hb + 4 * g + 2 * pr;
-      const float c0 = __fmul_rn(__fmul_rn(w[h0], qs[h0]), inv);
-      const float c1 = __fmul_rn(__fmul_rn(w[h0 + 1], qs[h0 + 1]), inv);
-      Q.c[2 * k + pr] = h2{(__fp16)c0, (__fp16)c1};
-    }
+  for (int e = 0; e < 8; ++e) {
+    const int h = 32 * hh + 16 * (e >> 2) + 4 * g + (e & 3);
+    Q.wa[e] = (_Float16)__fmul_rn(__fmul_rn(w[h], qs[h]), inv);
   }
 }
 
-// Fold the two MFMA results of a head half: sum over this lane's 8 heads of c' ReLU(x).
-__device__ __forceinline__ float fold_half(const IdxHalf& Q, v4f x0, v4f x1) {
-  const h2 zero = h2{(__fp16)0.f, (__fp16)0.f};
-  float p = 0.f;
-  h2 r;
-  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x0[0], x0[1]), zero);
-  p = __builtin_amdgcn_fdot2(Q.c[0], r, p, false);
-  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x0[2], x0[3]), zero);
-  p = __builtin_amdgcn_fdot2(Q.c[1], r, p, false);
-  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x1[0], x1[1]), zero);
-  p = __builtin_amdgcn_fdot2(Q.c[2], r, p, false);
-  r = __builtin_elementwise_max(__builtin_amdgcn_cvt_pkrtz(x1[2], x1[3]), zero);
-  p = __builtin_amdgcn_fdot2(Q.c[3], r, p, false);
-  return p;
+// ReLU'd f16 B operand of the head-sum MFMA from the two FP8 MFMA results of a head half
+// (slot e = head block e/4, MFMA row 4g + e%4).
+__device__ __forceinline__ v8h relu_pack(v4f x0, v4f x1) {
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  const h2v zero = h2v{(_Float16)0.f, (_Float16)0.f};
+  const h2v r0 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0[0], x0[1])), zero);
+  const h2v r1 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0[2], x0[3])), zero);
+  const h2v r2 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x1[0], x1[1])), zero);
+  const h2v r3 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x1[2], x1[3])), zero);
+  return v8h{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
-// Combine four per-lane partial vectors across the four 16-lane groups: lane l returns
-// the total of vector l/16 at column l%16, summed as (g0 + g2) + (g1 + g3).
-__device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
-  auto r02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
-  auto r13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
-  const float qa = __fadd_rn(__uint_as_float(r02[0]), __uint_as_float(r02[1]));
-  const float qb = __fadd_rn(__uint_as_float(r13[0]), __uint_as_float(r13[1]));
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(qa), __float_as_uint(qb), false, false);
-  return __fadd_rn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// The head half's weighted ReLU sum for key l % 16 of the fragment, in every lane (element 0).
+__device__ __forceinline__ float head_half_sum(const IdxHalf& Q, v4f x0, v4f x1) {
+  const v4f d = __builtin_amdgcn_mfma_f32_16x16x32_f16(Q.wa, relu_pack(x0, x1), v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  return d[0];
 }
 
 // Final score from the two head-half totals.
@@ -155,7 +146,8 @@ __device__ __forceinline__ v8i global_key_fragment(const uint8_t* __restrict__ k
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Score of key (key0 + lane) of a 64-key tile given the four fragments' B operands.
+// Score of key (key0 + lane) of a 64-key tile given the four fragments' B operands: lane l
+// takes fragment l/16's sums (every lane of a fragment's head-sum MFMA holds key l % 16).
 __device__ __forceinline__ float score_tile64(const IdxRow& R, const v8i* b, float kscale) {
   v4f x[4][2][2];
 #pragma unroll
@@ -165,14 +157,14 @@ __device__ __forceinline__ float score_tile64(const IdxRow& R, const v8i* b, flo
       x[f][hh][0] = mfma_fp8_scaled(R.h[hh].a[0], b[f]);
       x[f][hh][1] = mfma_fp8_scaled(R.h[hh].a[1], b[f]);
     }
-  __builtin_amdgcn_sched_barrier(0);  // all 16 MFMAs issue back to back, then the folds
-  float p[2][4];
+  float t[4][2];
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) p[hh][f] = fold_half(R.h[hh], x[f][hh][0], x[f][hh][1]);
-  const float t0 = reduce_scatter4(p[0][0], p[0][1], p[0][2], p[0][3]);
-  const float t1 = reduce_scatter4(p[1][0], p[1][1], p[1][2], p[1][3]);
+    for (int hh = 0; hh < 2; ++hh) t[f][hh] = head_half_sum(R.h[hh], x[f][hh][0], x[f][hh][1]);
+  const int fl = lane_id() >> 4;
+  const float t0 = fl == 0 ? t[0][0] : fl == 1 ? t[1][0] : fl == 2 ? t[2][0] : t[3][0];
+  const float t1 = fl == 0 ? t[0][1] : fl == 1 ? t[1][1] : fl == 2 ? t[2][1] : t[3][1];
   return finish_score(t0, t1, R.cmax, kscale);
 }
 

@@ -423,16 +423,18 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
                 dma_key_tile(tks[(jj + 3) & 3], tss[(jj + 3) & 3], k8, ks, (i + 3) * KEY_TILE, L, dl, wv, lane);
               const v8i b = ring_key_fragment(tks[jj], f, lane);
               v4f x[4][2];
+              float t[4];
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 x[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
                 x[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
               }
-              __builtin_amdgcn_sched_barrier(0);
-              float p[4];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) p[j] = fold_half(Qh[j], x[j][0], x[j][1]);
-              lds_store(&xbuf[i & 1][hh][lane >> 4][16 * f + (lane & 15)], reduce_scatter4(p[0], p[1], p[2], p[3]));
+              for (int j = 0; j < 4; ++j) t[j] = head_half_sum(Qh[j], x[j][0], x[j][1]);
+              // lane l holds every row's sum for key 16f + l%16; it stores row l/16's
+              const int jr = lane >> 4;
+              const float v = jr == 0 ? t[0] : jr == 1 ? t[1] : jr == 2 ? t[2] : t[3];
+              lds_store(&xbuf[i & 1][hh][jr][16 * f + (lane & 15)], v);
             }
           }
         }
