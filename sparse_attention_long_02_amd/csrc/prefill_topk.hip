@@ -24,7 +24,7 @@
 
 namespace dsa {
 
-constexpr int CAND = 3584;  // candidate slots per row
+constexpr int CAND = 3072;  // candidate slots per row
 
 // Per-row selection state of the fused kernel, at file scope so the compiler can tell it
 // apart from the key tiles that direct loads are still writing (accesses to these arrays
@@ -242,21 +242,23 @@ __device__ uint32_t cut_candidates(int r, int n, int k, uint32_t lo, uint32_t mx
 // ---------------------------------------------------------------------------------------
 // Persistent fused kernel.  A block owns groups of 4 consecutive rows; blocks take groups
 // longest-first in lockstep (group G = block + round * blocks), so the blocks on one XCD
-// sweep the same key tiles at about the same time and the tiles stay in L2.
-//   * scoring waves 0-7: wave w scores key fragment f = w/2 (16 keys of each 64-key tile)
-//     for head half hh = w%2 of all 4 rows: 8 MFMAs, then the fold, then its half-totals
-//     go to LDS.  The two scoring waves of a SIMD keep its matrix core busy.
-//   * owner waves 8-11: wave 8+j owns row j's selection.  At step i it takes tile i-1
-//     (whose half-totals were completed before the step's barrier), in the VALU and LDS
-//     issue slots the scoring waves leave free.
-// Key tiles arrive by direct global->LDS loads in a ring of 4 buffers (three in flight).
-// When any owner's buffer nears full, all four owners cut at the same step (one stall of
-// the block instead of four).
+// sweep the same key tiles at about the same time and the tiles stay in L2.  Keys are
+// processed in steps of two 64-key tiles (one barrier per step):
+//   * scoring waves 0-7: wave w scores key fragment f = w/2 (16 keys of each tile) for
+//     head half hh = w%2 of all 4 rows: per tile 8 FP8 MFMAs and 4 head-sum MFMAs; the
+//     half-totals go to LDS;
+//   * owner waves 8-11: wave 8+j owns row j's selection.  At step s it takes step s-1's
+//     128 scores (completed before the step's barrier), in the VALU and LDS issue slots
+//     the scoring waves leave free.
+// Key tiles arrive by direct global->LDS loads in a ring of three tile pairs (two steps in
+// flight).  When any owner's buffer nears full, all four owners cut at the same step (one
+// stall of the block instead of four).
 // ---------------------------------------------------------------------------------------
 constexpr int PF_SCORE_WAVES = 8;
 constexpr int PF_WAVES = PF_SCORE_WAVES + 4;
 constexpr int TILE_BYTES = KEY_TILE * IDX_DIM;
-constexpr int COMPACT_AT = CAND - 3 * KEY_TILE;  // collective compaction trigger
+constexpr int STEP_KEYS = 2 * KEY_TILE;
+constexpr int COMPACT_AT = CAND - 3 * STEP_KEYS;  // collective compaction trigger
 
 #define WAIT_VM_LGKM0(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0x0 << 8))
@@ -281,18 +283,15 @@ __device__ __forceinline__ void dma_key_tile(uint8_t* tk, float* ts, const uint8
   if (wv == 0) __builtin_amdgcn_global_load_lds(ks + (uint32_t)min(key0 + lane, L - 1), ts, 4, 0, 0);
 }
 
-// wait until tile i has landed: tiles i+1, i+2 (if they exist) may still be in flight;
-// wave 0 issues two loads per tile, the other scoring waves one.  Also drains this wave's
-// LDS ops.
-__device__ __forceinline__ void wait_tile(int i, int ntiles, int wv) {
-  const int after = min(2, ntiles - 1 - i);
+// wait until step s's two tiles have landed (step s+1's may still be in flight); wave 0
+// issues four loads per step, the other scoring waves two.  Also drains this wave's LDS ops.
+__device__ __forceinline__ void wait_step(int st, int nsteps, int wv) {
+  const bool more = st + 1 < nsteps;
   if (wv == 0) {
-    if (after >= 2) WAIT_VM_LGKM0(4);
-    else if (after == 1) WAIT_VM_LGKM0(2);
+    if (more) WAIT_VM_LGKM0(4);
     else WAIT_VM_LGKM0(0);
   } else {
-    if (after >= 2) WAIT_VM_LGKM0(2);
-    else if (after == 1) WAIT_VM_LGKM0(1);
+    if (more) WAIT_VM_LGKM0(2);
     else WAIT_VM_LGKM0(0);
   }
 }
@@ -317,29 +316,31 @@ struct OwnerState {
   uint32_t lo;   // every buffered key is >= lo
   uint32_t mx;   // this lane's largest key appended so far
   float cmax;
-  float ksc;  // key scale (this lane's key) of the tile not yet taken
 };
 
 __shared__ __align__(16) int s_cnt[4];  // owners' published candidate counts
-// Half-totals of tile scores exchanged between the scoring waves and the owners
-// ([tile % 2][head half][row][key]).
-__shared__ float xbuf[2][2][4][KEY_TILE];
+// Half-totals of a step's scores exchanged between the scoring waves and the owners
+// ([step % 2][head half][row][key of the step]).
+__shared__ float xbuf[2][2][4][STEP_KEYS];
 
-// An owner's reads for one step, completing together: the two half-totals of its row's
-// scores of the previous tile, this tile's key scale, and the published counts.
-__device__ __forceinline__ void owner_reads(const float* x0p, const float* x1p, const float* ksp, float& x0,
-                                            float& x1, float& ksc, v4i& cnts) {
+// An owner's reads for one step, completing together: the half-totals of its row's scores
+// of the previous step (keys lane and 64 + lane, both head halves), this step's two key
+// scales, and the published counts.
+__device__ __forceinline__ void owner_reads(int slot, int r, const float* ks0, const float* ks1, float x[4],
+                                            float ksn[2], v4i& cnts) {
+  const int l = lane_id();
   asm volatile(
-      "ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(ksc), "=&v"(cnts)
-      : "v"(lds_addr(x0p)), "v"(lds_addr(x1p)), "v"(lds_addr(ksp)), "v"(lds_addr(s_cnt))
+      "ds_read_b32 %0, %7\n\tds_read_b32 %1, %8\n\tds_read_b32 %2, %9\n\tds_read_b32 %3, %10\n\t"
+      "ds_read_b32 %4, %11\n\tds_read_b32 %5, %12\n\tds_read_b128 %6, %13\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(ksn[0]), "=&v"(ksn[1]), "=&v"(cnts)
+      : "v"(lds_addr(&xbuf[slot][0][r][l])), "v"(lds_addr(&xbuf[slot][1][r][l])),
+        "v"(lds_addr(&xbuf[slot][0][r][64 + l])), "v"(lds_addr(&xbuf[slot][1][r][64 + l])),
+        "v"(lds_addr(ks0 + l)), "v"(lds_addr(ks1 + l)), "v"(lds_addr(s_cnt))
       : "memory");
 }
 
-// Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer; cut when
-// this buffer is full or when any owner's buffer nears full (all cut together).
-__device__ __forceinline__ void owner_take(OwnerState& S, int r, float s, int key0, int row, int k, int most) {
+// Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer.
+__device__ __forceinline__ void owner_append(OwnerState& S, int r, float s, int key0, int row) {
   const int lane = lane_id();
   const int key = key0 + lane;
   const uint32_t u = score_key(s);
@@ -354,13 +355,18 @@ __device__ __forceinline__ void owner_take(OwnerState& S, int r, float s, int ke
     }
     S.cnt += __popcll((unsigned long long)m);
   }
-  if (S.cnt > CAND - KEY_TILE || (most > COMPACT_AT && S.cnt > k + 4 * KEY_TILE)) {
+}
+
+// Cut when the buffer has no room for another step or when any owner's buffer nears full
+// (all cut together).
+__device__ __forceinline__ void owner_maybe_cut(OwnerState& S, int r, int k, int most) {
+  if (S.cnt > CAND - STEP_KEYS || (most > COMPACT_AT && S.cnt > k + 2 * STEP_KEYS)) {
     __builtin_amdgcn_wave_barrier();
     uint32_t mx = S.mx;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, WAVE));
     int kept;
-    const uint32_t e = cut_candidates(r, S.cnt, k, S.lo, mx, CAND - 4 * KEY_TILE, kept);
+    const uint32_t e = cut_candidates(r, S.cnt, k, S.lo, mx, CAND - 2 * STEP_KEYS, kept);
     if (e != 0u) {
       S.thr = e - 1u;
       S.lo = e;
@@ -377,17 +383,22 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, int L, int row_lo, int k,
     int n_groups, int32_t* __restrict__ idx) {
+  // ring of three tile pairs (pair p = tiles 2p, 2p+1) and their key scales
   __shared__ __align__(16) uint8_t tk0[TILE_BYTES];
   __shared__ __align__(16) uint8_t tk1[TILE_BYTES];
   __shared__ __align__(16) uint8_t tk2[TILE_BYTES];
   __shared__ __align__(16) uint8_t tk3[TILE_BYTES];
+  __shared__ __align__(16) uint8_t tk4[TILE_BYTES];
+  __shared__ __align__(16) uint8_t tk5[TILE_BYTES];
   __shared__ __align__(16) float ts0[KEY_TILE];
   __shared__ __align__(16) float ts1[KEY_TILE];
   __shared__ __align__(16) float ts2[KEY_TILE];
   __shared__ __align__(16) float ts3[KEY_TILE];
+  __shared__ __align__(16) float ts4[KEY_TILE];
+  __shared__ __align__(16) float ts5[KEY_TILE];
 
-  uint8_t* const tks[4] = {tk0, tk1, tk2, tk3};
-  float* const tss[4] = {ts0, ts1, ts2, ts3};
+  uint8_t* const tks[6] = {tk0, tk1, tk2, tk3, tk4, tk5};
+  float* const tss[6] = {ts0, ts1, ts2, ts3, ts4, ts5};
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
 
   if (wv < PF_SCORE_WAVES) {
@@ -405,36 +416,44 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
         load_idx_half(Qh[j], q8 + (size_t)r * IDX_HEADS * IDX_DIM, qs + (size_t)r * IDX_HEADS,
                       w + (size_t)r * IDX_HEADS, hh, cmax);
       }
-      const int ntiles = (row_hi + KEY_TILE - 1) / KEY_TILE;
+      const int nsteps = (row_hi + STEP_KEYS - 1) / STEP_KEYS;
+      // (a step's second tile may lie past L: its loads clamp to row L-1, and the owners
+      // never take a key past their row)
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < ntiles) dma_key_tile(tks[j], tss[j], k8, ks, j * KEY_TILE, L, dl, wv, lane);
+      for (int j = 0; j < 4; ++j)
+        if (j < 2 * nsteps) dma_key_tile(tks[j], tss[j], k8, ks, j * KEY_TILE, L, dl, wv, lane);
 
-      for (int base = 0; base <= ntiles; base += 4) {
+      for (int base = 0; base <= nsteps; base += 3) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int i = base + jj;
-          if (i <= ntiles) {
-            if (i < ntiles) wait_tile(i, ntiles, wv);
+        for (int pp = 0; pp < 3; ++pp) {
+          const int st = base + pp;
+          if (st <= nsteps) {
+            if (st < nsteps) wait_step(st, nsteps, wv);
             else WAIT_VM_LGKM0(0);
             __builtin_amdgcn_s_barrier();
-            if (i < ntiles) {
-              if (i + 3 < ntiles)
-                dma_key_tile(tks[(jj + 3) & 3], tss[(jj + 3) & 3], k8, ks, (i + 3) * KEY_TILE, L, dl, wv, lane);
-              const v8i b = ring_key_fragment(tks[jj], f, lane);
-              v4f x[4][2];
-              float t[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                x[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
-                x[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
+            if (st < nsteps) {
+              if (st + 2 < nsteps) {  // into the pair of step st-1, which every wave is done with
+                const int q = (pp + 2) % 3;
+                dma_key_tile(tks[2 * q], tss[2 * q], k8, ks, (2 * st + 4) * KEY_TILE, L, dl, wv, lane);
+                dma_key_tile(tks[2 * q + 1], tss[2 * q + 1], k8, ks, (2 * st + 5) * KEY_TILE, L, dl, wv, lane);
               }
 #pragma unroll
-              for (int j = 0; j < 4; ++j) t[j] = head_half_sum(Qh[j], x[j][0], x[j][1]);
-              // lane l holds every row's sum for key 16f + l%16; it stores row l/16's
-              const int jr = lane >> 4;
-              const float v = jr == 0 ? t[0] : jr == 1 ? t[1] : jr == 2 ? t[2] : t[3];
-              lds_store(&xbuf[i & 1][hh][jr][16 * f + (lane & 15)], v);
+              for (int h = 0; h < 2; ++h) {
+                const v8i b = ring_key_fragment(tks[2 * pp + h], f, lane);
+                v4f x[4][2];
+                float t[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  x[j][0] = mfma_fp8_scaled(Qh[j].a[0], b);
+                  x[j][1] = mfma_fp8_scaled(Qh[j].a[1], b);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t[j] = head_half_sum(Qh[j], x[j][0], x[j][1]);
+                // lane l holds every row's sum for key 16f + l%16; it stores row l/16's
+                const int jr = lane >> 4;
+                const float v = jr == 0 ? t[0] : jr == 1 ? t[1] : jr == 2 ? t[2] : t[3];
+                lds_store(&xbuf[st & 1][hh][jr][64 * h + 16 * f + (lane & 15)], v);
+              }
             }
           }
         }
@@ -450,27 +469,30 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
       const int my_row = row_hi - 4 + r;
       const bool valid = my_row >= row_lo;
       const int rq = max(my_row, row_lo);
-      OwnerState S{0, 0u, 0u, 0u, row_cmax(qs + (size_t)rq * IDX_HEADS, w + (size_t)rq * IDX_HEADS), 0.f};
+      OwnerState S{0, 0u, 0u, 0u, row_cmax(qs + (size_t)rq * IDX_HEADS, w + (size_t)rq * IDX_HEADS)};
       if (lane == 0) lds_store(&s_cnt[r], __int_as_float(0));
-      const int ntiles = (row_hi + KEY_TILE - 1) / KEY_TILE;
-      for (int base = 0; base <= ntiles; base += 4) {
+      const int nsteps = (row_hi + STEP_KEYS - 1) / STEP_KEYS;
+      float ksc[2] = {0.f, 0.f};  // key scales of the step not yet taken
+      for (int base = 0; base <= nsteps; base += 3) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int i = base + jj;
-          if (i <= ntiles) {
+        for (int pp = 0; pp < 3; ++pp) {
+          const int st = base + pp;
+          if (st <= nsteps) {
             WAIT_VM_LGKM0(0);
             __builtin_amdgcn_s_barrier();
-            // tile i's key scales are read now (their ring slot is reloaded at step i+1)
-            float x0, x1, ksc;
+            // take step st-1; read step st's key scales (their pair is reloaded at step st+1)
+            float x[4], ksn[2];
             v4i c;
-            const int slot = (i - 1) & 1;
-            owner_reads(&xbuf[slot][0][r][lane], &xbuf[slot][1][r][lane], tss[jj] + lane, x0, x1, ksc, c);
-            if (i >= 1 && valid) {
-              const int most = max(max(c[0], c[1]), max(c[2], c[3]));
-              owner_take(S, r, finish_score(x0, x1, S.cmax, S.ksc), (i - 1) * KEY_TILE, my_row, k, most);
+            owner_reads((st - 1) & 1, r, tss[2 * pp], tss[2 * pp + 1], x, ksn, c);
+            if (st >= 1 && valid) {
+              const int key0 = (st - 1) * STEP_KEYS;
+              owner_append(S, r, finish_score(x[0], x[1], S.cmax, ksc[0]), key0, my_row);
+              owner_append(S, r, finish_score(x[2], x[3], S.cmax, ksc[1]), key0 + KEY_TILE, my_row);
+              owner_maybe_cut(S, r, k, max(max(c[0], c[1]), max(c[2], c[3])));
               if (lane == 0) lds_store(&s_cnt[r], __int_as_float(S.cnt));
             }
-            S.ksc = ksc;
+            ksc[0] = ksn[0];
+            ksc[1] = ksn[1];
           }
         }
       }
