@@ -493,9 +493,9 @@ __global__ __launch_bounds__(64) void sparse_mla_f32_kernel(
 int sparse_mla_splits(int64_t B, int64_t n_q, int32_t k, int32_t dtype) {
   if (dtype != DSA_BF16) return 1;
   const int64_t blocks = B * n_q;
-  if (blocks >= 1024) return 1;
+  if (blocks >= 256) return 1;
   const int64_t chunks = (k + KC - 1) / KC;
-  int64_t s = (1024 + blocks - 1) / blocks;
+  int64_t s = (256 + blocks - 1) / blocks;
   if (s > chunks / 4) s = chunks / 4;  // at least 4 chunks per split
   if (s > 16) s = 16;
   return s < 1 ? 1 : (int)s;

@@ -17,19 +17,20 @@
 namespace dsa {
 
 constexpr int TK_THREADS = 512;
-constexpr int TK_WAVES = TK_THREADS / WAVE;
 constexpr int TK_WORDS = (int)(TOPK_MAX_N / 32);
 constexpr int TK_BINS = 4096;
 
-// exclusive scan over the block; returns the prefix and writes the block total
+// exclusive scan over a block of NT threads; returns the prefix and writes the block total
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
+  constexpr int NW = NT / WAVE;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == WAVE - 1) wtot[wv] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < TK_WAVES; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const uint32_t t = wtot[i];
     before += i < wv ? t : 0u;
     tot += t;
@@ -39,96 +40,106 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, 
   return before + incl - v;
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(
-    const float* __restrict__ scores, int64_t ld, int64_t n_rows, int64_t n_k,
-    const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int k,
-    int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[TK_BINS];
-  __shared__ uint32_t sel[TK_WORDS];
-  __shared__ uint32_t tie[TK_WORDS];
-  __shared__ uint32_t wtot[TK_WAVES];
-  __shared__ uint32_t s_digit, s_above;
-
+// Block-wide choice of the digit holding the rem-th largest key from a histogram of nb
+// bins (thread t owns bins nb-1-t*per .. downward).  Returns the digit; `above` = keys in
+// higher bins.
+template <int NT>
+__device__ __forceinline__ uint32_t pick_digit(const uint32_t* hist, int nb, uint32_t rem, uint32_t* wtot,
+                                               uint32_t* s_digit, uint32_t* s_above, uint32_t& above) {
   const int tid = threadIdx.x;
-  const int64_t i = blockIdx.x;
-  const int b = blockIdx.y;
-  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + row_begin + i;
-  int64_t n = pos + 1 < n_k ? pos + 1 : n_k;
-  n = n > 0 ? n : 0;
-  const float* srow = scores + ((int64_t)b * n_rows + i) * ld;
-  int32_t* out = idx + ((int64_t)b * n_rows + i) * k;
-
-  if (n <= k) {  // every visible key is kept
-    for (int j = tid; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
-    return;
+  const int per = nb / NT > 0 ? nb / NT : 1;
+  uint32_t local = 0;
+  const int top = nb - 1 - tid * per;
+  if (tid * per < nb)
+    for (int j = 0; j < per; ++j) local += hist[top - j];
+  uint32_t total;
+  uint32_t c = block_excl_scan<NT>(local, wtot, total);
+  if (tid * per < nb && c < rem && c + local >= rem) {
+    for (int j = 0; j < per; ++j) {
+      const uint32_t h = hist[top - j];
+      if (c + h >= rem) {
+        *s_digit = (uint32_t)(top - j);
+        *s_above = c;
+        break;
+      }
+      c += h;
+    }
   }
+  __syncthreads();
+  above = *s_above;
+  const uint32_t d = *s_digit;
+  __syncthreads();
+  return d;
+}
 
-  // ---- 1. radix select: digits [31:20], [19:8], [7:0]
+// Exact radix select over the visible part of a score row: the k-th largest key v* and
+// how many keys equal to v* are kept (digits of 12, 12 and 8 bits, LDS histograms).
+template <int NT>
+__device__ void select_row(const float* __restrict__ srow, int64_t n, int k, uint32_t* hist, uint32_t* wtot,
+                           uint32_t* s_digit, uint32_t* s_above, uint32_t& vstar, uint32_t& rem) {
+  const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
-  uint32_t rem = (uint32_t)k;
+  rem = (uint32_t)k;
   const int shifts[3] = {20, 8, 0};
   const int widths[3] = {12, 12, 8};
   for (int r = 0; r < 3; ++r) {
     const int shift = shifts[r];
     const uint32_t dmask = (1u << widths[r]) - 1u;
     const int nb = 1 << widths[r];
-    for (int j = tid; j < nb; j += TK_THREADS) hist[j] = 0;
+    for (int j = tid; j < nb; j += NT) hist[j] = 0;
     __syncthreads();
-    for (int64_t s = tid; s < n; s += TK_THREADS) {
+    for (int64_t s = tid; s < n; s += NT) {
       const uint32_t u = score_key(srow[s]);
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
     }
     __syncthreads();
-    // thread t owns the bins nb-1-t*per .. (descending); cumulative count from the top
-    const int per = nb / TK_THREADS > 0 ? nb / TK_THREADS : 1;
-    uint32_t local = 0;
-    const int top = nb - 1 - tid * per;
-    if (tid * per < nb)
-      for (int j = 0; j < per; ++j) local += hist[top - j];
-    uint32_t total;
-    uint32_t c = block_excl_scan(local, wtot, total);
-    if (tid * per < nb && c < rem && c + local >= rem) {
-      for (int j = 0; j < per; ++j) {
-        const uint32_t h = hist[top - j];
-        if (c + h >= rem) {
-          s_digit = (uint32_t)(top - j);
-          s_above = c;
-          break;
-        }
-        c += h;
-      }
-    }
-    __syncthreads();
-    const uint32_t d = s_digit;
-    rem -= s_above;
+    uint32_t above;
+    const uint32_t d = pick_digit<NT>(hist, nb, rem, wtot, s_digit, s_above, above);
+    rem -= above;
     prefix |= d << shift;
     pmask |= dmask << shift;
+  }
+  vstar = prefix;
+}
+
+// Exact radix select of the rank-th largest of n keys held in LDS (8-bit digits).
+template <int NT>
+__device__ uint32_t select_lds(const uint32_t* keys, int n, uint32_t rank, uint32_t* hist, uint32_t* wtot,
+                               uint32_t* s_digit, uint32_t* s_above, uint32_t& rem) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  rem = rank;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int j = tid; j < 256; j += NT) hist[j] = 0;
     __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t u = keys[i];
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    uint32_t above;
+    const uint32_t d = pick_digit<NT>(hist, 256, rem, wtot, s_digit, s_above, above);
+    rem -= above;
+    prefix |= d << shift;
+    pmask |= 255u << shift;
   }
-  const uint32_t vstar = prefix;  // k-th largest key; `rem` keys equal to it are kept
+  return prefix;
+}
 
-  // ---- 2. mark kept keys and ties
+// Keep the first `rem` ties (lowest positions), then write the kept positions in ascending
+// order, -1 padded.  sel / tie: bitmaps over the row's n positions.
+template <int NT>
+__device__ void write_kept(uint32_t* sel, const uint32_t* tie, int64_t n, uint32_t rem, int k, int32_t* out,
+                           uint32_t* wtot) {
+  const int tid = threadIdx.x;
   const int64_t nw = (n + 31) / 32;
-  for (int64_t j = tid; j < nw; j += TK_THREADS) {
-    sel[j] = 0;
-    tie[j] = 0;
-  }
-  __syncthreads();
-  for (int64_t s = tid; s < n; s += TK_THREADS) {
-    const uint32_t u = score_key(srow[s]);
-    if (u > vstar) atomicOr(&sel[s >> 5], 1u << (s & 31));
-    else if (u == vstar) atomicOr(&tie[s >> 5], 1u << (s & 31));
-  }
-  __syncthreads();
-
-  // ---- 3. keep the first `rem` ties, then write the kept indices in ascending order
-  const int64_t wpt = (nw + TK_THREADS - 1) / TK_THREADS;
+  const int64_t wpt = (nw + NT - 1) / NT;
   const int64_t w0 = tid * wpt;
   const int64_t w1 = w0 + wpt < nw ? w0 + wpt : nw;
   uint32_t tcount = 0;
   for (int64_t j = w0; j < w1; ++j) tcount += __popc(tie[j]);
   uint32_t tot;
-  uint32_t tbefore = block_excl_scan(tcount, wtot, tot);
+  uint32_t tbefore = block_excl_scan<NT>(tcount, wtot, tot);
   for (int64_t j = w0; j < w1; ++j) {
     uint32_t m = tie[j];
     while (m) {
@@ -140,7 +151,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(
   }
   uint32_t scount = 0;
   for (int64_t j = w0; j < w1; ++j) scount += __popc(sel[j]);
-  uint32_t o = block_excl_scan(scount, wtot, tot);
+  uint32_t o = block_excl_scan<NT>(scount, wtot, tot);
   for (int64_t j = w0; j < w1; ++j) {
     uint32_t m = sel[j];
     while (m) {
@@ -150,13 +161,159 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(
       m &= m - 1;
     }
   }
-  for (int64_t j = (int64_t)tot + tid; j < k; j += TK_THREADS) out[j] = -1;
+  for (int64_t j = (int64_t)tot + tid; j < k; j += NT) out[j] = -1;
+}
+
+// mark every visible key > v* in sel and every key == v* in tie (bitmaps zeroed first)
+template <int NT>
+__device__ void mark_row(const float* __restrict__ srow, int64_t n, uint32_t vstar, uint32_t* sel, uint32_t* tie) {
+  const int tid = threadIdx.x;
+  const int64_t nw = (n + 31) / 32;
+  for (int64_t j = tid; j < nw; j += NT) {
+    sel[j] = 0;
+    tie[j] = 0;
+  }
+  __syncthreads();
+  for (int64_t s = tid; s < n; s += NT) {
+    const uint32_t u = score_key(srow[s]);
+    if (u > vstar) atomicOr(&sel[s >> 5], 1u << (s & 31));
+    else if (u == vstar) atomicOr(&tie[s >> 5], 1u << (s & 31));
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void row_geometry(int64_t n_rows, int64_t n_k, const int32_t* q_pos, int64_t pos_offset,
+                                             int64_t row_begin, int k, int64_t ld, const float* scores,
+                                             int32_t* idx, int64_t& n, const float*& srow, int32_t*& out) {
+  const int64_t i = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + row_begin + i;
+  n = pos + 1 < n_k ? pos + 1 : n_k;
+  n = n > 0 ? n : 0;
+  srow = scores + ((int64_t)b * n_rows + i) * ld;
+  out = idx + ((int64_t)b * n_rows + i) * k;
+}
+
+// One 512-thread block per row (rows of any length):
+//   1. exact radix select of v* over the whole row;  2. mark kept keys and ties in LDS
+//   bitmaps;  3. ascending write.
+__global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t n_rows, int64_t n_k,
+    const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int k,
+    int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t sel[TK_WORDS];
+  __shared__ uint32_t tie[TK_WORDS];
+  __shared__ uint32_t wtot[TK_THREADS / WAVE];
+  __shared__ uint32_t s_digit, s_above;
+  int64_t n;
+  const float* srow;
+  int32_t* out;
+  row_geometry(n_rows, n_k, q_pos, pos_offset, row_begin, k, ld, scores, idx, n, srow, out);
+  const int tid = threadIdx.x;
+  if (n <= k) {  // every visible key is kept
+    for (int j = tid; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
+    return;
+  }
+  uint32_t vstar, rem;
+  select_row<TK_THREADS>(srow, n, k, hist, wtot, &s_digit, &s_above, vstar, rem);
+  mark_row<TK_THREADS>(srow, n, vstar, sel, tie);
+  write_kept<TK_THREADS>(sel, tie, n, rem, k, out, wtot);
+}
+
+// Long rows with a small k: one 1024-thread block per row.
+//   1. a threshold T from 4096 evenly spaced samples of the row (the sample key of rank
+//      about twice the k-th key's expected rank), so that roughly 2k keys exceed it;
+//   2. one pass appends the keys > T (key, position) to an LDS candidate buffer;
+//   3. if at least k and at most TL_CAP keys exceed T, the k-th largest key is > T, so
+//      v* and every key equal to it are among the candidates: the exact select runs on
+//      them alone.  Otherwise (an unlucky sample, heavy ties) the exact full-row select
+//      runs instead.  Either way the result is the exact top-k.
+constexpr int TL_THREADS = 1024;
+constexpr int TL_SAMPLES = 4096;
+constexpr int TL_CAP = 8192;
+constexpr int TL_MIN_N = 16384;  // rows at least this long (and k <= TL_CAP / 4) use it
+
+__global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t n_rows, int64_t n_k,
+    const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int k,
+    int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t sel[TK_WORDS];
+  __shared__ uint32_t tie[TK_WORDS];
+  __shared__ uint32_t ckey[TL_CAP];  // samples first, then candidate keys
+  __shared__ int32_t cpos[TL_CAP];
+  __shared__ uint32_t wtot[TL_THREADS / WAVE];
+  __shared__ uint32_t s_digit, s_above, s_cnt;
+  int64_t n;
+  const float* srow;
+  int32_t* out;
+  row_geometry(n_rows, n_k, q_pos, pos_offset, row_begin, k, ld, scores, idx, n, srow, out);
+  const int tid = threadIdx.x;
+  if (n <= k) {
+    for (int j = tid; j < k; j += TL_THREADS) out[j] = j < n ? j : -1;
+    return;
+  }
+  // 1. threshold from the samples
+  for (int j = tid; j < TL_SAMPLES; j += TL_THREADS) ckey[j] = score_key(srow[((int64_t)j * n) / TL_SAMPLES]);
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  const int64_t expect = ((int64_t)k * TL_SAMPLES + n - 1) / n;  // sample rank of the k-th key
+  const uint32_t srank = (uint32_t)min<int64_t>(TL_SAMPLES, 2 * expect + 16);
+  uint32_t srem;
+  const uint32_t T = select_lds<TL_THREADS>(ckey, TL_SAMPLES, srank, hist, wtot, &s_digit, &s_above, srem);
+  // 2. candidates: keys > T
+  for (int64_t s0 = 0; s0 < n; s0 += TL_THREADS) {
+    const int64_t s = s0 + tid;
+    const uint32_t u = s < n ? score_key(srow[s]) : 0u;
+    const bool pass = s < n && u > T;
+    const uint64_t m = ballot(pass);
+    uint32_t base = 0;
+    if ((tid & 63) == 0 && m) base = atomicAdd(&s_cnt, (uint32_t)__popcll((unsigned long long)m));
+    base = __shfl(base, 0, WAVE);
+    if (pass) {
+      const uint32_t slot = base + lanes_below(m);
+      if (slot < (uint32_t)TL_CAP) {
+        ckey[slot] = u;
+        cpos[slot] = (int32_t)s;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nc = s_cnt;
+  uint32_t vstar, rem;
+  if (nc < (uint32_t)k || nc > (uint32_t)TL_CAP) {
+    // 3b. the threshold did not bracket the k-th key: exact select over the whole row
+    select_row<TL_THREADS>(srow, n, k, hist, wtot, &s_digit, &s_above, vstar, rem);
+    mark_row<TL_THREADS>(srow, n, vstar, sel, tie);
+  } else {
+    // 3a. exact select among the candidates, then mark them
+    vstar = select_lds<TL_THREADS>(ckey, (int)nc, (uint32_t)k, hist, wtot, &s_digit, &s_above, rem);
+    const int64_t nw = (n + 31) / 32;
+    for (int64_t j = tid; j < nw; j += TL_THREADS) {
+      sel[j] = 0;
+      tie[j] = 0;
+    }
+    __syncthreads();
+    for (int c = tid; c < (int)nc; c += TL_THREADS) {
+      const uint32_t u = ckey[c];
+      const int32_t sp = cpos[c];
+      if (u > vstar) atomicOr(&sel[sp >> 5], 1u << (sp & 31));
+      else if (u == vstar) atomicOr(&tie[sp >> 5], 1u << (sp & 31));
+    }
+    __syncthreads();
+  }
+  write_kept<TL_THREADS>(sel, tie, n, rem, k, out, wtot);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   dim3 grid((unsigned)a.n_rows, (unsigned)a.B);
-  hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(TK_THREADS), 0, st, a.scores, a.ld_scores,
-                     a.n_rows, a.n_k, a.q_pos, a.pos_offset, a.row_begin, a.k, a.idx);
+  if (a.n_k >= TL_MIN_N && a.k <= TL_CAP / 4)
+    hipLaunchKernelGGL(topk_long_kernel, grid, dim3(TL_THREADS), 0, st, a.scores, a.ld_scores, a.n_rows, a.n_k,
+                       a.q_pos, a.pos_offset, a.row_begin, a.k, a.idx);
+  else
+    hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(TK_THREADS), 0, st, a.scores, a.ld_scores, a.n_rows, a.n_k,
+                       a.q_pos, a.pos_offset, a.row_begin, a.k, a.idx);
   return hipGetLastError();
 }
 

@@ -153,6 +153,31 @@ def test_topk_long_rows():
     _check_topk_exact(scores, idx, 2048, lambda i: n - 1)
 
 
+def test_topk_long_rows_threshold_fallback():
+    """Long rows where a threshold estimated from evenly spaced samples cannot bracket the
+    k-th key, so the exact full-row select must take over: 1000 positives among zeros (the
+    k-th key is a tie at 0), a pattern repeating with the sample stride (every sample sees
+    the same value), all keys equal; plus an ordinary row, and a short visible prefix."""
+    _say("[topk long rows, threshold fallback]")
+    rng = np.random.default_rng(13)
+    n = 131072
+    s = np.zeros((5, n), dtype=np.float32)
+    s[0, rng.choice(n, 1000, replace=False)] = rng.random(1000).astype(np.float32) + 0.5
+    pattern = rng.standard_normal(n // 4096).astype(np.float32)
+    s[1] = np.tile(pattern, 4096)   # period 32 = the sample stride: every sample is pattern[0]
+    s[2] = 1.25
+    s[3] = rng.standard_normal(n).astype(np.float32)
+    s[4] = rng.standard_normal(n).astype(np.float32)
+    scores = torch.from_numpy(s).cuda()
+    pos = [n - 1, n - 1, n - 1, n - 1, 3000]
+    for k in (2048, 64):
+        idx = torch.stack([dsa.topk(scores[i:i + 1], k, q_pos=torch.tensor([pos[i]], dtype=torch.int32,
+                                                                            device="cuda"))[0]
+                           for i in range(5)])
+        torch.cuda.synchronize()
+        _check_topk_exact(scores, idx, k, lambda i: pos[i])
+
+
 # ------------------------------------------------------------------ sparse MLA
 
 def _random_idx(rng, n_q, n_k, k, pos):
