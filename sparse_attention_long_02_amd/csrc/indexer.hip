@@ -89,25 +89,44 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
   n_vis = n_vis > 0 ? n_vis : 0;
   const int64_t vis_tiles = (n_vis + KEY_TILE - 1) / KEY_TILE;
 
+  const int64_t all_tiles = (n_k + KEY_TILE - 1) / KEY_TILE;
+  const int64_t t_end = t0 + SPLIT_TILES < all_tiles ? t0 + SPLIT_TILES : all_tiles;
+  const int64_t t_vis = t_end < vis_tiles ? t_end : vis_tiles;
+  // tiles wholly beyond the query's position
+  for (int64_t t = (t0 > t_vis ? t0 : t_vis) + wv; t < t_end; t += 4) {
+    const int64_t key = t * KEY_TILE + lane;
+    if (key < n_k) srow[key] = -INFINITY;
+  }
+  // visible tiles of this wave: t0 + wv, t0 + wv + 4, ...; each tile's key fragments are
+  // loaded one tile ahead, while the previous tile is scored
+  int64_t t = t0 + wv;
+  if (t >= t_vis) return;
   IdxRow Q;
-  bool loaded = false;
-  for (int64_t t = t0 + wv; t < t0 + SPLIT_TILES; t += 4) {
-    const int64_t key0 = t * KEY_TILE;
-    if (key0 >= n_k) break;
-    const int64_t key = key0 + lane;
-    if (t >= vis_tiles) {  // wholly beyond the query's position
-      if (key < n_k) srow[key] = -INFINITY;
-      continue;
+  load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
+  v8i bf[4];
+  float ksc;
+  {
+    const int64_t key0 = t * KEY_TILE, key = key0 + lane;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bf[f] = global_key_fragment(kb8, key0, f, n_k);
+    ksc = ksb[key < n_k ? key : n_k - 1];
+  }
+  for (; t < t_vis; t += 4) {
+    const int64_t tn = t + 4;
+    v8i bn[4] = {bf[0], bf[1], bf[2], bf[3]};
+    float kn = ksc;
+    if (tn < t_vis) {
+      const int64_t key0 = tn * KEY_TILE, key = key0 + lane;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) bn[f] = global_key_fragment(kb8, key0, f, n_k);
+      kn = ksb[key < n_k ? key : n_k - 1];
     }
-    if (!loaded) {
-      load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
-      loaded = true;
-    }
-    const float ksc = ksb[key < n_k ? key : n_k - 1];
-    const v8i bf[4] = {global_key_fragment(kb8, key0, 0, n_k), global_key_fragment(kb8, key0, 1, n_k),
-                       global_key_fragment(kb8, key0, 2, n_k), global_key_fragment(kb8, key0, 3, n_k)};
-    const float s = score_tile64(Q, bf, ksc);
-    if (key < n_k) srow[key] = key <= pos ? s : -INFINITY;
+    const int64_t key = t * KEY_TILE + lane;
+    const float sc = score_tile64(Q, bf, ksc);
+    if (key < n_k) srow[key] = key <= pos ? sc : -INFINITY;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bf[f] = bn[f];
+    ksc = kn;
   }
 }
 

@@ -232,6 +232,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(
 constexpr int TL_THREADS = 1024;
 constexpr int TL_SAMPLES = 4096;
 constexpr int TL_CAP = 8192;
+constexpr int TL_BATCH = 8;
 constexpr int TL_MIN_N = 16384;  // rows at least this long (and k <= TL_CAP / 4) use it
 
 __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
@@ -262,20 +263,29 @@ __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
   const uint32_t srank = (uint32_t)min<int64_t>(TL_SAMPLES, 2 * expect + 16);
   uint32_t srem;
   const uint32_t T = select_lds<TL_THREADS>(ckey, TL_SAMPLES, srank, hist, wtot, &s_digit, &s_above, srem);
-  // 2. candidates: keys > T
-  for (int64_t s0 = 0; s0 < n; s0 += TL_THREADS) {
-    const int64_t s = s0 + tid;
-    const uint32_t u = s < n ? score_key(srow[s]) : 0u;
-    const bool pass = s < n && u > T;
-    const uint64_t m = ballot(pass);
-    uint32_t base = 0;
-    if ((tid & 63) == 0 && m) base = atomicAdd(&s_cnt, (uint32_t)__popcll((unsigned long long)m));
-    base = __shfl(base, 0, WAVE);
-    if (pass) {
-      const uint32_t slot = base + lanes_below(m);
-      if (slot < (uint32_t)TL_CAP) {
-        ckey[slot] = u;
-        cpos[slot] = (int32_t)s;
+  // 2. candidates: keys > T (TL_BATCH independent loads in flight per thread)
+  for (int64_t s0 = 0; s0 < n; s0 += (int64_t)TL_THREADS * TL_BATCH) {
+    float v[TL_BATCH];
+#pragma unroll
+    for (int q = 0; q < TL_BATCH; ++q) {
+      const int64_t s = s0 + (int64_t)q * TL_THREADS + tid;
+      v[q] = s < n ? srow[s] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < TL_BATCH; ++q) {
+      const int64_t s = s0 + (int64_t)q * TL_THREADS + tid;
+      const uint32_t u = score_key(v[q]);
+      const bool pass = s < n && u > T;
+      const uint64_t m = ballot(pass);
+      uint32_t base = 0;
+      if ((tid & 63) == 0 && m) base = atomicAdd(&s_cnt, (uint32_t)__popcll((unsigned long long)m));
+      base = __shfl(base, 0, WAVE);
+      if (pass) {
+        const uint32_t slot = base + lanes_below(m);
+        if (slot < (uint32_t)TL_CAP) {
+          ckey[slot] = u;
+          cpos[slot] = (int32_t)s;
+        }
       }
     }
   }
