@@ -6,20 +6,18 @@
 // section DeepSeek Sparse Attention).  Attention is computed only over the k kept keys,
 // so its cost per query is O(k) (same sections).
 //
-// bf16 kernel (H = 128, d_qk = 576, d_v = 512), one block of 8 waves per query:
-//   * waves 2h and 2h+1 share heads 32h .. +31.  The even wave forms the partial logits
-//     S^T = K Q^T over values 0..287 of each row, the odd one over values 288..575; the
-//     two exchange partials through LDS and add them in the same order, so both hold the
-//     same S.  Each then keeps the softmax state of its 32 heads and accumulates
-//     O^T = V^T P^T for its half of the 512 output values.  Per wave: Q^T operands 72
-//     registers, O^T accumulators 128, so two waves share a SIMD, and those two (w, w+4)
-//     run half a chunk apart;
-//   * 32x32x16 bf16 MFMAs: S^T is one 32 keys x 32 heads tile; O^T is 8 tiles of 32
-//     values x 32 heads;
+// bf16 kernel (H = 128, d_qk = 576, d_v = 512), one block of 4 waves per query:
+//   * wave w owns heads 32w .. 32w+31 over all 576 values of S^T = K Q^T (one 32 keys x 32
+//     heads tile, 36 MFMAs of 32x32x16 per chunk) and all 512 values of O^T = V^T P^T
+//     (16 tiles, 32 MFMAs per chunk).  Its Q^T operands take 144 vector registers and its
+//     O^T accumulators all 256 accumulation registers, so one wave runs per SIMD and no
+//     wave exchanges partial results with another;
 //   * keys are processed in chunks of 32 gathered rows.  The rows go straight from HBM to
 //     LDS with 16-byte direct loads (no staging registers; the latent half of a row is one
-//     wave-wide 1 KB load from a scalar address) into a ring of three buffers, so two
-//     chunks are in flight while one is computed;
+//     wave-wide 1 KB load from a scalar address) into a ring of four buffers: while chunk c
+//     is finished, chunks c+2 and c+3 are in flight;
+//   * per chunk, the logits of chunk c+1 are formed while the softmax of chunk c runs on
+//     the VALU between those MFMAs, then O^T += V^T P^T for chunk c;
 //   * after the softmax each lane already holds P^T in the B-operand layout of the PV
 //     product; V^T is read from the same row-major rows with the gfx950 transposing LDS
 //     read, so no transposed copy is stored;
@@ -40,19 +38,23 @@ constexpr int MH = 128, MDQK = 576, MDV = 512, KC = 32;
 //     banks), and within row r the 16-byte unit u is stored at unit u ^ ((r >> 2) & 3).
 //     Both read patterns are then free of bank conflicts: the K operand (one unit of 16
 //     rows per pass) and the transposed V operand (4 consecutive rows x 4 units per pass);
-//   rope:   values 512..575 of each row, 144 B apart (128 B + one unused unit).
-constexpr int LAT_PITCH = 1088, ROPE_PITCH = 144;
-constexpr int LAT_BYTES = KC * LAT_PITCH;                      // 34816
-constexpr int ROPE_UNITS = KC * ROPE_PITCH / 16;               // 288
-constexpr int ROPE_INSTR = (ROPE_UNITS + 63) / 64;             // 5
-constexpr int CHUNK_BYTES = LAT_BYTES + ROPE_INSTR * 64 * 16;  // 34816 + 5120 = 39936
+//   rope:   values 512..575 of each row, 128 B apart, unit u of row r stored at unit
+//     u ^ ((r >> 1) & 7): 16 consecutive rows at one unit then fall in 16 distinct
+//     16-byte bank groups.
+constexpr int LAT_PITCH = 1088, ROPE_PITCH = 128;
+constexpr int LAT_BYTES = KC * LAT_PITCH;                 // 34816
+constexpr int CHUNK_BYTES = LAT_BYTES + KC * ROPE_PITCH;  // 38912
+constexpr int NBUF = 4;                                   // chunk buffers (4 x 38912 B)
 __device__ __forceinline__ int lat_swz(int r) { return (r >> 2) & 3; }
-constexpr int MLA_WAVES = 8;
-constexpr int HALF_STEPS = MDQK / 2 / 16;                      // 18 d-steps of 16 per half
-constexpr int MAX_K = 2048;
+__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
+constexpr int MLA_WAVES = 4;
+constexpr int D_STEPS = MDQK / 16;  // 36 contraction steps of S^T
+constexpr int O_TILES = MDV / 32;   // 16 O^T tiles per wave
+constexpr int MAX_K = 2048, MAX_CHUNKS = MAX_K / KC;
+constexpr int LOADS_PER_CHUNK = 9;  // per wave: 8 latent rows + 1 rope instruction
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float RESCALE_SLACK = 8.f;              // log2 units the running max may lag
+constexpr float RESCALE_SLACK = 8.f;  // log2 units the running max may lag
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -67,8 +69,167 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+
+// O^T += V^T P^T for one chunk: 32 MFMAs (key step s = i/16, value tile t = i%16) with the
+// accumulator tiles pinned in the accumulation registers (a[]): the 16 O^T tiles of a
+// wave take all 256 of them, leaving the 256 vector registers for the Q^T operands, the
+// logits and the fragments.  Written as one block so that the V^T fragments (two
+// transposing reads each, into the four staging quads v240..v255) run three MFMAs ahead
+// with exact LDS counter waits.  The matrix core forwards an accumulator to the next MFMA
+// on the same tile without wait states; P^T and the tiles were last written by the VALU at
+// least the 7 instructions of the block's head earlier (2 wait states are required).
+// `va` / `vb`: LDS byte addresses of this lane's first / second read of fragment 0.
+__device__ __forceinline__ void pv_chunk(v16f* O, v8bf P0, v8bf P1, uint32_t va, uint32_t vb) {
+  asm volatile(
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:64\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:64\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:128\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:128\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], v[240:243], %[p0], %[o0]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:192\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:192\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], v[244:247], %[p0], %[o1]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:256\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o2], v[248:251], %[p0], %[o2]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:320\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:320\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o3], v[252:255], %[p0], %[o3]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:384\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p0], %[o4]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:448\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:448\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p0], %[o5]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:512\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p0], %[o6]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:576\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:576\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p0], %[o7]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:640\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:640\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o8], v[240:243], %[p0], %[o8]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:704\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:704\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o9], v[244:247], %[p0], %[o9]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o10], v[248:251], %[p0], %[o10]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:832\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:832\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o11], v[252:255], %[p0], %[o11]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:896\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:896\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p0], %[o12]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:960\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:960\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p0], %[o13]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:17408\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:17408\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p0], %[o14]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:17472\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:17472\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p0], %[o15]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:17536\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:17536\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], v[240:243], %[p1], %[o0]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:17600\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:17600\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], v[244:247], %[p1], %[o1]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:17664\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:17664\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o2], v[248:251], %[p1], %[o2]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:17728\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:17728\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o3], v[252:255], %[p1], %[o3]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:17792\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:17792\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p1], %[o4]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:17856\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:17856\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p1], %[o5]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:17920\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:17920\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p1], %[o6]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:17984\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:17984\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p1], %[o7]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:18048\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:18048\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o8], v[240:243], %[p1], %[o8]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:18112\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:18112\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o9], v[244:247], %[p1], %[o9]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[va] offset:18176\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[vb] offset:18176\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o10], v[248:251], %[p1], %[o10]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[va] offset:18240\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[vb] offset:18240\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o11], v[252:255], %[p1], %[o11]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[va] offset:18304\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[vb] offset:18304\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o12], v[240:243], %[p1], %[o12]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[va] offset:18368\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[vb] offset:18368\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o13], v[244:247], %[p1], %[o13]\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o14], v[248:251], %[p1], %[o14]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o15], v[252:255], %[p1], %[o15]\n\t"
+      : [o0] "+a"(O[0]), [o1] "+a"(O[1]), [o2] "+a"(O[2]), [o3] "+a"(O[3]), [o4] "+a"(O[4]),
+        [o5] "+a"(O[5]), [o6] "+a"(O[6]), [o7] "+a"(O[7]), [o8] "+a"(O[8]), [o9] "+a"(O[9]),
+        [o10] "+a"(O[10]), [o11] "+a"(O[11]), [o12] "+a"(O[12]), [o13] "+a"(O[13]), [o14] "+a"(O[14]),
+        [o15] "+a"(O[15])
+      : [p0] "v"(P0), [p1] "v"(P1), [va] "v"(va), [vb] "v"(vb)
+      : "memory", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
+        "v251", "v252", "v253", "v254", "v255");
+}
+
+// Orders every access to the O^T tiles after the last MFMA issued on them and before the
+// next: 20 wait states cover an MFMA result read or overwritten by the VALU (and the
+// VALU-write-then-MFMA-read case), whatever the pass count.
+__device__ __forceinline__ void o_guard(v16f* O) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]), "+a"(O[6]),
+                 "+a"(O[7]), "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]), "+a"(O[12]), "+a"(O[13]),
+                 "+a"(O[14]), "+a"(O[15]));
+}
+
 // instruction classes for the scheduler's interleave directives
-constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
 
 // two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -78,206 +239,133 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 }
 
 // The value itself, opaque to the optimiser: keeps lane offsets from being computed once
-// and held across the chunk loop (they would not fit in registers beside the Q^T operands
-// and the accumulators); recomputing them costs a few VALU ops per chunk.
+// and held across the chunk loop, where registers are scarce.
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
 
-__device__ __forceinline__ int64_t safe_row(int32_t s, int64_t n_k) {
-  return (s >= 0 && s < n_k) ? (int64_t)s : 0;
+// Issue this wave's direct global->LDS loads for chunk c: rows 8w .. 8w+7 of the chunk,
+// each latent half as one wave-wide 1 KB load from a scalar row address, and their rope
+// parts as one instruction whose lane L loads unit (L%8) ^ swz of row 8w + L/8.
+// ids outside [0, n_k) load row 0 (their keys are masked).
+__device__ __forceinline__ uint32_t safe_row(int32_t s, uint32_t n_k) {
+  return (uint32_t)s < n_k ? (uint32_t)s : 0u;
+}
+// Workgroup barrier that is also a compiler memory barrier (LDS accesses stay on their side),
+// with no wait-counter drain: the chunk loads stay in flight across it.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" : : : "memory");
 }
 
-// Issue this wave's direct global->LDS loads for chunk c (rows ids[32c .. 32c+31]): the
-// latent halves of rows 4w .. 4w+3 (one wave-wide 1 KB load each, scalar row address)
-// and, for w < 5, rope instruction w, whose lane loads unit u = 64w + lane: row u / 9,
-// 16-byte unit u % 9 of the row's rope part (unit 8 is the pitch padding and loads a
-// harmless copy).  Waves 0-4 issue 5 loads, waves 5-7 issue 4.
-__device__ __forceinline__ void gather_chunk(uint8_t* buf, const uint16_t* __restrict__ kvb,
-                                             const int32_t* ids, int c, int64_t n_k, int wv, int lane) {
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// One direct global->LDS load of 16 bytes per lane: lane i's bytes go to LDS address
+// lds + 16 i.  Issued from inline asm, so the compiler's wait-counter model does not see
+// it: the chunk ring is ordered by explicit vector-memory waits and barriers instead, and
+// the LDS reads of the logits keep exact LDS-counter waits (a direct load the compiler can
+// see would force every LDS wait behind it to zero).  No register is written; one wait
+// state separates the M0 write from the load that reads it.  M0 holds nothing else in
+// this file's kernels, so clobbering it is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_saddr(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_vaddr(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(gaddr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void gather_chunk(uint32_t buf, const uint16_t* __restrict__ kvb, const int32_t* ids,
+                                             int c, uint32_t n_k, int wv, int lane) {
+  const int32_t* cid = ids + c * KC + 8 * wv;
+  // all eight ids first (each DMA statement is a compiler memory barrier)
+  const int4 i0 = *reinterpret_cast<const int4*>(cid);
+  const int4 i1 = *reinterpret_cast<const int4*>(cid + 4);
+  const int32_t idv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+  const uint32_t rope_row = safe_row(cid[lane >> 3], n_k);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 4 * wv + j;
-    const int64_t row = safe_row(__builtin_amdgcn_readfirstlane(ids[c * KC + r]), n_k);
-    // LDS unit `lane` of the row holds the row's unit lane ^ swz
-    __builtin_amdgcn_global_load_lds(kvb + row * MDQK + 8 * (lane ^ lat_swz(r)), buf + r * LAT_PITCH, 16, 0, 0);
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * wv + j;
+    const uint32_t row = safe_row(__builtin_amdgcn_readfirstlane(idv[j]), n_k);
+    dma16_saddr(kvb + (size_t)row * MDQK, 16 * (lane ^ lat_swz(r)), buf + r * LAT_PITCH);
   }
-  if (wv < ROPE_INSTR) {
-    const int u = opaque(wv * 64 + lane);
-    const int rope_r = min(u / 9, KC - 1);
-    const int rope_e = 512 + 8 * ((u % 9) & 7);
-    const int64_t row = safe_row(ids[c * KC + rope_r], n_k);
-    __builtin_amdgcn_global_load_lds(kvb + row * MDQK + rope_e, buf + LAT_BYTES + wv * 1024, 16, 0, 0);
-  }
+  const int r = 8 * wv + (lane >> 3);
+  const uint32_t row = rope_row;
+  dma16_vaddr(kvb + (size_t)row * MDQK + 512 + 8 * ((lane & 7) ^ rope_swz(r)), buf + LAT_BYTES + wv * 1024);
 }
 
 // A operand of S^T for d-step ds (values 16ds .. 16ds+15): row = key r = l%32, elements
-// 16ds + 8(l/32) .. +7, i.e. logical unit 2ds + g of the row (g = l/32), stored at unit
-// (2ds + g) ^ swz(r).  As the swizzle only flips the two low unit bits, that is
-// 2ds + ((g ^ swz) & 1) + (swz & 2) for even ds and 2ds + ((g ^ swz) & 1) - (swz & 2) for
-// odd ds: `lat_e` / `lat_o` are this lane's byte offsets of those two cases at ds = 0, so
-// the step offsets 32ds are compile-time constants that fold into the LDS read's
-// immediate.  `rope` = this lane's offset of step 32 in the rope region.
-__device__ __forceinline__ v8bf krow_frag(const uint8_t* buf, int lat_e, int lat_o, int rope, int ds) {
-  const uint8_t* p = ds < 32 ? buf + ((ds & 1) ? lat_o : lat_e) + 32 * ds : buf + rope + 32 * (ds - 32);
-  return *reinterpret_cast<const v8bf*>(p);
+// 16ds + 8(l/32) .. +7, i.e. logical unit 2ds + g of the row (g = l/32).  Latent steps
+// (ds < 32): stored at unit (2ds + g) ^ swz(r); as the swizzle only flips the two low
+// unit bits, that is 2ds + ((g ^ swz) & 1) + (swz & 2) for even ds and
+// 2ds + ((g ^ swz) & 1) - (swz & 2) for odd ds, so `lat_e` / `lat_o` (this lane's byte
+// offsets of those two cases at ds = 0) plus the constant 32ds address every step.  Rope
+// steps (ds >= 32) use `rope`, this lane's offset for that step.
+__device__ __forceinline__ v8bf k_frag(const uint8_t* buf, int off) {
+  return *reinterpret_cast<const v8bf*>(buf + off);
+}
+__device__ __forceinline__ int rope_offset(int r, int g, int ds) {
+  return LAT_BYTES + r * ROPE_PITCH + 16 * ((2 * (ds - 32) + g) ^ rope_swz(r));
 }
 
-// A operand of O^T = V^T P^T for latent values d0 .. d0+31 (rows) and key step s: the
+// A operand of O^T = V^T P^T for latent values 32t .. 32t+31 (rows) and key step s: the
 // contraction slots j of lane group g = l/32 are keys 16s + 4g + 8(j/4) + j%4, the keys
 // whose probabilities that lane holds in P^T slot j.  The gfx950 transposing LDS read does
 // the transpose: in a 16-lane group, lanes 4rr..4rr+3 supply 16 values of one key and lane
 // p receives value p of the group's 16 values for four keys.
 // Lane (G = l/16, p = l%16, rr = p/4, qq = p%4) reads row 16s + 4(G/2) + rr (first read;
-// second read: 8 rows further), values d0 + 16(G%2) + 4qq .. +3 = logical unit
-// 32 half + 4t + 2(G%2) + qq/2, bytes 8(qq%2) within it.  The row's swizzle is G/2 (first
-// read) or G/2 + 2 (second read) for every s, and it only flips the unit's two low bits,
-// so `vt0` / `vt1` (byte offsets at s = 0, t = 0) plus the constants 16 s LAT_PITCH + 64 t
-// address every fragment.
-__device__ __forceinline__ int vt_lane_offset(int half, int second) {
+// second read: 8 rows further), values 32t + 16(G%2) + 4qq .. +3 = logical unit
+// 4t + 2(G%2) + qq/2, bytes 8(qq%2) within it.  The row's swizzle is G/2 (first read) or
+// G/2 + 2 (second read) for every s, and it only flips the unit's two low bits, so `vt0` /
+// `vt1` (byte offsets at s = 0, t = 0) plus the constants 16 s LAT_PITCH + 64 t address
+// every fragment.
+__device__ __forceinline__ int vt_lane_offset(int second) {
   const int l = lane_id();
   const int p = l & 15, G = l >> 4;
   const int rr = p >> 2, qq = p & 3;
   const int row = 4 * (G >> 1) + rr + 8 * second;
-  const int unit = 32 * half + ((2 * (G & 1) + (qq >> 1)) ^ lat_swz(row));
+  const int unit = (2 * (G & 1) + (qq >> 1)) ^ lat_swz(row);
   return row * LAT_PITCH + 16 * unit + 8 * (qq & 1);
 }
-__device__ __forceinline__ v8bf vt_frag(const uint8_t* buf, int vt0, int vt1, int t, int s) {
-  typedef __attribute__((address_space(3))) v4s* lds_v4s;
-  const uint8_t* a0 = buf + vt0 + 16 * s * LAT_PITCH + 64 * t;
-  const uint8_t* a1 = buf + vt1 + 16 * s * LAT_PITCH + 64 * t;
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(__attribute__((address_space(3))) uint8_t*)a0);
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(__attribute__((address_space(3))) uint8_t*)a1);
-  const v8s v = v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(v8bf, v);
-}
-
-struct MlaState {
-  v8bf Qt[HALF_STEPS];  // B operands of S^T for this wave's 288 values
-  v16f O[8];            // O^T tiles: values 256*half + 32t + row, head l%32
-  float m_ref, l_run;   // softmax state of head l%32 (the same in both lane halves)
+// This lane's K-fragment offsets (see k_frag / rope_offset), from a lane index the
+// optimiser cannot hoist out of the chunk loop.
+struct KOff {
+  int lat_e, lat_o, r, g;
 };
-
-// Partial-logit exchange between the two waves of a head group: [wave][4][64 lanes][4].
-__shared__ __align__(16) float s_xch[MLA_WAVES][4][64][4];
-
-// Phase 1 of a chunk: this wave's partial logits S^T over its 288 values, left in its
-// exchange slot.
-__device__ __forceinline__ void mla_logits(const MlaState& st, const uint8_t* buf, int wv, int half) {
-  // lane offsets recomputed per chunk (a few VALU ops) rather than held across the loop
+__device__ __forceinline__ KOff k_offsets() {
   const int l = opaque(lane_id());
-  const int r = l & 31, g = l >> 5;
-  const int swz = lat_swz(r);
-  const int lat_e = r * LAT_PITCH + 16 * (((g ^ swz) & 1) + (swz & 2));
-  const int lat_o = r * LAT_PITCH + 16 * (((g ^ swz) & 1) - (swz & 2));
-  const int rope = LAT_BYTES + r * ROPE_PITCH + 16 * g;
+  KOff o;
+  o.r = l & 31;
+  o.g = l >> 5;
+  const int swz = lat_swz(o.r);
+  o.lat_e = o.r * LAT_PITCH + 16 * (((o.g ^ swz) & 1) + (swz & 2));
+  o.lat_o = o.r * LAT_PITCH + 16 * (((o.g ^ swz) & 1) - (swz & 2));
+  return o;
+}
+__device__ __forceinline__ int k_off(const KOff& o, int ds) {
+  return ds < 32 ? ((ds & 1) ? o.lat_o : o.lat_e) + 32 * ds : rope_offset(o.r, o.g, ds);
+}
+
+// S^T (32 keys x this wave's 32 heads) of one chunk, all 36 steps (used for the first chunk).
+__device__ __forceinline__ v16f mla_logits(const v8bf* Qt, const uint8_t* buf) {
+  const KOff ko = k_offsets();
   v16f S = {};
-  // each K fragment read is issued one step ahead of the MFMA that uses it
-  if (half == 0) {
 #pragma unroll
-    for (int j = 0; j < HALF_STEPS; ++j) S = mfma_bf16_32x32x16(krow_frag(buf, lat_e, lat_o, rope, j), st.Qt[j], S);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-#pragma unroll
-    for (int j = 0; j < HALF_STEPS - 1; ++j) {
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-  } else {
-#pragma unroll
-    for (int j = 0; j < HALF_STEPS; ++j)
-      S = mfma_bf16_32x32x16(krow_frag(buf, lat_e, lat_o, rope, HALF_STEPS + j), st.Qt[j], S);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-#pragma unroll
-    for (int j = 0; j < HALF_STEPS - 1; ++j) {
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<float4*>(&s_xch[wv][q][l][0]) = make_float4(S[4 * q], S[4 * q + 1], S[4 * q + 2], S[4 * q + 3]);
+  for (int ds = 0; ds < D_STEPS; ++ds) S = mfma_bf16_32x32x16(k_frag(buf, k_off(ko, ds)), Qt[ds], S);
+  return S;
 }
 
-// Phase 2 of a chunk (after a barrier): S = S(values 0..287) + S(values 288..575) read
-// from the two exchange slots in that order (so both waves hold the same bits), online
-// softmax (base 2, lazily rescaled), O^T += V^T P^T.
-__device__ __forceinline__ void mla_update(MlaState& st, const uint8_t* buf, uint32_t vmask, float scale_log2,
-                                           int wv, int half) {
-  const int l = lane_id(), g = l >> 5;
-  const int vt0 = opaque(vt_lane_offset(half, 0)), vt1 = opaque(vt_lane_offset(half, 1));
-  v16f S;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 a = *reinterpret_cast<const float4*>(&s_xch[wv & ~1][q][l][0]);
-    const float4 o = *reinterpret_cast<const float4*>(&s_xch[wv | 1][q][l][0]);
-    S[4 * q] = a.x + o.x;
-    S[4 * q + 1] = a.y + o.y;
-    S[4 * q + 2] = a.z + o.z;
-    S[4 * q + 3] = a.w + o.w;
-  }
-  // lane holds head l%32 and keys 8(r/4) + 4g + r%4; S becomes the base-2 logits
-  float mx = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const bool ok = (vmask >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u;
-    S[r] = ok ? S[r] * scale_log2 : -INFINITY;
-    mx = fmaxf(mx, S[r]);
-  }
-  mx = fmaxf(mx, xor32(mx));
-  // move the reference max only when a logit exceeds it by more than the slack
-  if (ballot(mx > st.m_ref + RESCALE_SLACK)) {
-    const float m_new = fmaxf(st.m_ref, mx);
-    const float alpha = st.m_ref == -INFINITY ? 0.f : exp2f(st.m_ref - m_new);
-    st.l_run *= alpha;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) st.O[t] *= alpha;
-    st.m_ref = m_new;
-  }
-  // m is finite once any key of the row was valid; before that every logit is -inf and
-  // m = -inf, so use 0 as the offset (exp2(-inf) = 0 either way)
-  const float m = st.m_ref == -INFINITY ? 0.f : st.m_ref;
-  float ps = 0.f;
-  uint32_t pk[8];
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(S[r] - m);
-    const float p1 = __builtin_amdgcn_exp2f(S[r + 1] - m);
-    ps += p0 + p1;
-    pk[r >> 1] = cvt_pk_bf16(p0, p1);
-  }
-  ps += xor32(ps);
-  st.l_run += ps;
-  // P^T for key step s = slots 8s .. 8s+7 (keys 16s + 4g + 8(j/4) + j%4)
-  const v8bf P0 = __builtin_bit_cast(v8bf, v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
-  const v8bf P1 = __builtin_bit_cast(v8bf, v4i{(int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]});
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    st.O[t] = mfma_bf16_32x32x16(vt_frag(buf, vt0, vt1, t, 0), P0, st.O[t]);
-    st.O[t] = mfma_bf16_32x32x16(vt_frag(buf, vt0, vt1, t, 1), P1, st.O[t]);
-  }
-  // V fragment reads (two per MFMA) run one MFMA ahead
-  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
-#pragma unroll
-  for (int j = 0; j < 15; ++j) {
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
-  }
-  __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ uint32_t chunk_mask(const int32_t* ids, int c, int64_t n_k) {
-  const int32_t s = ids[c * KC + (lane_id() & 31)];
-  return (uint32_t)ballot(s >= 0 && s < n_k);
-}
-
-// grid.x = n_q * n_split, grid.y = B.  Pipeline: chunk c+1 is in flight while chunk c is
-// computed, and chunk c+2's loads are issued right after (3 LDS buffers, loop unrolled by 3
-// so each buffer is a distinct static array).
+// grid.x = n_q * n_split, grid.y = B.  One block of 4 waves per query (and key split);
+// wave w owns heads 32w .. 32w+31 over all 576 values (S^T) and all 512 output values
+// (O^T).  Pipeline over chunks of 32 selected rows, 4 LDS buffers: in the step of chunk
+// c, chunks c+2 and c+3 are in flight, the logits of chunk c+1 are formed while the
+// softmax of chunk c runs, then O^T += V^T P^T for chunk c.
 __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int64_t n_q, int64_t n_k, int k, float scale_log2, int n_split, uint16_t* __restrict__ out,
@@ -285,134 +373,172 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   __shared__ __align__(16) uint8_t buf0[CHUNK_BYTES];
   __shared__ __align__(16) uint8_t buf1[CHUNK_BYTES];
   __shared__ __align__(16) uint8_t buf2[CHUNK_BYTES];
+  __shared__ __align__(16) uint8_t buf3[CHUNK_BYTES];
   __shared__ int32_t ids[MAX_K];
-  __shared__ int32_t s_last[MLA_WAVES];
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 5;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
-  const bool grp_x = wv < 4;
-  const int hg = wv >> 1, half = wv & 1;  // head group (heads 32hg..), value half of the pair
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.y;
   const int64_t qi = blockIdx.x / n_split;
   const int split = blockIdx.x % n_split;
   const int64_t qrow = (int64_t)b * n_q + qi;
   const int32_t* irow = idx + qrow * k;
   const uint16_t* kvb = kv + (int64_t)b * n_k * MDQK;
-  const int head = 32 * hg + (l & 31);
 
-  MlaState st;
-  const uint16_t* qh = q + (qrow * MH + head) * MDQK + 288 * half + 8 * g;
+  // B operands of S^T: head 32w + l%32, values 16ds + 8g .. +7
+  v8bf Qt[D_STEPS];
+  {
+    const uint16_t* qh = q + (qrow * MH + 32 * wv + (l & 31)) * MDQK + 8 * g;
 #pragma unroll
-  for (int j = 0; j < HALF_STEPS; ++j) st.Qt[j] = *reinterpret_cast<const v8bf*>(qh + 16 * j);
-
-  // the row's selected ids -> LDS; chunks up to the last valid id
-  int last = -1;
-  for (int j = tid; j < k; j += MLA_WAVES * 64) {
-    const int32_t s = irow[j];
-    ids[j] = s;
-    if (s >= 0 && s < n_k) last = j;
+    for (int ds = 0; ds < D_STEPS; ++ds) Qt[ds] = *reinterpret_cast<const v8bf*>(qh + 16 * ds);
   }
-  last = (int)wave_max((float)last);
-  if (l == 0) s_last[wv] = last;
+
+  // the row's selected ids -> LDS; every wave then finds the last valid one, and the
+  // chunks run up to the one holding it
+  const uint32_t nk = (uint32_t)min(n_k, (int64_t)INT32_MAX);
+  for (int j = tid; j < k; j += MLA_WAVES * 64) ids[j] = irow[j];
   __syncthreads();
-#pragma unroll
-  for (int w = 0; w < MLA_WAVES; ++w) last = max(last, s_last[w]);
+  int last = -1;
+  for (int j = l; j < k; j += 64)
+    if ((uint32_t)ids[j] < nk) last = j;
+  last = (int)wave_max((float)last);
   const int nchunks = (last + KC) / KC;
   const int c_lo = (int)((int64_t)nchunks * split / n_split);
   const int c_hi = (int)((int64_t)nchunks * (split + 1) / n_split);
-
-#pragma unroll
-  for (int t = 0; t < 8; ++t) st.O[t] = v16f{};
-  st.m_ref = -INFINITY;
-  st.l_run = 0.f;
-
-  uint8_t* bufs[3] = {buf0, buf1, buf2};
   const int n = c_hi - c_lo;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    if (j < n) gather_chunk(bufs[j], kvb, ids, c_lo + j, n_k, wv, l);
 
-  // Chunk periods p = 0..n, each split by two barriers.  Waves 0-3 (group X) form chunk
-  // p's logits in the first half and finish chunk p in the second; waves 4-7 (group Y)
-  // finish chunk p-1 in the first half and form chunk p's logits in the second.  The two
-  // waves of a SIMD (w, w+4) are in different groups, so one's softmax and fragment reads
-  // run while the other's MFMAs keep the matrix core busy.
-  // the two groups run the same barriers in separate loops (one ordering each keeps the
-  // register allocation of the two orderings apart)
-#define MLA_WAIT_CHUNK(p)                   \
-  if (wv < ROPE_INSTR) {                    \
-    if ((p) + 1 < n) VMCNT(5);              \
-    else VMCNT(0);                          \
-  } else {                                  \
-    if ((p) + 1 < n) VMCNT(4);              \
-    else VMCNT(0);                          \
-  }                                         \
-  LGKM0();                                  \
-  __builtin_amdgcn_s_barrier()
-  if (grp_x) {
-    for (int base = 0; base <= n; base += 3) {
+  v16f O[O_TILES];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int p = base + j;
-        if (p <= n) {
-          MLA_WAIT_CHUNK(p);
-          if (p < n) mla_logits(st, bufs[j], wv, half);
-          LGKM0();
-          __builtin_amdgcn_s_barrier();
-          if (p + 2 < n) gather_chunk(bufs[(j + 2) % 3], kvb, ids, c_lo + p + 2, n_k, wv, l);
-          if (p < n) mla_update(st, bufs[j], chunk_mask(ids, c_lo + p, n_k), scale_log2, wv, half);
-        }
-      }
-    }
-  } else {
-    for (int base = 0; base <= n; base += 3) {
+  for (int t = 0; t < O_TILES; ++t) O[t] = v16f{};
+  float m_ref = -INFINITY, l_run = 0.f;
+
+  uint8_t* bufs[NBUF] = {buf0, buf1, buf2, buf3};
+  VMCNT(0);  // the Q^T operands are in registers before the chunk loads start
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int p = base + j;
-        if (p <= n) {
-          MLA_WAIT_CHUNK(p);
-          if (p >= 1)
-            mla_update(st, bufs[(j + 2) % 3], chunk_mask(ids, c_lo + p - 1, n_k), scale_log2, wv, half);
-          LGKM0();
-          __builtin_amdgcn_s_barrier();
-          if (p + 2 < n) gather_chunk(bufs[(j + 2) % 3], kvb, ids, c_lo + p + 2, n_k, wv, l);
-          if (p < n) mla_logits(st, bufs[j], wv, half);
+  for (int j = 0; j < 3; ++j)
+    if (j < n) gather_chunk(lds_addr(bufs[j]), kvb, ids, c_lo + j, nk, wv, l);
+
+  v16f S_cur = {};
+  if (n > 0) {
+    if (n >= 3) VMCNT(2 * LOADS_PER_CHUNK);
+    else if (n == 2) VMCNT(LOADS_PER_CHUNK);
+    else VMCNT(0);
+    block_barrier();
+    S_cur = mla_logits(Qt, buf0);
+  }
+
+  for (int base = 0; base < n; base += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      const int c = base + j;
+      if (c < n) {
+        // chunk c+1 has landed (every wave's loads), and chunk c-1's buffer is free
+        if (c + 2 < n) VMCNT(LOADS_PER_CHUNK);
+        else VMCNT(0);
+        LGKM0();
+        block_barrier();
+        if (c + 3 < n) gather_chunk(lds_addr(bufs[(j + 3) % NBUF]), kvb, ids, c_lo + c + 3, nk, wv, l);
+        // online softmax of chunk c (base 2, lazily rescaled) interleaved with the logits
+        // of chunk c+1 (formed from a stale buffer on the last chunk, and then unused):
+        // lane holds head l%32 and keys 8(r/4) + 4g + r%4 of S^T
+        const uint32_t vmask = (uint32_t)ballot((uint32_t)ids[(c_lo + c) * KC + (l & 31)] < nk);
+        if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((vmask >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u)) S_cur[r] = -INFINITY;
         }
+        const uint8_t* bn = bufs[(j + 1) % NBUF];
+        const KOff ko = k_offsets();
+        v8bf kf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[i] = k_frag(bn, k_off(ko, i));
+        v16f S_next = {};
+        // first half of the logits, with the chunk's row max
+#pragma unroll
+        for (int ds = 0; ds < D_STEPS / 2; ++ds) {
+          S_next = mfma_bf16_32x32x16(kf[ds & 3], Qt[ds], S_next);
+          kf[ds & 3] = k_frag(bn, k_off(ko, ds + 4));
+        }
+        float mx = fmaxf(fmaxf(S_cur[0], S_cur[1]), S_cur[2]);
+#pragma unroll
+        for (int r = 3; r < 16; r += 2) mx = fmaxf(fmaxf(mx, S_cur[r]), S_cur[r + 1]);
+        mx = fmaxf(mx, S_cur[15]);
+        mx = fmaxf(mx, xor32(mx)) * scale_log2;
+        if (ballot(mx > m_ref + RESCALE_SLACK)) {
+          const float m_new = fmaxf(m_ref, mx);
+          if (ballot(m_ref != -INFINITY)) {
+            const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
+            l_run *= alpha;
+            o_guard(O);
+            // one tile at a time, each back in its accumulation registers before the next
+#pragma unroll
+            for (int t = 0; t < O_TILES; ++t) {
+              O[t] *= alpha;
+              asm volatile("" : "+a"(O[t]));
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            o_guard(O);
+          }
+          m_ref = m_new;
+        }
+        // second half of the logits, with the probabilities.  Before any valid key,
+        // m_ref = -inf and every logit is -inf: offset 0.
+        const float m = m_ref == -INFINITY ? 0.f : m_ref;
+#pragma unroll
+        for (int ds = D_STEPS / 2; ds < D_STEPS; ++ds) {
+          S_next = mfma_bf16_32x32x16(kf[ds & 3], Qt[ds], S_next);
+          if (ds + 4 < D_STEPS) kf[ds & 3] = k_frag(bn, k_off(ko, ds + 4));
+        }
+        float ps = 0.f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S_cur[r], scale_log2, -m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S_cur[r + 1], scale_log2, -m));
+          ps += p0 + p1;
+          pk[r >> 1] = cvt_pk_bf16(p0, p1);
+        }
+        ps += xor32(ps);
+        l_run += ps;
+        const v8bf P0 = __builtin_bit_cast(v8bf, v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
+        const v8bf P1 = __builtin_bit_cast(v8bf, v4i{(int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]});
+        const uint32_t bc = lds_addr(bufs[j]);
+        pv_chunk(O, P0, P1, bc + opaque(vt_lane_offset(0)), bc + opaque(vt_lane_offset(1)));
+        S_cur = S_next;
       }
     }
   }
-#undef MLA_WAIT_CHUNK
 
-  // ---- epilogue: lane holds head 32hg + l%32, values 256 half + 32t + 8(r/4) + 4g + r%4
-  // (addresses recomputed here rather than kept from the prologue across the loop)
+  // ---- epilogue: lane holds head 32w + l%32, values 32t + 8(r/4) + 4g + r%4
+  o_guard(O);
   const int le = opaque(l);
   const int ge = le >> 5;
-  const int64_t row_head = ((int64_t)b * n_q + qi) * MH + 32 * hg + (le & 31);
-  const bool nonempty = st.l_run > 0.f;
-  const float inv = nonempty ? 1.f / st.l_run : 0.f;
-  const float lse_v = nonempty ? (st.m_ref + log2f(st.l_run)) * LN2 : -INFINITY;
+  const int64_t row_head = ((int64_t)b * n_q + qi) * MH + 32 * wv + (le & 31);
+  const bool nonempty = l_run > 0.f;
+  const float inv = nonempty ? 1.f / l_run : 0.f;
+  const float lse_v = nonempty ? (m_ref + log2f(l_run)) * LN2 : -INFINITY;
   if (n_split == 1) {
-    uint16_t* orow = out + row_head * MDV + 256 * half + 4 * ge;
+    uint16_t* orow = out + row_head * MDV + 4 * ge;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < O_TILES; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint2 pkd;
-        pkd.x = pack_bf16x2(st.O[t][4 * i] * inv, st.O[t][4 * i + 1] * inv);
-        pkd.y = pack_bf16x2(st.O[t][4 * i + 2] * inv, st.O[t][4 * i + 3] * inv);
+        pkd.x = pack_bf16x2(O[t][4 * i] * inv, O[t][4 * i + 1] * inv);
+        pkd.y = pack_bf16x2(O[t][4 * i + 2] * inv, O[t][4 * i + 3] * inv);
         *reinterpret_cast<uint2*>(orow + 32 * t + 8 * i) = pkd;
       }
-    if (lse && half == 0 && ge == 0) lse[row_head] = lse_v;
+    if (lse && ge == 0) lse[row_head] = lse_v;
   } else {
-    const int64_t prh = (((int64_t)b * n_q + qi) * n_split + split) * MH + 32 * hg + (le & 31);
-    float* prow = part_o + prh * MDV + 256 * half + 4 * ge;
+    const int64_t prh = (((int64_t)b * n_q + qi) * n_split + split) * MH + 32 * wv + (le & 31);
+    float* prow = part_o + prh * MDV + 4 * ge;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < O_TILES; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<v4f*>(prow + 32 * t + 8 * i) =
-            v4f{st.O[t][4 * i], st.O[t][4 * i + 1], st.O[t][4 * i + 2], st.O[t][4 * i + 3]} * inv;
-    if (half == 0 && ge == 0) part_lse[prh] = lse_v;
+            v4f{O[t][4 * i], O[t][4 * i + 1], O[t][4 * i + 2], O[t][4 * i + 3]} * inv;
+    if (ge == 0) part_lse[prh] = lse_v;
   }
 }
 
