@@ -48,6 +48,7 @@ constexpr int NBUF = 4;                                   // chunk buffers (4 x 
 __device__ __forceinline__ int lat_swz(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 constexpr int MLA_WAVES = 4;
+constexpr int KRING = 10;  // K fragments read ahead of the logit MFMAs
 constexpr int D_STEPS = MDQK / 16;  // 36 contraction steps of S^T
 constexpr int O_TILES = MDV / 32;   // 16 O^T tiles per wave
 constexpr int MAX_K = 2048, MAX_CHUNKS = MAX_K / KC;
@@ -269,35 +270,73 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the LDS reads of the logits keep exact LDS-counter waits (a direct load the compiler can
 // see would force every LDS wait behind it to zero).  No register is written; one wait
 // state separates the M0 write from the load that reads it.  M0 holds nothing else in
-// this file's kernels, so clobbering it is safe.
+// this file's kernels, so clobbering it is safe.  The exec mask is narrowed for the load
+// and restored; the AND sets SCC, which is therefore clobbered too.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16_saddr(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(gbase)
-               : "memory", "m0");
+__device__ __forceinline__ void dma16_saddr(const void* gbase, uint32_t voff, uint32_t lds, uint64_t on) {
+  uint64_t sv;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b64 exec, exec, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %4\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(sv)
+      : "s"(on), "s"(lds), "v"(voff), "s"(gbase)
+      : "memory", "m0", "scc");
 }
-__device__ __forceinline__ void dma16_vaddr(const void* gaddr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(gaddr) : "memory", "m0");
+__device__ __forceinline__ void dma16_vaddr(const void* gaddr, uint32_t lds, uint64_t on) {
+  uint64_t sv;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b64 exec, exec, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(sv)
+      : "s"(on), "s"(lds), "v"(gaddr)
+      : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
 
+// The ids of this wave's eight rows of one chunk (read ahead of the loads that use them).
+struct ChunkIds {
+  int4 a, b;       // rows 8w .. 8w+7
+  int32_t rope;    // row 8w + lane/8
+};
+__device__ __forceinline__ ChunkIds chunk_ids(const int32_t* ids, int c, int wv, int lane) {
+  const int32_t* cid = ids + c * KC + 8 * wv;
+  ChunkIds r;
+  r.a = *reinterpret_cast<const int4*>(cid);
+  r.b = *reinterpret_cast<const int4*>(cid + 4);
+  r.rope = cid[lane >> 3];
+  return r;
+}
+// Load number j (0..7: latent half of row 8w + j; 8: the rope parts of rows 8w .. 8w+7)
+// of this wave's share of a chunk into the buffer at LDS address `buf`; `on` = 0 issues
+// nothing (no lanes active).
+__device__ __forceinline__ void gather_load(int j, const ChunkIds& ci, uint32_t buf, const uint16_t* __restrict__ kvb,
+                                            uint32_t n_k, int wv, int lane, uint64_t on) {
+  if (j < 8) {
+    const int32_t id = j == 0 ? ci.a.x : j == 1 ? ci.a.y : j == 2 ? ci.a.z : j == 3 ? ci.a.w
+                     : j == 4 ? ci.b.x : j == 5 ? ci.b.y : j == 6 ? ci.b.z : ci.b.w;
+    const int r = 8 * wv + j;
+    const uint32_t row = safe_row(__builtin_amdgcn_readfirstlane(id), n_k);
+    dma16_saddr(kvb + (size_t)row * MDQK, 16 * (lane ^ lat_swz(r)), buf + r * LAT_PITCH, on);
+  } else {
+    const int r = 8 * wv + (lane >> 3);
+    const uint32_t row = safe_row(ci.rope, n_k);
+    dma16_vaddr(kvb + (size_t)row * MDQK + 512 + 8 * ((lane & 7) ^ rope_swz(r)), buf + LAT_BYTES + wv * 1024, on);
+  }
+}
 __device__ __forceinline__ void gather_chunk(uint32_t buf, const uint16_t* __restrict__ kvb, const int32_t* ids,
                                              int c, uint32_t n_k, int wv, int lane) {
-  const int32_t* cid = ids + c * KC + 8 * wv;
-  // all eight ids first (each DMA statement is a compiler memory barrier)
-  const int4 i0 = *reinterpret_cast<const int4*>(cid);
-  const int4 i1 = *reinterpret_cast<const int4*>(cid + 4);
-  const int32_t idv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-  const uint32_t rope_row = safe_row(cid[lane >> 3], n_k);
+  const ChunkIds ci = chunk_ids(ids, c, wv, lane);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * wv + j;
-    const uint32_t row = safe_row(__builtin_amdgcn_readfirstlane(idv[j]), n_k);
-    dma16_saddr(kvb + (size_t)row * MDQK, 16 * (lane ^ lat_swz(r)), buf + r * LAT_PITCH);
-  }
-  const int r = 8 * wv + (lane >> 3);
-  const uint32_t row = rope_row;
-  dma16_vaddr(kvb + (size_t)row * MDQK + 512 + 8 * ((lane & 7) ^ rope_swz(r)), buf + LAT_BYTES + wv * 1024);
+  for (int j = 0; j < LOADS_PER_CHUNK; ++j) gather_load(j, ci, buf, kvb, n_k, wv, lane, ~0ull);
 }
 
 // A operand of S^T for d-step ds (values 16ds .. 16ds+15): row = key r = l%32, elements
@@ -308,7 +347,9 @@ __device__ __forceinline__ void gather_chunk(uint32_t buf, const uint16_t* __res
 // offsets of those two cases at ds = 0) plus the constant 32ds address every step.  Rope
 // steps (ds >= 32) use `rope`, this lane's offset for that step.
 __device__ __forceinline__ v8bf k_frag(const uint8_t* buf, int off) {
-  return *reinterpret_cast<const v8bf*>(buf + off);
+  typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  return *(lds_v8bf*)((lds_u8*)buf + off);
 }
 __device__ __forceinline__ int rope_offset(int r, int g, int ds) {
   return LAT_BYTES + r * ROPE_PITCH + 16 * ((2 * (ds - 32) + g) ^ rope_swz(r));
@@ -391,6 +432,9 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     const uint16_t* qh = q + (qrow * MH + 32 * wv + (l & 31)) * MDQK + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < D_STEPS; ++ds) Qt[ds] = *reinterpret_cast<const v8bf*>(qh + 16 * ds);
+    // held in registers for the whole row (never re-read from memory)
+#pragma unroll
+    for (int ds = 0; ds < D_STEPS; ++ds) asm volatile("" : "+v"(Qt[ds]));
   }
 
   // the row's selected ids -> LDS; every wave then finds the last valid one, and the
@@ -401,7 +445,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   int last = -1;
   for (int j = l; j < k; j += 64)
     if ((uint32_t)ids[j] < nk) last = j;
-  last = (int)wave_max((float)last);
+  last = __builtin_amdgcn_readfirstlane((int)wave_max((float)last));
   const int nchunks = (last + KC) / KC;
   const int c_lo = (int)((int64_t)nchunks * split / n_split);
   const int c_hi = (int)((int64_t)nchunks * (split + 1) / n_split);
@@ -437,27 +481,35 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
         else VMCNT(0);
         LGKM0();
         block_barrier();
-        if (c + 3 < n) gather_chunk(lds_addr(bufs[(j + 3) % NBUF]), kvb, ids, c_lo + c + 3, nk, wv, l);
+        // chunk c+3's loads go out one every four logit MFMAs (none past the last chunk)
+        const ChunkIds gi = chunk_ids(ids, c_lo + min(c + 3, n - 1), wv, l);
+        // (through a vector register and back, so that it is formed in scalar registers)
+        const uint32_t gon32 = __builtin_amdgcn_readfirstlane(opaque(c + 3 < n ? -1 : 0));
+        const uint64_t gon = ((uint64_t)gon32 << 32) | gon32;
+        const uint32_t gbuf = lds_addr(bufs[(j + 3) % NBUF]);
         // online softmax of chunk c (base 2, lazily rescaled) interleaved with the logits
         // of chunk c+1 (formed from a stale buffer on the last chunk, and then unused):
         // lane holds head l%32 and keys 8(r/4) + 4g + r%4 of S^T
         const uint32_t vmask = (uint32_t)ballot((uint32_t)ids[(c_lo + c) * KC + (l & 31)] < nk);
         if (vmask != 0xFFFFFFFFu) {
+          const uint32_t vm = vmask >> (4 * (opaque(lane_id()) >> 5));  // this lane's keys at bit 8(r/4) + r%4
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (!((vmask >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u)) S_cur[r] = -INFINITY;
+            if (!((vm >> (8 * (r >> 2) + (r & 3))) & 1u)) S_cur[r] = -INFINITY;
         }
         const uint8_t* bn = bufs[(j + 1) % NBUF];
         const KOff ko = k_offsets();
-        v8bf kf[4];
+        v8bf kf[KRING];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kf[i] = k_frag(bn, k_off(ko, i));
+        for (int i = 0; i < KRING; ++i) kf[i] = k_frag(bn, k_off(ko, i));
         v16f S_next = {};
-        // first half of the logits, with the chunk's row max
+        // logits, part 1 (with chunk c's row max)
+        constexpr int PART1 = LOADS_PER_CHUNK + 1;
 #pragma unroll
-        for (int ds = 0; ds < D_STEPS / 2; ++ds) {
-          S_next = mfma_bf16_32x32x16(kf[ds & 3], Qt[ds], S_next);
-          kf[ds & 3] = k_frag(bn, k_off(ko, ds + 4));
+        for (int ds = 0; ds < PART1; ++ds) {
+          S_next = mfma_bf16_32x32x16(kf[ds % KRING], Qt[ds], S_next);
+          kf[ds % KRING] = k_frag(bn, k_off(ko, ds + KRING));
+          if (ds % 4 == 1) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon);
         }
         float mx = fmaxf(fmaxf(S_cur[0], S_cur[1]), S_cur[2]);
 #pragma unroll
@@ -481,14 +533,9 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
           }
           m_ref = m_new;
         }
-        // second half of the logits, with the probabilities.  Before any valid key,
-        // m_ref = -inf and every logit is -inf: offset 0.
+        // chunk c's probabilities (before any valid key, m_ref = -inf and every logit is
+        // -inf: offset 0), then the rest of the logits
         const float m = m_ref == -INFINITY ? 0.f : m_ref;
-#pragma unroll
-        for (int ds = D_STEPS / 2; ds < D_STEPS; ++ds) {
-          S_next = mfma_bf16_32x32x16(kf[ds & 3], Qt[ds], S_next);
-          if (ds + 4 < D_STEPS) kf[ds & 3] = k_frag(bn, k_off(ko, ds + 4));
-        }
         float ps = 0.f;
         uint32_t pk[8];
 #pragma unroll
@@ -502,6 +549,12 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
         l_run += ps;
         const v8bf P0 = __builtin_bit_cast(v8bf, v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
         const v8bf P1 = __builtin_bit_cast(v8bf, v4i{(int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]});
+#pragma unroll
+        for (int ds = PART1; ds < D_STEPS; ++ds) {
+          S_next = mfma_bf16_32x32x16(kf[ds % KRING], Qt[ds], S_next);
+          if (ds + KRING < D_STEPS) kf[ds % KRING] = k_frag(bn, k_off(ko, ds + KRING));
+          if (ds % 4 == 1 && ds / 4 < LOADS_PER_CHUNK) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon);
+        }
         const uint32_t bc = lds_addr(bufs[j]);
         pv_chunk(O, P0, P1, bc + opaque(vt_lane_offset(0)), bc + opaque(vt_lane_offset(1)));
         S_cur = S_next;
