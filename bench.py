@@ -256,6 +256,29 @@ def main():
                 "traffic": recorded_traffic("sparse_mla_bf16_kernel", cfg.name)}
     roof["traffic_unit"] = "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)"
 
+    # the FP8 quantisation of the indexer operands (the step before the indexer; not part
+    # of the metric, which starts from FP8 operands): seeded bf16 activations of the
+    # workload's shape, quantised per query token (all its heads) and per key
+    gq = torch.Generator(device="cuda").manual_seed(0)
+    xq = torch.randn((L, cfg.H_I, cfg.d_I), generator=gq, device="cuda").to(torch.bfloat16)
+    xk = torch.randn((L, cfg.d_I), generator=gq, device="cuda").to(torch.bfloat16)
+    cq = torch.empty_like(xq, dtype=torch.uint8)
+    sq = torch.empty((L, cfg.H_I), dtype=torch.float32, device="cuda")
+    ck = torch.empty_like(xk, dtype=torch.uint8)
+    sk = torch.empty((L, 1), dtype=torch.float32, device="cuda")
+
+    def quant():
+        dsa.fp8_quantize_rows(xq, repeat=cfg.H_I, codes=cq, scale=sq)
+        dsa.fp8_quantize_rows(xk, codes=ck, scale=sk)
+    quant()
+    t_q = time_calls(torch, quant, args.stage_reps)
+    q_bytes = L * (cfg.H_I * cfg.d_I * 3 + cfg.H_I * 4) + L * (cfg.d_I * 3 + 4)
+    stages["quantize"] = {"ms": t_q * 1e3, "bytes": q_bytes, "hbm_frac": q_bytes / t_q / PEAK_HBM,
+                          "note": "bf16 indexer activations -> FP8 codes + fp32 scales (q_I and k_I); "
+                                  "not in the metric"}
+    log(f"[bench] FP8 quantisation of q_I and k_I: {t_q * 1e3:.3f} ms ({q_bytes / t_q / 1e9:.0f} GB/s)")
+    del xq, xk, cq, sq, ck, sk
+
     decode = None
     if args.decode_workload != "none":
         del out, lse, q

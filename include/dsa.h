@@ -201,6 +201,43 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
                        int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
                        size_t ws_bytes, dsa_stream_t stream);
 
+/*
+ * dsa_fp8_quantize_rows -- FP8 E4M3FN quantisation of the indexer operands, the step
+ * before the lightning indexer (the indexer runs in FP8: 53ai.com V3.2-Exp summary,
+ * section 创新架构; juhe.plus explainer, section 第一步：Lightning Indexer).  Per row of
+ * `width` values (a key: d_I values; a query token: its H_I x d_I values):
+ *     scale = amax / 448 in fp32, correctly rounded (1 when the row is all zero);
+ *     code  = the E4M3FN value nearest to x / scale (that quotient in fp32, correctly
+ *             rounded), ties to the even mantissa, saturating at +-448.
+ *
+ *   x      [n_rows, ld_x] input (x_dtype DSA_BF16 or DSA_F32); row r = x + r * ld_x
+ *   codes  [n_rows, ld_codes] uint8 output (the first `width` bytes of each row)
+ *   scale  output: row r's scale is written `repeat` times, at scale[r * scale_stride + j],
+ *          j < repeat (a query token: repeat = H_I, scale_stride = H_I, which fills the
+ *          indexer's q_scale [L, H_I]; a key: repeat = scale_stride = 1)
+ * Buffers are device memory owned by the caller; nothing is allocated.  Invalid shapes
+ * or null pointers return DSA_ERR_INVALID_ARG before anything is enqueued.
+ */
+int dsa_fp8_quantize_rows(const void* x, int32_t x_dtype, int64_t n_rows, int64_t width,
+                          int64_t ld_x, uint8_t* codes, int64_t ld_codes, float* scale,
+                          int64_t scale_stride, int32_t repeat, dsa_stream_t stream);
+
+/*
+ * dsa_kcache_append -- indexer key-cache append for decode and chunked prefill: the
+ * n_new new key rows of each of the B sequences are quantised as by
+ * dsa_fp8_quantize_rows (one scale per key) and written into the FP8 key cache at rows
+ * pos[b] .. pos[b] + n_new - 1 of sequence b.
+ *
+ *   k_new        [B, n_new, d_I] (dtype DSA_BF16 or DSA_F32)
+ *   pos          [B] int32, device: first cache row of each sequence's new keys; rows at
+ *                or past n_k_max (or below 0) are skipped on the device
+ *   k_cache      [B, n_k_max, d_I] uint8, k_cache_scale [B, n_k_max] fp32 (updated in place)
+ * Buffers are device memory owned by the caller; nothing is allocated.
+ */
+int dsa_kcache_append(const void* k_new, int32_t dtype, int64_t B, int64_t n_new, int32_t d_I,
+                      const int32_t* pos, int64_t n_k_max, uint8_t* k_cache,
+                      float* k_cache_scale, dsa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

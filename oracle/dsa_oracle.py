@@ -82,6 +82,54 @@ def dequant(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------
+# step 0: FP8 quantisation of the indexer operands  [P4 "创新架构"; P3 "第一步"; P5 "1.1 DSA"]
+# ----------------------------------------------------------------------------------------
+# The pages say the indexer runs in FP8 and give no quantiser.  Reading: one fp32 scale per
+# row (a key; a query token over all its heads), scale = amax / 448 (1 for an all-zero
+# row), code = the E4M3FN value nearest to x / scale, ties to the even mantissa,
+# saturating at +-448.  Where floating point decides the code, the decision is taken in
+# fp32 as the kernel takes it: scale and x / scale are correctly rounded fp32 divisions.
+
+
+def _e4m3fn_positive_grid() -> tuple:
+    """The finite non-negative E4M3FN values in increasing order, and their codes."""
+    codes = np.array([c for c in range(0x7F)], dtype=np.int64)  # 0x7F is NaN
+    return E4M3FN_TABLE[codes], codes
+
+
+def e4m3fn_encode(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3FN code of each finite value, ties to the even mantissa (even code),
+    saturating at +-448; the sign bit follows the value's sign (so -0.0 -> 0x80)."""
+    v = np.asarray(v, dtype=np.float64)
+    vals, codes = _e4m3fn_positive_grid()
+    a = np.minimum(np.abs(v), vals[-1])
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    mag = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    return mag | (np.signbit(v).astype(np.uint8) << np.uint8(7))
+
+
+def fp8_quantize_row(x: np.ndarray) -> tuple:
+    """One row (any shape, all its values share the scale): (codes uint8, scale fp32)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    scale = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
+    q = x32 / scale  # fp32 division, correctly rounded
+    return e4m3fn_encode(q.astype(np.float64)), np.float32(scale)
+
+
+def fp8_quantize_rows(x: np.ndarray) -> tuple:
+    """Rows along the first axis: (codes of x's shape, scales [n_rows] fp32)."""
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[0], dtype=np.float32)
+    for r in range(x.shape[0]):
+        codes[r], scales[r] = fp8_quantize_row(x[r])
+    return codes, scales
+
+
+# ----------------------------------------------------------------------------------------
 # step 1: lightning indexer  [P3 "第一步"; P4 "创新架构"; P5 "1.1 DSA"]
 # ----------------------------------------------------------------------------------------
 

@@ -256,4 +256,27 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
   return hip_status(dsa::launch_sparse_mla(a, s), "decode sparse attention launch");
 }
 
+int dsa_fp8_quantize_rows(const void* x, int32_t x_dtype, int64_t n_rows, int64_t width, int64_t ld_x,
+                          uint8_t* codes, int64_t ld_codes, float* scale, int64_t scale_stride, int32_t repeat,
+                          dsa_stream_t stream) {
+  REQUIRE(x && codes && scale, "null pointer argument");
+  REQUIRE(x_dtype == DSA_BF16 || x_dtype == DSA_F32, "x_dtype must be DSA_BF16 or DSA_F32 (got %d)", x_dtype);
+  REQUIRE(n_rows > 0 && width > 0, "n_rows and width must be positive");
+  REQUIRE(n_rows <= (int64_t)4 * 2147483647, "n_rows too large");
+  REQUIRE(ld_x >= width && ld_codes >= width, "row strides must be >= width");
+  REQUIRE(repeat >= 1 && scale_stride >= repeat, "need 1 <= repeat <= scale_stride");
+  dsa::QuantArgs a{x, x_dtype, 1, n_rows, width, ld_x, nullptr, n_rows, codes, ld_codes, scale, scale_stride, repeat};
+  return hip_status(dsa::launch_fp8_quant_rows(a, (hipStream_t)stream), "fp8 quantiser launch");
+}
+
+int dsa_kcache_append(const void* k_new, int32_t dtype, int64_t B, int64_t n_new, int32_t d_I, const int32_t* pos,
+                      int64_t n_k_max, uint8_t* k_cache, float* k_cache_scale, dsa_stream_t stream) {
+  REQUIRE(k_new && pos && k_cache && k_cache_scale, "null pointer argument");
+  REQUIRE(dtype == DSA_BF16 || dtype == DSA_F32, "dtype must be DSA_BF16 or DSA_F32 (got %d)", dtype);
+  REQUIRE(B > 0 && B <= 65535 && n_new > 0 && d_I > 0 && n_k_max > 0, "B in [1, 65535], n_new, d_I, n_k_max > 0");
+  REQUIRE(n_new <= (int64_t)4 * 2147483647, "n_new too large");
+  dsa::QuantArgs a{k_new, dtype, B, n_new, d_I, d_I, pos, n_k_max, k_cache, d_I, k_cache_scale, 1, 1};
+  return hip_status(dsa::launch_fp8_quant_rows(a, (hipStream_t)stream), "key-cache append launch");
+}
+
 }  // extern "C"

@@ -68,4 +68,22 @@ struct PrefillTopkArgs {
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 
+// FP8 E4M3FN row quantiser: rows of `groups` groups; group b's row i (source row
+// b * n_per + i, ld_x elements apart) goes to destination row b * dst_per + base + i,
+// base = pos ? pos[b] : 0 (rows outside [0, dst_per) skipped); its scale is written
+// `repeat` times at scale[dst_row * scale_stride + r].
+struct QuantArgs {
+  const void* x;
+  int32_t dtype;  // DSA_BF16 or DSA_F32
+  int64_t groups, n_per, width, ld_x;
+  const int32_t* pos;
+  int64_t dst_per;
+  uint8_t* codes;
+  int64_t ld_codes;
+  float* scale;
+  int64_t scale_stride;
+  int32_t repeat;
+};
+hipError_t launch_fp8_quant_rows(const QuantArgs& a, hipStream_t st);
+
 }  // namespace dsa

@@ -40,6 +40,8 @@ _SIGNATURES = {
     "dsa_forward_decode": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                           _vp, _vp, _vp, _sz, _vp]),
+    "dsa_fp8_quantize_rows": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
+    "dsa_kcache_append": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -209,3 +211,36 @@ def forward_decode(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cac
                                     _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
+
+
+def _x_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"quantiser input must be bfloat16 or float32, got {t.dtype}")
+
+
+def fp8_quantize_rows(x, repeat: int = 1, codes=None, scale=None):
+    """Per-row FP8 E4M3FN quantisation of a [n_rows, ...] tensor (each row flattened):
+    returns (codes uint8 of x's shape, scale fp32 [n_rows, repeat]); the row's scale is
+    written `repeat` times (a query token's scale for each of its H_I heads)."""
+    assert x.is_cuda and x.is_contiguous()
+    n_rows = x.shape[0]
+    width = x.numel() // n_rows
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((n_rows, repeat), dtype=torch.float32, device=x.device)
+    _check(lib().dsa_fp8_quantize_rows(_ptr(x), _x_dtype(x), n_rows, width, width, _ptr(codes), width,
+                                       _ptr(scale), repeat, repeat, _stream()))
+    return codes, scale
+
+
+def kcache_append(k_new, pos, k_cache, k_cache_scale):
+    """Quantise k_new [B, n_new, d_I] into k_cache [B, n_k_max, d_I] / k_cache_scale
+    [B, n_k_max] at rows pos[b] .. pos[b] + n_new - 1 (in place)."""
+    assert k_new.is_cuda and k_new.is_contiguous() and k_cache.is_contiguous() and k_cache_scale.is_contiguous()
+    B, n_new, d_I = k_new.shape
+    _check(lib().dsa_kcache_append(_ptr(k_new), _x_dtype(k_new), B, n_new, d_I, _ptr(pos), k_cache.shape[1],
+                                   _ptr(k_cache), _ptr(k_cache_scale), _stream()))

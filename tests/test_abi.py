@@ -27,7 +27,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 10
+    assert len(syms) == 12
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(dsa._SIGNATURES)
@@ -118,3 +118,24 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         dsa._ptr(torch.zeros(4))
+
+
+def test_quantiser_validation(L):
+    order = [("x", FAKE), ("dt", dsa.DSA_BF16), ("n", 4), ("w", 128), ("ldx", 128), ("c", FAKE),
+             ("ldc", 128), ("s", FAKE), ("ss", 1), ("rep", 1), ("st", None)]
+    call = lambda **kw: L.dsa_fp8_quantize_rows(*[kw.get(n, d) for n, d in order])
+    assert call(x=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(dt=dsa.DSA_FP8_E4M3) == dsa.DSA_ERR_INVALID_ARG
+    assert call(n=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldx=127) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldc=100) == dsa.DSA_ERR_INVALID_ARG
+    assert call(rep=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(rep=4, ss=2) == dsa.DSA_ERR_INVALID_ARG
+    order = [("k", FAKE), ("dt", dsa.DSA_BF16), ("B", 2), ("n", 3), ("d", 128), ("pos", FAKE),
+             ("nmax", 64), ("c", FAKE), ("s", FAKE), ("st", None)]
+    call = lambda **kw: L.dsa_kcache_append(*[kw.get(n, d) for n, d in order])
+    assert call(pos=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(B=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(B=70000) == dsa.DSA_ERR_INVALID_ARG
+    assert call(nmax=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(dt=dsa.DSA_F32 + 7) == dsa.DSA_ERR_INVALID_ARG

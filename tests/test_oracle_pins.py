@@ -330,3 +330,61 @@ def test_generator_planted_structure():
     assert abs((qn @ kn.T).mean() - 0.5) < 0.05
     other = np.nonzero(owner == -1)[0]
     assert abs((qn @ (kk["kv"][other] / np.linalg.norm(kk["kv"][other], axis=-1, keepdims=True)).T).mean()) < 0.02
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 row quantiser (the step before the indexer)
+# ---------------------------------------------------------------------------------------
+
+def test_e4m3fn_encode_matches_torch_on_every_midpoint_and_value():
+    """The oracle's encoder against torch's float32 -> float8_e4m3fn conversion (a library
+    routine, round-to-nearest-even) on every representable value, every midpoint between
+    neighbours (where ties to even decide) and the points just beside each midpoint."""
+    vals = np.array(sorted(set(O.E4M3FN_TABLE[:0x7F].tolist())), dtype=np.float64)
+    mids = (vals[1:] + vals[:-1]) / 2
+    pts = np.concatenate([vals, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                          np.nextafter(mids.astype(np.float32), np.float32(1000))]).astype(np.float32)
+    pts = np.concatenate([pts, -pts])
+    mine = O.e4m3fn_encode(pts.astype(np.float64))
+    ref = torch.from_numpy(pts).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def test_e4m3fn_encode_saturates_and_signs():
+    assert O.e4m3fn_encode(np.array([448.0, 464.0, 1e6, -1e6]))[:].tolist() == [0x7E, 0x7E, 0x7E, 0xFE]
+    assert O.e4m3fn_encode(np.array([-0.0, 0.0])).tolist() == [0x80, 0x00]
+    # smallest subnormal 2^-9; half of it is a tie that rounds to even (0)
+    assert O.e4m3fn_encode(np.array([2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10])).tolist() == [0x01, 0x00, 0x02]
+
+
+def test_fp8_quantize_row_worked_example():
+    """By hand from the E4M3FN definition: amax 448 gives scale 1; 224 = 1.75 * 2^7 is
+    exponent field 14, mantissa 6 (0x76); 1 = exponent field 7 (0x38); -0.5 = exponent
+    field 6 with the sign (0xB0); 3.3 lies between 3.25 and 3.5 and rounds to 3.25
+    (exponent field 8, mantissa 5: 0x45)."""
+    codes, scale = O.fp8_quantize_row(np.array([448.0, 224.0, 1.0, -0.5, 3.3], dtype=np.float32))
+    assert scale == np.float32(1.0)
+    assert codes.tolist() == [0x7E, 0x76, 0x38, 0xB0, 0x45]
+    # an all-zero row: scale 1, codes 0
+    codes, scale = O.fp8_quantize_row(np.zeros(16, dtype=np.float32))
+    assert scale == np.float32(1.0) and not codes.any()
+
+
+def test_fp8_quantize_rows_invariants():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((64, 128)) * np.exp(rng.uniform(-20, 20, (64, 1)))).astype(np.float32)
+    codes, scales = O.fp8_quantize_rows(x)
+    back = O.fp8_to_f64(codes) * scales[:, None].astype(np.float64)
+    for r in range(64):
+        amax = np.abs(x[r]).max()
+        assert scales[r] == np.float32(amax) / np.float32(448.0)
+        # the largest magnitude maps to +-448
+        j = int(np.argmax(np.abs(x[r])))
+        assert codes[r, j] & 0x7F == 0x7E
+        # every value is within half a quantum (3 mantissa bits: 2^-4 relative, or the
+        # subnormal quantum 2^-9 * scale) of its reconstruction
+        tol = np.maximum(np.abs(x[r]) * 2.0 ** -4, 2.0 ** -10 * scales[r]) * (1 + 1e-6)
+        assert np.all(np.abs(back[r] - x[r]) <= tol)
+    # scaling a row by a power of two leaves its codes unchanged and scales its scale
+    c2, s2 = O.fp8_quantize_rows(x * np.float32(8.0))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales * np.float32(8.0))
