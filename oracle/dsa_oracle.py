@@ -173,9 +173,10 @@ def topk_row(scores: np.ndarray, pos: int, k: int) -> np.ndarray:
     """Top-k of keys 0..pos by (score descending, key index ascending), as int32 [k].
 
     The kept indices are emitted in ascending order and padded with -1.  A full sort is
-    the definition; -0.0 and +0.0 compare equal, as floats do.
+    the definition; -0.0 and +0.0 compare equal, as floats do.  A query at a negative
+    position has no key before it and keeps nothing.
     """
-    n = min(pos + 1, scores.shape[0])
+    n = max(0, min(pos + 1, scores.shape[0]))
     s = np.arange(n)
     order = np.lexsort((s, -np.asarray(scores[:n], dtype=np.float64)))   # primary: -score
     keep = np.sort(order[: min(k, n)])
@@ -190,7 +191,7 @@ def topk(scores: np.ndarray, pos: np.ndarray, k: int) -> np.ndarray:
 
 def topk_row_bruteforce(scores, pos: int, k: int) -> list:
     """Pure-Python version of ``topk_row`` for tiny inputs (pins the numpy sort)."""
-    n = min(pos + 1, len(scores))
+    n = max(0, min(pos + 1, len(scores)))
     ranked = sorted(range(n), key=lambda s: (-float(scores[s]), s))
     keep = sorted(ranked[: min(k, n)])
     return keep + [-1] * (k - len(keep))

@@ -212,6 +212,26 @@ def test_topk_bruteforce_with_ties():
         _check_certificate(levels, pos, k, np.array(a))
 
 
+def test_topk_positions_outside_the_keys():
+    """A query before the first key (negative position) sees nothing; one at or past the
+    last key sees every key (causal visibility s <= t over the keys that exist)."""
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal(30)
+    for pos in (-1, -5, -31):
+        assert O.topk_row(s, pos, 8).tolist() == [-1] * 8 == O.topk_row_bruteforce(s, pos, 8)
+    for pos in (29, 30, 100):
+        want = sorted(np.argsort(-s, kind="stable")[:8].tolist())
+        assert O.topk_row(s, pos, 8).tolist() == want == O.topk_row_bruteforce(s, pos, 8)[:8]
+    assert O.topk_row(s, 50, 40).tolist() == list(range(30)) + [-1] * 10
+    # the dense indexer leaves a negative-position row at -inf and caps a late one at the keys
+    qhat = rng.standard_normal((2, 3, 4))
+    w = rng.standard_normal((2, 3))
+    khat = rng.standard_normal((6, 4))
+    I = O.indexer(qhat, w, khat, np.array([-3, 9]))
+    assert np.all(I[0] == -np.inf) and np.all(np.isfinite(I[1]))
+    assert np.array_equal(I[1], O.indexer_row(qhat[1], w[1], khat, 5))
+
+
 def test_topk_signed_zero_equal():
     s = np.array([0.0, -0.0, 0.0, -0.0])
     assert O.topk_row(s, 3, 2).tolist() == [0, 1]
