@@ -191,6 +191,7 @@ def main():
     ap.add_argument("--decode-workload", default="decode_64x128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=8192, help="tokens of the chunked-prefill stage")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the DSA layer on a single MI355X "
@@ -278,6 +279,29 @@ def main():
                                   "not in the metric"}
     log(f"[bench] FP8 quantisation of q_I and k_I: {t_q * 1e3:.3f} ms ({q_bytes / t_q / 1e9:.0f} GB/s)")
     del xq, xk, cq, sq, ck, sk
+
+    # chunked prefill: the sequence's last CHUNK tokens as one chunk against the cache that
+    # holds all L rows (the most expensive chunk: its rows see the most keys)
+    C = min(args.chunk, L)
+    p0 = L - C
+    pos_c = torch.tensor([p0], dtype=torch.int32, device="cuda")
+    cidx = torch.empty((1, C, k), dtype=torch.int32, device="cuda")
+    cout = torch.empty((1, C, cfg.H, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    clse = torch.empty((1, C, cfg.H), dtype=torch.float32, device="cuda")
+    ws_c_n = dsa.workspace_size(dsa.DSA_OP_CHUNK, 1, C, L, cfg.H, cfg.d_v, k, dsa.DSA_BF16)
+    ws_c = torch.empty(ws_c_n, dtype=torch.uint8, device="cuda") if ws_c_n else None
+
+    def chunk():
+        dsa.forward_chunk(pos_c, qi[None, p0:], qs[None, p0:], w[None, p0:], ki[None], ks[None], q[None, p0:],
+                          kv[None], k, cfg.sm_scale, cfg.d_v, idx=cidx, out=cout, lse=clse, ws=ws_c)
+    chunk()
+    t_c = time_calls(torch, chunk, args.stage_reps)
+    f_c = indexer_flops(L, cfg.H_I, cfg.d_I) - indexer_flops(p0, cfg.H_I, cfg.d_I)
+    stages["chunk"] = {"ms": t_c * 1e3, "tokens": C, "q_pos": p0, "n_k": L, "tokens_per_s": C / t_c,
+                       "indexer_fp8_flop": f_c, "indexer_mfma_frac_of_step": f_c / t_c / PEAK_FP8,
+                       "note": "the last chunk of the sequence through dsa_forward_chunk"}
+    log(f"[bench] chunk of {C} tokens at q_pos {p0}: {t_c * 1e3:.3f} ms ({C / t_c:.0f} tokens/s)")
+    del cidx, cout, clse, ws_c
 
     decode = None
     if args.decode_workload != "none":

@@ -73,7 +73,7 @@ enum dsa_status {
 enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 };
 
 enum dsa_op { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2,
-              DSA_OP_PREFILL = 3, DSA_OP_DECODE = 4, DSA_OP_SELECT = 5 };
+              DSA_OP_PREFILL = 3, DSA_OP_DECODE = 4, DSA_OP_SELECT = 5, DSA_OP_CHUNK = 6 };
 
 /* DSA_ABI_VERSION of the loaded library. */
 int dsa_abi_version(void);
@@ -87,8 +87,9 @@ const char* dsa_last_error(void);
 /*
  * Workspace bytes an entry point needs (0 if none).  op is a dsa_op; the other
  * arguments are the ones the entry point takes (unused ones may be 0).  For
- * DSA_OP_PREFILL pass the attention dtype (DSA_F32 selects the fp32 path, whose
- * selection ranks materialised scores); for DSA_OP_SELECT pass the indexer dtype.
+ * DSA_OP_PREFILL and DSA_OP_CHUNK pass the attention dtype (DSA_F32 selects the fp32
+ * path, whose selection ranks materialised scores); for DSA_OP_SELECT pass the indexer
+ * dtype.
  */
 size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32_t H,
                           int32_t d_v, int32_t k, int32_t dtype);
@@ -200,6 +201,42 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
                        int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype,
                        int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
                        size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_forward_chunk -- the whole layer for a chunk of n_q new tokens in each of B
+ * sequences (chunked prefill; multi-token decode): the chunk's queries attend to the
+ * sequence's cached rows, which already hold the chunk's own rows (dsa_kcache_append
+ * writes the indexer keys).  The decode path is the n_q = 1 case; dsa_forward_prefill
+ * is B = 1, q_pos = 0, n_q = n_k_max.  DSA lowers the per-token cost of both the
+ * prefill and the decode stage (yunpan.plus article, section 1.1 DSA, and its
+ * inference-cost figure); each query keeps its own top-k of the keys before it (juhe.plus
+ * explainer, section 第二步：Fine-grained Token Selection).
+ *
+ * Row i of sequence b is the query at position p = q_pos[b] + i (q_pos: [B] int32,
+ * device).  It sees cached rows 0 .. min(p, n_k_max - 1); a row with p < 0 sees none
+ * (idx all -1, out 0, lse -inf).  Rows whose position leaves at most k visible keys keep
+ * all of them.
+ *
+ *   q_idx [B, n_q, H_I, d_I], q_scale [B, n_q, H_I], w [B, n_q, H_I]
+ *   k_cache [B, n_k_max, d_I], k_cache_scale [B, n_k_max]
+ *   q [B, n_q, H, d_qk], kv_cache [B, n_k_max, d_qk], v_cache [B, n_k_max, d_v] or NULL
+ *   idx [B, n_q, k] int32 (output: S_t ascending, -1 padded), out [B, n_q, H, d_v],
+ *   lse [B, n_q, H] or NULL
+ * idx_dtype / attn_dtype: DSA_FP8_E4M3 with DSA_BF16 (the indexer and the streaming
+ * top-k fused on chip: no score matrix, k <= 2048, n_k_max < 2^25), or DSA_F32 with
+ * DSA_F32 (materialised scores in the workspace, n_q <= 65535).  Selection and
+ * attention of a row do not depend on the other rows of the call: a prefill cut into
+ * chunks returns what the one-shot prefill returns, bit for bit.
+ * Workspace: dsa_workspace_size(DSA_OP_CHUNK, B, n_q, n_k_max, H, d_v, k, attn_dtype).
+ * Buffers are device memory owned by the caller.
+ */
+int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max,
+                      const void* q_idx, const float* q_scale, const float* w,
+                      const void* k_cache, const float* k_cache_scale, const void* q,
+                      const void* kv_cache, const void* v_cache, int32_t H_I, int32_t d_I,
+                      int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
+                      int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out,
+                      float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * dsa_fp8_quantize_rows -- FP8 E4M3FN quantisation of the indexer operands, the step

@@ -68,6 +68,14 @@ size_t decode_scores_bytes(int64_t B, int64_t n_k) { return (size_t)B * n_k * si
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// the fp32 chunk path ranks materialised scores; the FP8 path selects on chip
+size_t chunk_scores_bytes(int64_t B, int64_t n_q, int64_t n_k, int32_t attn_dtype) {
+  return attn_dtype == DSA_F32 ? align256((size_t)B * n_q * n_k * sizeof(float)) : 0;
+}
+
+// largest key count of the fused selection (32-bit byte offsets within a sequence's keys)
+constexpr int64_t FUSED_MAX_KEYS = ((int64_t)1 << 25) - 1;
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +109,8 @@ size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32
       return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : 0;
     case DSA_OP_DECODE:
       return align256(decode_scores_bytes(B, n_k)) + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
+    case DSA_OP_CHUNK:
+      return chunk_scores_bytes(B, n_q, n_k, dtype) + dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, dtype);
     default:
       return 0;
   }
@@ -162,7 +172,8 @@ static int select_prefill(const void* q_idx, const float* q_scale, const void* k
                           int32_t* idx, void* ws, size_t ws_bytes, hipStream_t s) {
   if (idx_dtype == DSA_FP8_E4M3) {
     SUPPORT(k <= 2048, "fused selection keeps at most 2048 keys (k = %d)", k);
-    dsa::PrefillTopkArgs pa{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, L, k, idx};
+    dsa::PrefillTopkArgs pa{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, 1, L, L,
+                            nullptr, k, idx};
     return hip_status(dsa::launch_prefill_topk(pa, s), "prefill indexer/top-k launch");
   }
   SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
@@ -277,6 +288,56 @@ int dsa_kcache_append(const void* k_new, int32_t dtype, int64_t B, int64_t n_new
   REQUIRE(n_new <= (int64_t)4 * 2147483647, "n_new too large");
   dsa::QuantArgs a{k_new, dtype, B, n_new, d_I, d_I, pos, n_k_max, k_cache, d_I, k_cache_scale, 1, 1};
   return hip_status(dsa::launch_fp8_quant_rows(a, (hipStream_t)stream), "key-cache append launch");
+}
+
+int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max, const void* q_idx,
+                      const float* q_scale, const float* w, const void* k_cache, const float* k_cache_scale,
+                      const void* q, const void* kv_cache, const void* v_cache, int32_t H_I, int32_t d_I, int32_t H,
+                      int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype,
+                      int32_t* idx, void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(q_pos && q_idx && q_scale && w && k_cache && k_cache_scale && q && kv_cache && idx && out,
+          "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k_max > 0, "B in [1, 65535], n_q > 0 and n_k_max > 0 required");
+  REQUIRE(n_q <= 2147483647LL && n_q * H <= 2147483647LL, "n_q too large");
+  int st = check_indexer_shape(H_I, d_I, idx_dtype);
+  if (st) return st;
+  st = check_attn_shape(H, d_qk, d_v, k, attn_dtype, v_cache != nullptr);
+  if (st) return st;
+  SUPPORT(idx_dtype == attn_dtype || (idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16),
+          "a chunk pairs an FP8 indexer with bf16 attention, or fp32 with fp32");
+  if (idx_dtype == DSA_FP8_E4M3) {
+    REQUIRE(aligned16(q_idx) && aligned16(k_cache), "FP8 operands must be 16-byte aligned");
+    SUPPORT(k <= 2048, "fused selection keeps at most 2048 keys (k = %d)", k);
+    SUPPORT(n_k_max <= FUSED_MAX_KEYS, "fused selection supports n_k_max <= %lld", (long long)FUSED_MAX_KEYS);
+    REQUIRE(B * ((n_q + 3) / 4) <= 2147483647LL, "B * n_q too large");
+  } else {
+    SUPPORT(n_k_max <= dsa::TOPK_MAX_N, "fp32 chunk supports n_k_max <= %lld", (long long)dsa::TOPK_MAX_N);
+    SUPPORT(n_q <= 65535, "fp32 chunk supports n_q <= 65535");
+  }
+  if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv_cache) && aligned16(out), "bf16 operands must be 16-byte aligned");
+  const size_t s_bytes = chunk_scores_bytes(B, n_q, n_k_max, attn_dtype);
+  const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, attn_dtype);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_forward_chunk needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  if (need) REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (idx_dtype == DSA_FP8_E4M3) {
+    dsa::PrefillTopkArgs pa{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_cache, k_cache_scale, w,
+                            B, n_q, n_k_max, q_pos, k, idx};
+    st = hip_status(dsa::launch_prefill_topk(pa, s), "chunk indexer/top-k launch");
+  } else {
+    float* scores = (float*)ws;
+    dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, n_q, n_k_max, q_pos, 0, H_I, d_I,
+                        idx_dtype, 0, n_q, scores, n_k_max};
+    st = hip_status(dsa::launch_indexer(ia, s), "chunk indexer launch");
+    if (st) return st;
+    dsa::TopkArgs ta{scores, n_k_max, B, n_q, n_k_max, q_pos, 0, 0, k, idx};
+    st = hip_status(dsa::launch_topk(ta, s), "chunk top-k launch");
+  }
+  if (st) return st;
+  dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, n_q, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
+                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes};
+  return hip_status(dsa::launch_sparse_mla(a, s), "chunk sparse attention launch");
 }
 
 }  // extern "C"

@@ -55,14 +55,17 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 size_t sparse_mla_ws_bytes(int64_t B, int64_t n_q, int32_t H, int32_t d_v, int32_t k, int32_t dtype);
 int sparse_mla_splits(int64_t B, int64_t n_q, int32_t k, int32_t dtype);
 
-// fused FP8 indexer + streaming top-k for the prefill rows of one sequence (q_pos = 0)
+// fused FP8 indexer + streaming top-k: n_q query rows of each of B sequences against
+// that sequence's n_k key rows; row r of sequence b sits at position q_pos[b] + r
+// (q_pos null: r) and sees keys 0 .. min(position, n_k - 1).  Needs n_k * 128 < 2^32.
 struct PrefillTopkArgs {
   const uint8_t* q8;
   const float* qs;
   const uint8_t* k8;
   const float* ks;
   const float* w;
-  int64_t L;
+  int64_t B, n_q, n_k;
+  const int32_t* q_pos;
   int32_t k;
   int32_t* idx;
 };

@@ -339,12 +339,13 @@ __device__ __forceinline__ void owner_reads(int slot, int r, const float* ks0, c
       : "memory");
 }
 
-// Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer.
-__device__ __forceinline__ void owner_append(OwnerState& S, int r, float s, int key0, int row) {
+// Append the owner's 64 new scores (keys key0 + lane) to its candidate buffer; keys past
+// `lim` (the last key the row sees) are not taken.
+__device__ __forceinline__ void owner_append(OwnerState& S, int r, float s, int key0, int lim) {
   const int lane = lane_id();
   const int key = key0 + lane;
   const uint32_t u = score_key(s);
-  const bool pass = key <= row && u > S.thr;
+  const bool pass = key <= lim && u > S.thr;
   const uint64_t m = ballot(pass);
   if (m) {
     if (pass) {
@@ -379,10 +380,27 @@ __device__ __forceinline__ void owner_maybe_cut(OwnerState& S, int r, int k, int
   }
 }
 
+// Group G of the persistent loop: sequence b = G % B (consecutive blocks, hence each XCD's
+// blocks, stay on few sequences), rows row_hi - 4 .. row_hi - 1 of it, longest first.
+// Row r sits at position pos0 + r and sees keys 0 .. min(pos0 + r, n_k - 1); n_keys is what
+// the group's last row sees (0 if its position is negative).
+struct GroupGeom {
+  int b, row_hi, pos0, n_keys;
+};
+__device__ __forceinline__ GroupGeom group_geom(int G, int B, int n_q, int n_k, const int32_t* __restrict__ q_pos) {
+  GroupGeom g;
+  g.b = G % B;
+  g.row_hi = n_q - 4 * (G / B);
+  g.pos0 = q_pos ? q_pos[g.b] : 0;
+  const int64_t last = (int64_t)g.pos0 + g.row_hi;  // last row's position + 1
+  g.n_keys = (int)(last < 0 ? 0 : last > n_k ? n_k : last);
+  return g;
+}
+
 __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
-    const float* __restrict__ ks, const float* __restrict__ w, int L, int row_lo, int k,
-    int n_groups, int32_t* __restrict__ idx) {
+    const float* __restrict__ ks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int B,
+    int n_q, int n_k, int row_lo, int k, int n_groups, int32_t* __restrict__ idx) {
   // ring of three tile pairs (pair p = tiles 2p, 2p+1) and their key scales
   __shared__ __align__(16) uint8_t tk0[TILE_BYTES];
   __shared__ __align__(16) uint8_t tk1[TILE_BYTES];
@@ -406,22 +424,27 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const int f = wv >> 1, hh = wv & 1;
     const TileDma dl = tile_dma_lane(wv, lane);
     for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
-      const int row_hi = L - 4 * G;  // rows row_hi-4 .. row_hi-1
-      const int row0 = row_hi - 4;
+      const GroupGeom g = group_geom(G, B, n_q, n_k, q_pos);
+      if (g.n_keys <= k) continue;  // every row keeps all it sees: the owners write it
+      const int row0 = g.row_hi - 4;
+      const size_t rbase = (size_t)g.b * n_q;
+      const uint8_t* kb = k8 + (size_t)g.b * n_k * IDX_DIM;
+      const float* ksb = ks + (size_t)g.b * n_k;
       IdxHalf Qh[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = max(row0 + j, row_lo);  // rows below row_lo are not this kernel's: score a valid row
-        const float cmax = row_cmax(qs + (size_t)r * IDX_HEADS, w + (size_t)r * IDX_HEADS);
-        load_idx_half(Qh[j], q8 + (size_t)r * IDX_HEADS * IDX_DIM, qs + (size_t)r * IDX_HEADS,
-                      w + (size_t)r * IDX_HEADS, hh, cmax);
+        // rows below row_lo are not this kernel's: score a valid row
+        const size_t r = rbase + max(row0 + j, row_lo);
+        const float cmax = row_cmax(qs + r * IDX_HEADS, w + r * IDX_HEADS);
+        load_idx_half(Qh[j], q8 + r * IDX_HEADS * IDX_DIM, qs + r * IDX_HEADS, w + r * IDX_HEADS, hh, cmax);
       }
-      const int nsteps = (row_hi + STEP_KEYS - 1) / STEP_KEYS;
-      // (a step's second tile may lie past L: its loads clamp to row L-1, and the owners
-      // never take a key past their row)
+      const int L = g.n_keys;
+      const int nsteps = (L + STEP_KEYS - 1) / STEP_KEYS;
+      // (a step's second tile may lie past key L-1: its loads clamp to key L-1, and the
+      // owners never take a key past their row's position)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (j < 2 * nsteps) dma_key_tile(tks[j], tss[j], k8, ks, j * KEY_TILE, L, dl, wv, lane);
+        if (j < 2 * nsteps) dma_key_tile(tks[j], tss[j], kb, ksb, j * KEY_TILE, L, dl, wv, lane);
 
       for (int base = 0; base <= nsteps; base += 3) {
 #pragma unroll
@@ -434,8 +457,8 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
             if (st < nsteps) {
               if (st + 2 < nsteps) {  // into the pair of step st-1, which every wave is done with
                 const int q = (pp + 2) % 3;
-                dma_key_tile(tks[2 * q], tss[2 * q], k8, ks, (2 * st + 4) * KEY_TILE, L, dl, wv, lane);
-                dma_key_tile(tks[2 * q + 1], tss[2 * q + 1], k8, ks, (2 * st + 5) * KEY_TILE, L, dl, wv, lane);
+                dma_key_tile(tks[2 * q], tss[2 * q], kb, ksb, (2 * st + 4) * KEY_TILE, L, dl, wv, lane);
+                dma_key_tile(tks[2 * q + 1], tss[2 * q + 1], kb, ksb, (2 * st + 5) * KEY_TILE, L, dl, wv, lane);
               }
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
@@ -465,13 +488,22 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     // ---------------- owner waves ----------------
     const int r = wv - PF_SCORE_WAVES;
     for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
-      const int row_hi = L - 4 * G;
-      const int my_row = row_hi - 4 + r;
+      const GroupGeom g = group_geom(G, B, n_q, n_k, q_pos);
+      const int my_row = g.row_hi - 4 + r;
       const bool valid = my_row >= row_lo;
-      const int rq = max(my_row, row_lo);
-      OwnerState S{0, 0u, 0u, 0u, row_cmax(qs + (size_t)rq * IDX_HEADS, w + (size_t)rq * IDX_HEADS)};
+      // last key this row sees (-1: none)
+      const int64_t lim64 = min((int64_t)g.pos0 + my_row, (int64_t)n_k - 1);
+      const int lim = (int)(lim64 < -1 ? -1 : lim64);
+      int32_t* out = idx + ((size_t)g.b * n_q + max(my_row, 0)) * k;
+      if (g.n_keys <= k) {  // no row sees more than k keys: keep them all
+        if (valid)
+          for (int j = lane; j < k; j += WAVE) out[j] = j <= lim ? j : -1;
+        continue;
+      }
+      const size_t rq = (size_t)g.b * n_q + max(my_row, row_lo);
+      OwnerState S{0, 0u, 0u, 0u, row_cmax(qs + rq * IDX_HEADS, w + rq * IDX_HEADS)};
       if (lane == 0) lds_store(&s_cnt[r], __int_as_float(0));
-      const int nsteps = (row_hi + STEP_KEYS - 1) / STEP_KEYS;
+      const int nsteps = (g.n_keys + STEP_KEYS - 1) / STEP_KEYS;
       float ksc[2] = {0.f, 0.f};  // key scales of the step not yet taken
       for (int base = 0; base <= nsteps; base += 3) {
 #pragma unroll
@@ -486,8 +518,8 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
             owner_reads((st - 1) & 1, r, tss[2 * pp], tss[2 * pp + 1], x, ksn, c);
             if (st >= 1 && valid) {
               const int key0 = (st - 1) * STEP_KEYS;
-              owner_append(S, r, finish_score(x[0], x[1], S.cmax, ksc[0]), key0, my_row);
-              owner_append(S, r, finish_score(x[2], x[3], S.cmax, ksc[1]), key0 + KEY_TILE, my_row);
+              owner_append(S, r, finish_score(x[0], x[1], S.cmax, ksc[0]), key0, lim);
+              owner_append(S, r, finish_score(x[2], x[3], S.cmax, ksc[1]), key0 + KEY_TILE, lim);
               owner_maybe_cut(S, r, k, max(max(c[0], c[1]), max(c[2], c[3])));
               if (lane == 0) lds_store(&s_cnt[r], __int_as_float(S.cnt));
             }
@@ -505,26 +537,35 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
           select_compact(r, S.cnt, k);
           S.cnt = k;
         }
-        int32_t* out = idx + (size_t)my_row * k;
         for (int j = lane; j < k; j += WAVE) out[j] = j < S.cnt ? s_cidx[r][j] : -1;
       }
     }
   }
 }
 
-// rows [0, n) keep every visible key: idx[t] = 0..t, -1 padded
-__global__ __launch_bounds__(256) void prefill_fill_kernel(int64_t n, int k, int32_t* __restrict__ idx) {
+// rows [0, n) of each sequence (row t at position t) keep every key they see:
+// idx[b][t] = 0 .. min(t, n_k - 1), -1 padded
+__global__ __launch_bounds__(256) void prefill_fill_kernel(int64_t n, int64_t n_q, int64_t n_k, int k,
+                                                           int32_t* __restrict__ idx) {
   const int64_t t = blockIdx.x;
   if (t >= n) return;
-  int32_t* out = idx + t * (int64_t)k;
-  for (int j = threadIdx.x; j < k; j += 256) out[j] = j <= t ? j : -1;
+  const int64_t lim = t < n_k - 1 ? t : n_k - 1;
+  int32_t* out = idx + ((int64_t)blockIdx.y * n_q + t) * k;
+  for (int j = threadIdx.x; j < k; j += 256) out[j] = j <= lim ? j : -1;
 }
 
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
-  const int64_t row_lo = a.k < a.L ? a.k : a.L;
-  if (row_lo > 0)
-    hipLaunchKernelGGL(prefill_fill_kernel, dim3((unsigned)row_lo), dim3(256), 0, st, row_lo, a.k, a.idx);
-  const int64_t n_rows = a.L - row_lo;
+  // Without q_pos, row t sits at position t: rows below k keep every key they see and are
+  // written by the fill kernel.  With q_pos the positions live on the device, and groups
+  // whose rows see at most k keys are written by the fused kernel's owners.
+  int64_t row_lo = 0;
+  if (!a.q_pos) {
+    row_lo = a.k < a.n_q ? a.k : a.n_q;
+    if (row_lo > 0)
+      hipLaunchKernelGGL(prefill_fill_kernel, dim3((unsigned)row_lo, (unsigned)a.B), dim3(256), 0, st, row_lo,
+                         a.n_q, a.n_k, a.k, a.idx);
+  }
+  const int64_t n_rows = a.n_q - row_lo;
   if (n_rows > 0) {
     static int n_cu = 0;
     if (n_cu == 0) {
@@ -533,10 +574,11 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
           hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
         n_cu = 256;
     }
-    const int64_t n_groups = (n_rows + 3) / 4;
+    const int64_t n_groups = a.B * ((n_rows + 3) / 4);
     const int64_t blocks = n_groups < n_cu ? n_groups : n_cu;
     hipLaunchKernelGGL(prefill_idx_topk_kernel, dim3((unsigned)blocks), dim3(PF_WAVES * 64), 0, st, a.q8, a.qs,
-                       a.k8, a.ks, a.w, (int)a.L, (int)row_lo, a.k, (int)n_groups, a.idx);
+                       a.k8, a.ks, a.w, a.q_pos, (int)a.B, (int)a.n_q, (int)a.n_k, (int)row_lo, a.k,
+                       (int)n_groups, a.idx);
   }
   return hipGetLastError();
 }

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
-DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_PREFILL, DSA_OP_DECODE, DSA_OP_SELECT = range(6)
+DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_PREFILL, DSA_OP_DECODE, DSA_OP_SELECT, DSA_OP_CHUNK = range(7)
 
 _i64, _i32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -40,6 +40,9 @@ _SIGNATURES = {
     "dsa_forward_decode": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                           _vp, _vp, _vp, _sz, _vp]),
+    "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
+                                         _vp, _vp, _vp, _sz, _vp]),
     "dsa_fp8_quantize_rows": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
     "dsa_kcache_append": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp]),
 }
@@ -210,6 +213,29 @@ def forward_decode(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cac
                                     _ptr(v_cache), H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
                                     _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream()))
+    return idx, out, lse
+
+
+def forward_chunk(q_pos, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cache, k: int, sm_scale: float,
+                  d_v: int, v_cache=None, idx=None, out=None, lse=None, ws=None):
+    """Whole DSA layer for a chunk of n_q new tokens in each of B sequences; row i of
+    sequence b sits at position q_pos[b] + i and sees cache rows up to it
+    -> (idx [B, n_q, k], out [B, n_q, H, d_v], lse [B, n_q, H])."""
+    B, n_q, H_I, d_I = q_idx.shape
+    n_k_max = k_cache.shape[1]
+    _, _, H, d_qk = q.shape
+    it, at = _idx_dtype(q_idx), _attn_dtype(q)
+    dev = q.device
+    idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev) if idx is None else idx
+    out = torch.empty((B, n_q, H, d_v), dtype=q.dtype, device=dev) if out is None else out
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_CHUNK, B, n_q, n_k_max, H, d_v, k, at), dev)
+    _check(lib().dsa_forward_chunk(B, n_q, _ptr(q_pos), n_k_max, _ptr(q_idx), _ptr(q_scale), _ptr(w),
+                                   _ptr(k_cache), _ptr(k_cache_scale), _ptr(q), _ptr(kv_cache),
+                                   _ptr(v_cache), H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
+                                   _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
 
 

@@ -27,7 +27,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 12
+    assert len(syms) == 13
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(dsa._SIGNATURES)
@@ -112,6 +112,33 @@ def test_forward_validation(L):
     assert need >= 64 * 131072 * 4
     assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG   # misaligned workspace
     assert call(nkm=1 << 19, ws=FAKE, wsb=1 << 40) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_chunk_validation(L):
+    ch = dict(B=4, nq=512, qpos=FAKE, nkm=131072, qi=FAKE, qs=FAKE, w=FAKE, kc=FAKE, kcs=FAKE, q=FAKE,
+              kv=FAKE, v=None, H_I=64, d_I=128, H=128, dqk=576, dv=512, k=2048, sm=0.04,
+              it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    order = list(ch)
+    call = lambda **kw: L.dsa_forward_chunk(*[kw.get(n, ch[n]) for n in order])
+    assert call(qpos=None) == dsa.DSA_ERR_INVALID_ARG           # positions are required
+    assert call(nq=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(B=65536) == dsa.DSA_ERR_INVALID_ARG
+    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED               # fused selection keeps <= 2048
+    assert call(nkm=1 << 25) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(it=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED       # fp32 indexer with bf16 attention
+    assert call(kc=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG          # misaligned FP8 cache
+    # the FP8 path stores no scores; 4 x 512 queries need no split-key workspace either
+    assert L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 512, 131072, 128, 512, 2048, dsa.DSA_BF16) == 0
+    # one query per sequence splits keys over blocks: workspace required
+    need = L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 1, 131072, 128, 512, 2048, dsa.DSA_BF16)
+    assert need > 0 and call(nq=1) == dsa.DSA_ERR_WORKSPACE
+    f32 = dict(it=dsa.DSA_F32, at=dsa.DSA_F32, H_I=2, d_I=32, H=4, dqk=64, dv=64, v=FAKE, k=64, nkm=4096,
+               nq=16)
+    need = L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 16, 4096, 4, 64, 64, dsa.DSA_F32)
+    assert need >= 4 * 16 * 4096 * 4
+    assert call(**f32) == dsa.DSA_ERR_WORKSPACE
+    assert call(**dict(f32, ws=FAKE + 8, wsb=need)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(**dict(f32, nq=70000, ws=FAKE, wsb=1 << 42)) == dsa.DSA_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_host_tensors():
