@@ -237,6 +237,44 @@ def dense_causal_mqa(q: np.ndarray, kv: np.ndarray, v: np.ndarray, pos: np.ndarr
 
 
 # ----------------------------------------------------------------------------------------
+# indexer KL-alignment loss  [P3 "阶段一：Dense Warm-up", "阶段二：Sparse Training";
+#                             P4 "持续预训练"; P2 "DeepSeek Sparse Attention (DSA)"]
+# ----------------------------------------------------------------------------------------
+
+
+def _logsumexp(x: np.ndarray, axis=None) -> np.ndarray:
+    m = np.max(x, axis=axis, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    return np.squeeze(m, axis=axis) + np.log(np.sum(np.exp(x - m), axis=axis))
+
+
+def indexer_kl_row(q_t: np.ndarray, kv: np.ndarray, idx_t: np.ndarray, scores_t: np.ndarray,
+                   sm_scale: float) -> tuple:
+    """The indexer's KL loss for one query over its key set S (the valid ids of idx_t).
+
+    Target: the main attention's distribution, summed over the heads and L1-normalised,
+    p(s) = (1/H) sum_h softmax_{s in S}(sm_scale q_h . kv_s).  Indexer side: the softmax
+    over S of the index scores scores_t (one per slot of idx_t).  Returns
+    (sum_{s in S} p(s) (ln p(s) - ln q(s)), p per slot (0 for ids outside the keys)).
+    An empty S gives (0, zeros).  The dense warm-up is the case S = {0, .., t}.
+    """
+    idx_t = np.asarray(idx_t)
+    valid = (idx_t >= 0) & (idx_t < kv.shape[0])
+    p_slots = np.zeros(idx_t.shape[0])
+    if not valid.any():
+        return 0.0, p_slots
+    z = sm_scale * (q_t @ kv[idx_t[valid]].T)                 # [H, |S|]
+    P = np.exp(z - _logsumexp(z, axis=1)[:, None])           # each head's softmax over S
+    p = P.sum(axis=0) / P.sum()                              # summed over heads, L1-normalised
+    I = np.asarray(scores_t, dtype=np.float64)[valid]
+    log_q = I - _logsumexp(I)
+    pos = p > 0
+    kl = float(np.sum(p[pos] * (np.log(p[pos]) - log_q[pos])))
+    p_slots[valid] = p
+    return kl, p_slots
+
+
+# ----------------------------------------------------------------------------------------
 # whole layer
 # ----------------------------------------------------------------------------------------
 

@@ -408,3 +408,54 @@ def test_fp8_quantize_rows_invariants():
     # scaling a row by a power of two leaves its codes unchanged and scales its scale
     c2, s2 = O.fp8_quantize_rows(x * np.float32(8.0))
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales * np.float32(8.0))
+
+
+# ------------------------------------------------------------------ indexer KL loss
+
+def test_indexer_kl_two_point_closed_forms():
+    """One head, two keys with logits 0 and ln 3 -> p = (1/4, 3/4); equal index scores ->
+    q = (1/2, 1/2): KL = 1/4 ln(1/2) + 3/4 ln(3/2).  Two heads with mirrored logits average
+    to p = (1/2, 1/2); index scores (0, ln 3) -> q = (1/4, 3/4): KL = 1/2 ln 2 + 1/2 ln(2/3)."""
+    kv = np.array([[0.0], [math.log(3.0)]])
+    kl, p = O.indexer_kl_row(np.array([[1.0]]), kv, np.array([0, 1]), np.array([5.0, 5.0]), 1.0)
+    assert p.tolist() == pytest.approx([0.25, 0.75], abs=1e-15)
+    assert kl == pytest.approx(0.25 * math.log(0.5) + 0.75 * math.log(1.5), abs=1e-15)
+    kv2 = np.array([[0.0, math.log(3.0)], [math.log(3.0), 0.0]])
+    q2 = np.array([[1.0, 0.0], [0.0, 1.0]])    # head 0 sees (0, ln 3), head 1 sees (ln 3, 0)
+    kl2, p2 = O.indexer_kl_row(q2, kv2, np.array([0, 1]), np.array([0.0, math.log(3.0)]), 1.0)
+    assert p2.tolist() == pytest.approx([0.5, 0.5], abs=1e-15)
+    assert kl2 == pytest.approx(0.5 * math.log(2.0) + 0.5 * math.log(2.0 / 3.0), abs=1e-15)
+
+
+def test_indexer_kl_matches_scipy_entropy_and_invariants():
+    from scipy.stats import entropy
+    rng = np.random.default_rng(17)
+    H, d, n_k = 6, 12, 40
+    kv = rng.standard_normal((n_k, d))
+    q = rng.standard_normal((H, d))
+    idx = rng.choice(n_k, 25, replace=False)
+    sc = rng.standard_normal(25) * 3
+    kl, p = O.indexer_kl_row(q, kv, idx, sc, 0.4)
+    # the target distribution, built head by head without the oracle's code path
+    z = 0.4 * np.einsum("hd,sd->hs", q, kv[idx])
+    ph = np.exp(z - z.max(axis=1, keepdims=True))
+    ph /= ph.sum(axis=1, keepdims=True)
+    target = ph.mean(axis=0)
+    qd = np.exp(sc - sc.max())
+    qd /= qd.sum()
+    assert p == pytest.approx(target, rel=1e-12)
+    assert kl == pytest.approx(entropy(target, qd), rel=1e-12)
+    assert kl > 0
+    # a constant added to every index score, a permutation of the slots, and ignored slots
+    # leave the loss unchanged
+    assert O.indexer_kl_row(q, kv, idx, sc + 123.0, 0.4)[0] == pytest.approx(kl, rel=1e-12)
+    perm = rng.permutation(25)
+    assert O.indexer_kl_row(q, kv, idx[perm], sc[perm], 0.4)[0] == pytest.approx(kl, rel=1e-12)
+    idx_pad = np.concatenate([idx, [-1, n_k, -7]])
+    kl_pad, p_pad = O.indexer_kl_row(q, kv, idx_pad, np.concatenate([sc, [1e9, 1e9, 1e9]]), 0.4)
+    assert kl_pad == pytest.approx(kl, rel=1e-12) and np.all(p_pad[-3:] == 0)
+    # index scores equal to ln p (plus any constant) give q = p: zero loss
+    assert O.indexer_kl_row(q, kv, idx, np.log(target) - 4.0, 0.4)[0] == pytest.approx(0.0, abs=1e-13)
+    # an empty key set
+    kl0, p0 = O.indexer_kl_row(q, kv, np.array([-1, -1]), np.array([0.0, 0.0]), 0.4)
+    assert kl0 == 0.0 and np.all(p0 == 0)
