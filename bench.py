@@ -303,6 +303,23 @@ def main():
     log(f"[bench] chunk of {C} tokens at q_pos {p0}: {t_c * 1e3:.3f} ms ({C / t_c:.0f} tokens/s)")
     del cidx, cout, clse, ws_c
 
+    # indexer KL loss of the sparse training stage over this step's selection: the index
+    # scores of the selected keys, then the loss (one pass over the gathered rows)
+    isc = torch.empty((L, k), dtype=torch.float32, device="cuda")
+    klv = torch.empty((L,), dtype=torch.float32, device="cuda")
+    dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, k, cfg.sm_scale, cfg.d_v, idx=idx, out=out, lse=lse, ws=ws)
+    t_sa = time_calls(torch, lambda: dsa.indexer_scores_at(qi, qs, ki, ks, w, idx, out=isc), args.stage_reps)
+    t_kl = time_calls(torch, lambda: dsa.indexer_kl(q, kv, idx, lse, isc, cfg.sm_scale, kl=klv), args.stage_reps)
+    kept = kept_keys(L, k)
+    sa_bytes = kept * (cfg.d_I + 4) + 2 * L * k * 4
+    stages["indexer_kl"] = {
+        "scores_at_ms": t_sa * 1e3, "scores_at_bytes": sa_bytes, "scores_at_hbm_frac": sa_bytes / t_sa / PEAK_HBM,
+        "kl_ms": t_kl * 1e3, "kl_gather_bytes": g_bytes, "kl_hbm_frac": g_bytes / t_kl / PEAK_HBM,
+        "mean_kl": float(klv.mean()), "note": "sparse-stage indexer loss forward over the step's selection"}
+    log(f"[bench] indexer KL: scores at selected keys {t_sa * 1e3:.3f} ms, KL {t_kl * 1e3:.3f} ms "
+        f"({g_bytes / t_kl / 1e9:.0f} GB/s gathered), mean KL {float(klv.mean()):.4f}")
+    del isc, klv
+
     decode = None
     if args.decode_workload != "none":
         del out, lse, q

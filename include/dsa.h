@@ -239,6 +239,47 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
                       float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
+ * dsa_indexer_scores_at -- lightning-indexer scores of the listed keys only (the scores the
+ * selection ranked, for the indexer loss below).
+ *
+ *   q_idx, q_scale, k_idx, k_scale, w: as for dsa_indexer (B sequences, n_q rows, n_k keys)
+ *   idx     [B, n_q, k] int32 device: key ids per row; ids outside [0, n_k) score -inf
+ *   scores  [B, n_q, k] fp32 output: scores[b][i][j] = I[i, idx[b][i][j]]
+ * No causal mask is applied: the ids say which keys to score.  The value of every score
+ * is bit-identical to the one dsa_indexer writes for the same (row, key).  FP8 or fp32
+ * (dtype); no workspace.
+ */
+int dsa_indexer_scores_at(const void* q_idx, const float* q_scale, const void* k_idx,
+                          const float* k_scale, const float* w, const int32_t* idx, int64_t B,
+                          int64_t n_q, int64_t n_k, int32_t H_I, int32_t d_I, int32_t k,
+                          int32_t dtype, float* scores, dsa_stream_t stream);
+
+/*
+ * dsa_indexer_kl -- forward of the indexer's KL-alignment loss over each query's selected
+ * keys (the sparse training stage: juhe.plus explainer, section 阶段二：Sparse Training;
+ * 53ai.com V3.2-Exp summary, section 持续预训练).  For query row t with key set S_t (its
+ * valid ids):
+ *     p_t(s)  = (1/H) sum_h exp(sm_scale q_h . kv_s - lse_h)     (the heads' attention
+ *               probabilities over S_t, summed and L1-normalised)
+ *     KL_t    = sum_{s in S_t} p_t(s) (ln p_t(s) - ln softmax_{S_t}(idx_scores)(s))
+ *
+ *   q [B, n_q, H, d_qk], kv [B, n_k, d_qk]   attention operands (dtype DSA_BF16 or DSA_F32)
+ *   idx        [B, n_q, k] int32: S_t (ids outside [0, n_k) are ignored)
+ *   lse        [B, n_q, H] fp32: log-sum-exp of the scaled logits over S_t, as
+ *              dsa_sparse_mla / dsa_forward_* return it
+ *   idx_scores [B, n_q, k] fp32: index scores of the slots (dsa_indexer_scores_at)
+ *   kl         [B, n_q] fp32 output (0 for a row with no valid id); the loss of a batch
+ *              is their sum (or mean)
+ *   p_out      [B, n_q, k] fp32 or NULL: p_t of each slot (0 for ignored slots)
+ * bf16 path: H = 128, d_qk = 576, k a multiple of 32 up to 2048; fp32 path: H <= 64,
+ * d_qk <= 256.  No workspace.
+ */
+int dsa_indexer_kl(const void* q, const void* kv, const int32_t* idx, const float* lse,
+                   const float* idx_scores, int64_t B, int64_t n_q, int64_t n_k, int32_t H,
+                   int32_t d_qk, int32_t k, float sm_scale, int32_t dtype, float* kl,
+                   float* p_out, dsa_stream_t stream);
+
+/*
  * dsa_fp8_quantize_rows -- FP8 E4M3FN quantisation of the indexer operands, the step
  * before the lightning indexer (the indexer runs in FP8: 53ai.com V3.2-Exp summary,
  * section 创新架构; juhe.plus explainer, section 第一步：Lightning Indexer).  Per row of

@@ -340,4 +340,42 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
   return hip_status(dsa::launch_sparse_mla(a, s), "chunk sparse attention launch");
 }
 
+int dsa_indexer_scores_at(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                          const float* w, const int32_t* idx, int64_t B, int64_t n_q, int64_t n_k, int32_t H_I,
+                          int32_t d_I, int32_t k, int32_t dtype, float* scores, dsa_stream_t stream) {
+  REQUIRE(q_idx && q_scale && k_idx && k_scale && w && idx && scores, "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k > 0 && k > 0, "B in [1, 65535] and n_q, n_k, k > 0 required");
+  int st = check_indexer_shape(H_I, d_I, dtype);
+  if (st) return st;
+  if (dtype == DSA_FP8_E4M3) {
+    REQUIRE(aligned16(q_idx) && aligned16(k_idx), "FP8 operands must be 16-byte aligned");
+    REQUIRE((n_q + 3) / 4 <= 2147483647LL, "n_q too large");
+  } else {
+    REQUIRE(n_q <= 65535, "fp32 path supports n_q <= 65535");
+  }
+  dsa::ScoresAtArgs a{q_idx, q_scale, k_idx, k_scale, w, idx, B, n_q, n_k, H_I, d_I, k, dtype, scores};
+  return hip_status(dsa::launch_indexer_scores_at(a, (hipStream_t)stream), "dsa_indexer_scores_at launch");
+}
+
+int dsa_indexer_kl(const void* q, const void* kv, const int32_t* idx, const float* lse, const float* idx_scores,
+                   int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_qk, int32_t k, float sm_scale,
+                   int32_t dtype, float* kl, float* p_out, dsa_stream_t stream) {
+  REQUIRE(q && kv && idx && lse && idx_scores && kl, "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k > 0, "B in [1, 65535] and n_q, n_k > 0 required");
+  REQUIRE(n_q <= 2147483647LL, "n_q too large");
+  REQUIRE(H > 0 && d_qk > 0 && k > 0, "H, d_qk, k must be positive");
+  if (dtype == DSA_BF16) {
+    SUPPORT(H == 128 && d_qk == 576, "bf16 KL loss needs H = 128, d_qk = 576");
+    SUPPORT(k % 32 == 0 && k <= 2048, "bf16 KL loss needs k a multiple of 32, <= 2048 (got %d)", k);
+    REQUIRE(aligned16(q) && aligned16(kv) && aligned16(idx) && aligned16(idx_scores),
+            "bf16 path: q, kv, idx and idx_scores must be 16-byte aligned");
+  } else if (dtype == DSA_F32) {
+    SUPPORT(H <= 64 && d_qk <= 256 && k <= 4096, "fp32 KL loss needs H <= 64, d_qk <= 256, k <= 4096");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "KL loss dtype %d is not DSA_BF16 or DSA_F32", dtype);
+  }
+  dsa::KlArgs a{q, kv, idx, lse, idx_scores, B, n_q, n_k, H, d_qk, k, sm_scale, dtype, kl, p_out};
+  return hip_status(dsa::launch_indexer_kl(a, (hipStream_t)stream), "dsa_indexer_kl launch");
+}
+
 }  // extern "C"

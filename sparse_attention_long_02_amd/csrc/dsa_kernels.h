@@ -71,6 +71,36 @@ struct PrefillTopkArgs {
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 
+// index scores at the keys listed in idx [B, n_q, k] (-inf for ids outside [0, n_k))
+struct ScoresAtArgs {
+  const void* q_idx;
+  const float* q_scale;
+  const void* k_idx;
+  const float* k_scale;
+  const float* w;
+  const int32_t* idx;
+  int64_t B, n_q, n_k;
+  int32_t H_I, d_I, k, dtype;
+  float* scores;
+};
+hipError_t launch_indexer_scores_at(const ScoresAtArgs& a, hipStream_t st);
+
+// indexer KL loss over each query's selected keys, given the attention lse per head
+struct KlArgs {
+  const void* q;
+  const void* kv;
+  const int32_t* idx;
+  const float* lse;
+  const float* scores;  // index scores of the selected keys [B, n_q, k]
+  int64_t B, n_q, n_k;
+  int32_t H, d_qk, k;
+  float sm_scale;
+  int32_t dtype;
+  float* kl;     // [B, n_q]
+  float* p_out;  // [B, n_q, k] or null
+};
+hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st);
+
 // FP8 E4M3FN row quantiser: rows of `groups` groups; group b's row i (source row
 // b * n_per + i, ld_x elements apart) goes to destination row b * dst_per + base + i,
 // base = pos ? pos[b] : 0 (rows outside [0, dst_per) skipped); its scale is written

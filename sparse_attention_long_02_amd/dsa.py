@@ -43,6 +43,10 @@ _SIGNATURES = {
     "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                          _vp, _vp, _vp, _sz, _vp]),
+    "dsa_indexer_scores_at": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
+                                             _i32, _vp, _vp]),
+    "dsa_indexer_kl": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32,
+                                      _vp, _vp, _vp]),
     "dsa_fp8_quantize_rows": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
     "dsa_kcache_append": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp]),
 }
@@ -237,6 +241,38 @@ def forward_chunk(q_pos, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cache,
                                    _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
+
+
+def indexer_scores_at(q_idx, q_scale, k_idx, k_scale, w, idx, out=None) -> torch.Tensor:
+    """Index scores of the listed keys: q_idx [n_q, H_I, d_I] or [B, n_q, H_I, d_I], idx
+    [.., n_q, k] -> scores [.., n_q, k] fp32 (-inf for ids outside the keys)."""
+    batched = q_idx.dim() == 4
+    B = q_idx.shape[0] if batched else 1
+    n_q, H_I, d_I = q_idx.shape[-3:]
+    n_k = k_idx.shape[-2]
+    k = idx.shape[-1]
+    if out is None:
+        out = torch.empty(idx.shape, dtype=torch.float32, device=idx.device)
+    _check(lib().dsa_indexer_scores_at(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), _ptr(idx),
+                                       B, n_q, n_k, H_I, d_I, k, _idx_dtype(q_idx), _ptr(out), _stream()))
+    return out
+
+
+def indexer_kl(q, kv, idx, lse, idx_scores, sm_scale: float, p_out: bool = False, kl=None):
+    """Per-row KL(p_t || softmax of the index scores) over each row's selected keys, with
+    p_t the heads' attention probabilities (from lse) summed and L1-normalised.
+    q [n_q, H, d_qk] or [B, n_q, H, d_qk] -> (kl [.., n_q], p [.., n_q, k] or None)."""
+    batched = q.dim() == 4
+    B = q.shape[0] if batched else 1
+    n_q, H, d_qk = q.shape[-3:]
+    n_k = kv.shape[-2]
+    k = idx.shape[-1]
+    if kl is None:
+        kl = torch.empty(idx.shape[:-1], dtype=torch.float32, device=q.device)
+    p = torch.empty(idx.shape, dtype=torch.float32, device=q.device) if p_out else None
+    _check(lib().dsa_indexer_kl(_ptr(q), _ptr(kv), _ptr(idx), _ptr(lse), _ptr(idx_scores), B, n_q, n_k, H, d_qk, k,
+                                float(sm_scale), _attn_dtype(q), _ptr(kl), _ptr(p), _stream()))
+    return kl, p
 
 
 def _x_dtype(t: torch.Tensor) -> int:
