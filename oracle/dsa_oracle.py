@@ -226,6 +226,38 @@ def sparse_mqa(q: np.ndarray, kv: np.ndarray, v: np.ndarray, idx: np.ndarray,
     return np.stack([o for o, _ in outs]), np.stack([l for _, l in outs])
 
 
+def sparse_mqa_backward(q: np.ndarray, kv: np.ndarray, v: np.ndarray, idx: np.ndarray, d_out: np.ndarray,
+                        sm_scale: float, v_in_kv: bool) -> tuple:
+    """Gradients of ``sparse_mqa`` for the loss sum(O * d_out), by the chain rule through the
+    softmax over each row's kept keys (the sparse training stage trains the main model on
+    the selected keys: P3 "阶段二：Sparse Training"; P4 "持续预训练").
+
+    q [n_q, H, d_qk], kv [n_k, d_qk], v [n_k, d_v], idx [n_q, k] (-1 = unused; a repeated id
+    counts once per slot), d_out [n_q, H, d_v].  Returns (dq, dkv, dv): dkv sums every
+    query's contribution to each key row; with ``v_in_kv`` (V = kv[:, :d_v]) the value
+    gradient is added into dkv[:, :d_v] and dv is None.
+    """
+    n_q = q.shape[0]
+    dq = np.zeros_like(q, dtype=np.float64)
+    dkv = np.zeros(kv.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for i in range(n_q):
+        sel = idx[i][(idx[i] >= 0) & (idx[i] < kv.shape[0])]
+        if len(sel) == 0:
+            continue
+        z = sm_scale * (q[i] @ kv[sel].T)                       # [H, |S|]
+        P = np.exp(z - _logsumexp(z, axis=1)[:, None])         # softmax over the kept keys
+        dP = d_out[i] @ v[sel].T                                # dL/dP
+        dZ = P * (dP - np.sum(P * dP, axis=1, keepdims=True))   # through the softmax
+        dq[i] = sm_scale * (dZ @ kv[sel])
+        np.add.at(dkv, sel, sm_scale * (dZ.T @ q[i]))
+        np.add.at(dv, sel, P.T @ d_out[i])
+    if v_in_kv:
+        dkv[:, : v.shape[1]] += dv
+        return dq, dkv, None
+    return dq, dkv, dv
+
+
 def dense_causal_mqa(q: np.ndarray, kv: np.ndarray, v: np.ndarray, pos: np.ndarray,
                      sm_scale: float) -> tuple:
     """Ordinary causal attention (every head attends to keys 0..pos) for comparison."""

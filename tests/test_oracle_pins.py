@@ -459,3 +459,78 @@ def test_indexer_kl_matches_scipy_entropy_and_invariants():
     # an empty key set
     kl0, p0 = O.indexer_kl_row(q, kv, np.array([-1, -1]), np.array([0.0, 0.0]), 0.4)
     assert kl0 == 0.0 and np.all(p0 == 0)
+
+
+# ------------------------------------------------------------------ sparse attention backward
+
+def _bwd_problem(rng, n_q=5, n_k=9, H=3, d=6, d_v=4, k=4, v_in_kv=False):
+    q = rng.standard_normal((n_q, H, d))
+    kv = rng.standard_normal((n_k, d))
+    v = kv[:, :d_v] if v_in_kv else rng.standard_normal((n_k, d_v))
+    idx = np.stack([rng.choice(n_k, k, replace=False) for _ in range(n_q)]).astype(np.int32)
+    idx[1, 2] = -1                       # an unused slot
+    idx[3, 1] = idx[3, 0]                # a repeated id counts once per slot
+    g = rng.standard_normal((n_q, H, d_v))
+    return q, kv, v, idx, g
+
+
+def test_attention_backward_matches_finite_differences():
+    rng = np.random.default_rng(31)
+    for v_in_kv in (False, True):
+        q, kv, v, idx, g = _bwd_problem(rng, v_in_kv=v_in_kv)
+        sm = 0.37
+        dq, dkv, dv = O.sparse_mqa_backward(q, kv, v, idx, g, sm, v_in_kv)
+
+        def loss(q_, kv_, v_):
+            o, _ = O.sparse_mqa(q_, kv_, kv_[:, : v.shape[1]] if v_in_kv else v_, idx, sm)
+            return float(np.sum(o * g))
+
+        eps = 1e-6
+        for arr, grad in ((q, dq), (kv, dkv)) + (() if v_in_kv else ((v, dv),)):
+            num = np.zeros_like(arr)
+            for pos in np.ndindex(arr.shape):
+                old = arr[pos]
+                arr[pos] = old + eps
+                lp = loss(q, kv, v)
+                arr[pos] = old - eps
+                lm = loss(q, kv, v)
+                arr[pos] = old
+                num[pos] = (lp - lm) / (2 * eps)
+            assert np.allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def test_attention_backward_matches_torch_autograd():
+    """An independent torch float64 forward (gather, softmax, weighted sum) differentiated by
+    autograd, on a multi-query problem with V inside kv."""
+    rng = np.random.default_rng(32)
+    q, kv, v, idx, g = _bwd_problem(rng, n_q=7, n_k=12, H=4, d=10, d_v=6, k=5, v_in_kv=True)
+    sm = 0.2
+    dq, dkv, _ = O.sparse_mqa_backward(q, kv, v, idx, g, sm, True)
+    tq = torch.tensor(q, requires_grad=True)
+    tkv = torch.tensor(kv, requires_grad=True)
+    outs = []
+    for i in range(q.shape[0]):
+        ids = torch.tensor([s for s in idx[i] if s >= 0])
+        rows = tkv[ids]                                   # [|S|, d]
+        w = torch.softmax(sm * tq[i] @ rows.T, dim=1)     # [H, |S|]
+        outs.append(w @ rows[:, :6])
+    torch.sum(torch.stack(outs) * torch.tensor(g)).backward()
+    assert np.allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dkv, tkv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_backward_single_key_closed_form():
+    """One kept key: P = 1 whatever the logits, so dq = 0, the key part of dkv is 0 and the
+    value rows receive the heads' summed output gradients."""
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((2, 3, 5))
+    kv = rng.standard_normal((6, 5))
+    v = rng.standard_normal((6, 4))
+    idx = np.array([[4, -1], [-1, 1]], dtype=np.int32)
+    g = rng.standard_normal((2, 3, 4))
+    dq, dkv, dv = O.sparse_mqa_backward(q, kv, v, idx, g, 0.5, False)
+    assert np.all(dq == 0) and np.allclose(dkv, 0, atol=1e-15)
+    want = np.zeros((6, 4))
+    want[4] = g[0].sum(axis=0)
+    want[1] = g[1].sum(axis=0)
+    assert np.allclose(dv, want, rtol=1e-14)
