@@ -320,6 +320,25 @@ def main():
         f"({g_bytes / t_kl / 1e9:.0f} GB/s gathered), mean KL {float(klv.mean()):.4f}")
     del isc, klv
 
+    # backward of the sparse attention over the step's selection (the sparse training
+    # stage): seeded bf16 output gradients of the workload's shape
+    dout = torch.empty((L, cfg.H, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    gb = torch.Generator(device="cuda").manual_seed(1)
+    for r0 in range(0, L, 8192):
+        dout[r0:r0 + 8192] = torch.randn((min(8192, L - r0), cfg.H, cfg.d_v), generator=gb, device="cuda")
+    ws_b = torch.empty(dsa.workspace_size(dsa.DSA_OP_MLA_BWD, 1, L, L, cfg.H, cfg.d_v, k, dsa.DSA_BF16),
+                       dtype=torch.uint8, device="cuda")
+    t_bwd = time_calls(torch, lambda: dsa.sparse_mla_backward(q, kv, idx, out, lse, dout, cfg.sm_scale, ws=ws_b),
+                       args.stage_reps)
+    f_bwd = kept * cfg.H * 2 * (3 * cfg.d_qk + 2 * cfg.d_v)
+    stages["sparse_mla_backward"] = {
+        "ms": t_bwd * 1e3, "bf16_flop": f_bwd, "mfma_frac": f_bwd / t_bwd / PEAK_BF16,
+        "gather_bytes": g_bytes, "dkv_atomic_bytes": kept * cfg.d_qk * 4,
+        "note": "dq and dkv (fp32 atomics) of the step's attention for seeded output gradients"}
+    log(f"[bench] sparse MLA backward: {t_bwd * 1e3:.3f} ms ({f_bwd / t_bwd / 1e12:.0f} TFLOP/s bf16)")
+    del dout, ws_b
+    torch.cuda.empty_cache()
+
     decode = None
     if args.decode_workload != "none":
         del out, lse, q

@@ -73,7 +73,8 @@ enum dsa_status {
 enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 };
 
 enum dsa_op { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2,
-              DSA_OP_PREFILL = 3, DSA_OP_DECODE = 4, DSA_OP_SELECT = 5, DSA_OP_CHUNK = 6 };
+              DSA_OP_PREFILL = 3, DSA_OP_DECODE = 4, DSA_OP_SELECT = 5, DSA_OP_CHUNK = 6,
+              DSA_OP_MLA_BWD = 7 };
 
 /* DSA_ABI_VERSION of the loaded library. */
 int dsa_abi_version(void);
@@ -147,6 +148,33 @@ int dsa_sparse_mla(const void* q, const void* kv, const void* v, const int32_t* 
                    int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_qk, int32_t d_v,
                    int32_t k, float sm_scale, int32_t dtype, void* out, float* lse, void* ws,
                    size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_sparse_mla_backward -- gradients of dsa_sparse_mla for the sparse training stage
+ * (the main model learns on the sparse pattern: juhe.plus explainer, section
+ * 阶段二：Sparse Training; 53ai.com V3.2-Exp summary, section 持续预训练).  With the
+ * forward's P[h,s] = exp(sm_scale q_h . kv_s - lse_h) over each row's valid ids:
+ *     dP = dO . v_s,  dZ = P (dP - dO_h . O_h),  dq_h = sm_scale sum_s dZ kv_s,
+ *     dkv_s += sm_scale sum_h dZ q_h (and sum_h P dO_h on the V values)
+ * summed over every query that selected s.
+ *
+ *   q, kv, v, idx, lse: the forward's inputs and lse; out [B, n_q, H, d_v]: its output
+ *          (bf16 path; may be NULL for fp32); d_out [B, n_q, H, d_v]: gradient of out
+ *   d_q    [B, n_q, H, d_qk] output, dtype of q
+ *   d_kv   [B, n_k, d_qk] fp32 output, zeroed and accumulated by the call (V = kv[:, :d_v]
+ *          adds its gradient here); d_v_out [B, n_k, d_v] fp32 for a separate V (fp32
+ *          path), else NULL
+ * dtype DSA_BF16 (H = 128, d_qk = 576, d_v = 512, V inside kv, k a multiple of 32 up to
+ * 2048) or DSA_F32 (small shapes).  Workspace: dsa_workspace_size(DSA_OP_MLA_BWD, B, n_q,
+ * n_k, H, d_v, k, dtype) (bf16: the transposed q and dO and the bf16 P and dZ of up to
+ * 4096 queries at a time).  Order of the dkv sums is not fixed (atomics): d_kv is
+ * reproducible to rounding, not bit for bit.
+ */
+int dsa_sparse_mla_backward(const void* q, const void* kv, const void* v, const int32_t* idx,
+                            const void* out, const float* lse, const void* d_out, int64_t B,
+                            int64_t n_q, int64_t n_k, int32_t H, int32_t d_qk, int32_t d_v,
+                            int32_t k, float sm_scale, int32_t dtype, void* d_q, float* d_kv,
+                            float* d_v_out, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * dsa_select_prefill -- stages 1 and 2 for one sequence of L tokens (query t at position

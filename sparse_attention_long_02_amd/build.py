@@ -16,7 +16,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "prefill_topk.hip", "sparse_mla.hip", "quant.hip",
-           "attn_kl.hip"]
+           "attn_kl.hip", "sparse_mla_bwd.hip"]
+# sources whose kernels keep MFMA accumulators in the accumulation registers (the backward's
+# dq accumulators do not fit next to its operands in the vector registers)
+AGPR_ACC = {"sparse_mla_bwd.hip"}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -47,7 +50,10 @@ def build(verbose: bool = False, extra: list | None = None) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(HERE, "_build", os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-c",
+        flags = HIPCC_FLAGS
+        if src in AGPR_ACC:
+            flags = [f for f in HIPCC_FLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+        cmd = [hipcc(), *flags, *(extra or []), "-I", os.path.join(ROOT, "include"), "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

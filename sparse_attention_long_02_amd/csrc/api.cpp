@@ -109,6 +109,8 @@ size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32
       return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : 0;
     case DSA_OP_DECODE:
       return align256(decode_scores_bytes(B, n_k)) + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
+    case DSA_OP_MLA_BWD:
+      return dsa::sparse_mla_bwd_ws_bytes(B, n_q, k, dtype);
     case DSA_OP_CHUNK:
       return chunk_scores_bytes(B, n_q, n_k, dtype) + dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, dtype);
     default:
@@ -376,6 +378,33 @@ int dsa_indexer_kl(const void* q, const void* kv, const int32_t* idx, const floa
   }
   dsa::KlArgs a{q, kv, idx, lse, idx_scores, B, n_q, n_k, H, d_qk, k, sm_scale, dtype, kl, p_out};
   return hip_status(dsa::launch_indexer_kl(a, (hipStream_t)stream), "dsa_indexer_kl launch");
+}
+
+int dsa_sparse_mla_backward(const void* q, const void* kv, const void* v, const int32_t* idx, const void* out,
+                            const float* lse, const void* d_out, int64_t B, int64_t n_q, int64_t n_k, int32_t H,
+                            int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t dtype, void* d_q,
+                            float* d_kv, float* d_v_out, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(q && kv && idx && lse && d_out && d_q && d_kv, "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k > 0, "B in [1, 65535] and n_q, n_k > 0 required");
+  REQUIRE(B * n_q <= 2147483647LL, "B * n_q too large");
+  int st = check_attn_shape(H, d_qk, d_v, k, dtype, v != nullptr);
+  if (st) return st;
+  if (dtype == DSA_BF16) {
+    REQUIRE(out, "the bf16 backward needs the forward output (out)");
+    REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out) && aligned16(d_out) && aligned16(d_q) &&
+                aligned16(idx) && aligned16(d_kv),
+            "bf16 backward operands must be 16-byte aligned");
+    const size_t need = dsa::sparse_mla_bwd_ws_bytes(B, n_q, k, dtype);
+    if (!ws || ws_bytes < need)
+      return fail(DSA_ERR_WORKSPACE, "dsa_sparse_mla_backward needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  } else {
+    REQUIRE(!v || d_v_out, "a separate V needs d_v_out");
+    SUPPORT(n_q <= 65535, "fp32 backward supports n_q <= 65535");
+  }
+  dsa::MlaBwdArgs a{q, kv, v, idx, out, lse, d_out, B, n_q, n_k, H, d_qk, d_v, k, sm_scale, dtype,
+                    d_q, d_kv, d_v_out, ws};
+  return hip_status(dsa::launch_sparse_mla_bwd(a, (hipStream_t)stream), "dsa_sparse_mla_backward launch");
 }
 
 }  // extern "C"

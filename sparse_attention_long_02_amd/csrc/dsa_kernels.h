@@ -71,6 +71,28 @@ struct PrefillTopkArgs {
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 
+// backward of the sparse attention; dkv (and dv when v is separate, fp32 path) are
+// zeroed and accumulated
+struct MlaBwdArgs {
+  const void* q;
+  const void* kv;
+  const void* v;
+  const int32_t* idx;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  int64_t B, n_q, n_k;
+  int32_t H, d_qk, d_v, k;
+  float sm_scale;
+  int32_t dtype;
+  void* dq;
+  float* dkv;
+  float* dv;
+  void* ws;
+};
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, hipStream_t st);
+size_t sparse_mla_bwd_ws_bytes(int64_t B, int64_t n_q, int32_t k, int32_t dtype);
+
 // index scores at the keys listed in idx [B, n_q, k] (-inf for ids outside [0, n_k))
 struct ScoresAtArgs {
   const void* q_idx;

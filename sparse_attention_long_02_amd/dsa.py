@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
-DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_PREFILL, DSA_OP_DECODE, DSA_OP_SELECT, DSA_OP_CHUNK = range(7)
+(DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_PREFILL, DSA_OP_DECODE, DSA_OP_SELECT, DSA_OP_CHUNK,
+ DSA_OP_MLA_BWD) = range(8)
 
 _i64, _i32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -43,6 +44,8 @@ _SIGNATURES = {
     "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
                                          _vp, _vp, _vp, _sz, _vp]),
+    "dsa_sparse_mla_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                                               _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dsa_indexer_scores_at": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
                                              _i32, _vp, _vp]),
     "dsa_indexer_kl": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32,
@@ -241,6 +244,28 @@ def forward_chunk(q_pos, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cache,
                                    _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
+
+
+def sparse_mla_backward(q, kv, idx, out, lse, d_out, sm_scale: float, v=None, ws=None):
+    """Gradients of sparse_mla: q [n_q, H, d_qk] or [B, n_q, H, d_qk], kv [.., n_k, d_qk],
+    idx [.., n_q, k], the forward's out and lse, and d_out -> (d_q like q, d_kv fp32 like
+    kv, d_v fp32 or None)."""
+    batched = q.dim() == 4
+    B = q.shape[0] if batched else 1
+    n_q, H, d_qk = q.shape[-3:]
+    n_k = kv.shape[-2]
+    d_v = d_out.shape[-1]
+    k = idx.shape[-1]
+    dt = _attn_dtype(q)
+    d_q = torch.empty_like(q)
+    d_kv = torch.empty(kv.shape, dtype=torch.float32, device=q.device)
+    d_v_out = torch.empty(v.shape, dtype=torch.float32, device=q.device) if v is not None else None
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_MLA_BWD, B, n_q, n_k, H, d_v, k, dt), q.device)
+    _check(lib().dsa_sparse_mla_backward(_ptr(q), _ptr(kv), _ptr(v), _ptr(idx), _ptr(out), _ptr(lse), _ptr(d_out),
+                                         B, n_q, n_k, H, d_qk, d_v, k, float(sm_scale), dt, _ptr(d_q), _ptr(d_kv),
+                                         _ptr(d_v_out), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return d_q, d_kv, d_v_out
 
 
 def indexer_scores_at(q_idx, q_scale, k_idx, k_scale, w, idx, out=None) -> torch.Tensor:
