@@ -391,6 +391,7 @@ int dsa_sparse_mla_backward(const void* q, const void* kv, const void* v, const 
   if (st) return st;
   if (dtype == DSA_BF16) {
     REQUIRE(out, "the bf16 backward needs the forward output (out)");
+    SUPPORT(n_k * 576 < (1LL << 32), "bf16 backward supports n_k * 576 < 2^32");
     REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out) && aligned16(d_out) && aligned16(d_q) &&
                 aligned16(idx) && aligned16(d_kv),
             "bf16 backward operands must be 16-byte aligned");

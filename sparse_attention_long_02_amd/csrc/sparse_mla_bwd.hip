@@ -68,6 +68,9 @@ __global__ __launch_bounds__(256) void mla_bwd_transpose(const uint16_t* __restr
 // ---------------------------------------------------------------------------------------
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// instruction classes of the scheduler's group directives
+constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
+
 // The row's last valid slot (every lane of every wave gets it), from all its ids loaded at
 // once (k a multiple of 32, at most MAX_K); returns the number of 32-key chunks to run.
 __device__ __forceinline__ int bwd_chunks(const int32_t* __restrict__ irow, int k, int64_t n_k, int l) {
@@ -139,6 +142,14 @@ __device__ __forceinline__ int row_quad_off(int r, int j, int qq) {
   return LAT_BYTES + r * ROPE_PITCH + 16 * (u ^ rope_swz(r)) + 8 * (qq & 1);
 }
 
+// Blocks are dispatched to the 8 XCDs round robin (block i on XCD i % 8).  This maps block
+// i to a logical index so that each XCD takes one contiguous eighth of [0, n): neighbouring
+// queries, which select many of the same keys, then share that XCD's L2 (for the gathered
+// rows and for the dkv lines the atomics update).  Identity when n is not a multiple of 8.
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t i, int64_t n) {
+  return (n & 7) ? i : (i & 7) * (n >> 3) + (i >> 3);
+}
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -160,10 +171,11 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void mla_bwd_dq_kernel(
 
   const int tid = threadIdx.x, l = tid & 63, G = l >> 4, p = l & 15;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t gl = blockIdx.x >> 1;   // query within the pass
+  const int64_t lb = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t gl = lb >> 1;           // query within the pass
   const int64_t g = g0 + gl;            // query over all sequences
   const int64_t b = g / n_q;
-  const int head = 64 * (blockIdx.x & 1) + 16 * wv + p;
+  const int head = 64 * (int)(lb & 1) + 16 * wv + p;
   const int32_t* irow = idx + g * k;
   const uint16_t* kvb = kv + b * n_k * MDQK;
   const uint32_t nk = (uint32_t)min(n_k, (int64_t)INT32_MAX);
@@ -211,18 +223,31 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void mla_bwd_dq_kernel(
     }
     const uint8_t* cur = (c & 1) ? buf1 : buf0;
 
-    // S^T and dP^T for key tiles 0 (rows 0..15) and 1 (rows 16..31): A = the rows
-    v4f S[2], dP[2];
+    // S^T and dP^T for key tiles 0 (rows 0..15) and 1 (rows 16..31): A = the rows, read
+    // KPRE steps ahead of the MFMAs (step i: tile i/18, values 32(i%18) + 8G .. +7)
+    v4f S[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    v4f dP[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    {
+      constexpr int KPRE = 8, NSTEP = 36;
+      v8bf kr[KPRE];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-      dP[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-      const int r = 16 * kt + p;
+      for (int i = 0; i < KPRE; ++i) kr[i] = lds_v8bf(cur, row_unit_off(16 * (i / 18) + p, i % 18, G));
 #pragma unroll
-      for (int s = 0; s < 18; ++s) {
-        const v8bf kf = lds_v8bf(cur, row_unit_off(r, s, G));
+      for (int i = 0; i < NSTEP; ++i) {
+        const int kt = i / 18, s = i % 18;
+        const v8bf kf = kr[i % KPRE];
+        if (i + KPRE < NSTEP)
+          kr[i % KPRE] = lds_v8bf(cur, row_unit_off(16 * ((i + KPRE) / 18) + p, (i + KPRE) % 18, G));
         S[kt] = mfma_bf16_16x16x32(kf, Qb[s], S[kt]);
         if (s < 16) dP[kt] = mfma_bf16_16x16x32(kf, Db[s], dP[kt]);
+      }
+      // keep the reads ahead: the scheduler would otherwise sink each next to its MFMAs
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, KPRE, 0);
+#pragma unroll
+      for (int i = 0; i < NSTEP; ++i) {
+        if (i % 18 < 16) __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        if (i + KPRE < NSTEP) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
       }
     }
     // P, dZ (this lane: head `head`, keys 4G + r and 16 + 4G + r of the chunk)
@@ -252,12 +277,30 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void mla_bwd_dq_kernel(
     for (int e = 0; e < 8; ++e) Zb[e] = (__bf16)Zv[e];
     const int rr = p >> 2, qq = p & 3;
     const int r0 = 4 * G + rr, r1 = 16 + 4 * G + rr;
+    {
+      constexpr int TPRE = 8;  // tiles whose K^T reads run ahead of the MFMAs
+      v4s tlo[TPRE], thi[TPRE];
 #pragma unroll
-    for (int j = 0; j < DQ_TILES; ++j) {
-      const v4s lo = lds_tr4(cur, row_quad_off(r0, j, qq));
-      const v4s hi = lds_tr4(cur, row_quad_off(r1, j, qq));
-      const v8bf kt8 = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      dQt[j] = mfma_bf16_16x16x32(kt8, Zb, dQt[j]);
+      for (int j = 0; j < TPRE; ++j) {
+        tlo[j] = lds_tr4(cur, row_quad_off(r0, j, qq));
+        thi[j] = lds_tr4(cur, row_quad_off(r1, j, qq));
+      }
+#pragma unroll
+      for (int j = 0; j < DQ_TILES; ++j) {
+        const v8bf kt8 =
+            __builtin_bit_cast(v8bf, __builtin_shufflevector(tlo[j % TPRE], thi[j % TPRE], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (j + TPRE < DQ_TILES) {
+          tlo[j % TPRE] = lds_tr4(cur, row_quad_off(r0, j + TPRE, qq));
+          thi[j % TPRE] = lds_tr4(cur, row_quad_off(r1, j + TPRE, qq));
+        }
+        dQt[j] = mfma_bf16_16x16x32(kt8, Zb, dQt[j]);
+      }
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * TPRE, 0);
+#pragma unroll
+      for (int j = 0; j < DQ_TILES; ++j) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        if (j + TPRE < DQ_TILES) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+      }
     }
   }
   // dq[g][head][16j + 4G + r] = sm_scale * dQt[j][r]
@@ -288,7 +331,7 @@ __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
 
   const int tid = threadIdx.x, l = tid & 63, G = l >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t gl = blockIdx.x;
+  const int64_t gl = xcd_contiguous(blockIdx.x, gridDim.x);
   const int64_t g = g0 + gl;
   const int64_t b = g / n_q;
   const int32_t* irow = idx + g * k;
@@ -352,8 +395,8 @@ __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
           acc = mfma_bf16_32x32x16(ap, Dt[t][s], acc);
         }
       }
-      // lane: column 32j + l%32, rows (slots) 8(r/4) + 4G + r%4; 32-bit offsets from the
-      // sequence's base (n_k * 576 < 2^30 for every supported n_k)
+      // lane: column 32j + l%32, rows (slots) 8(r/4) + 4G + r%4; 32-bit element offsets
+      // from the sequence's base (n_k * 576 < 2^32, checked by the entry point)
       const uint32_t col = 32 * j + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
