@@ -1,11 +1,14 @@
 """Runs each prefill stage once, at a benchmark workload, for hardware-counter profiling.
 
     python -m sparse_attention_long_02_amd.stage_run [--workload prefill_128k] [--copy-mib 4096]
+                                                     [--training]
 
 Order of the dispatches: one device-to-device copy of --copy-mib MiB (its FETCH_SIZE and
 WRITE_SIZE readings calibrate the counters against a known byte count), then
 dsa_select_prefill (fill kernel + fused indexer/top-k kernel), then dsa_sparse_mla on that
-selection.  Inputs are the seeded synthetic tensors the benchmark uses.
+selection.  With --training, then the sparse-stage indexer loss (dsa_indexer_scores_at,
+dsa_indexer_kl) and dsa_sparse_mla_backward for seeded output gradients, as the benchmark
+runs them.  Inputs are the seeded synthetic tensors the benchmark uses.
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--copy-mib", type=int, default=4096)
+    ap.add_argument("--training", action="store_true")
     args = ap.parse_args()
 
     import torch
@@ -45,9 +49,23 @@ def main():
     dsa.select_prefill(qi, qs, ki, ks, w, cfg.k, idx=idx)
     torch.cuda.synchronize()
     print("[stage_run] select_prefill done", flush=True)
-    dsa.sparse_mla(q, kv, idx, cfg.sm_scale, cfg.d_v)
+    out, lse = dsa.sparse_mla(q, kv, idx, cfg.sm_scale, cfg.d_v)
     torch.cuda.synchronize()
     print("[stage_run] sparse_mla done", flush=True)
+    if not args.training:
+        return
+    isc = dsa.indexer_scores_at(qi, qs, ki, ks, w, idx)
+    dsa.indexer_kl(q, kv, idx, lse, isc, cfg.sm_scale)
+    torch.cuda.synchronize()
+    print("[stage_run] indexer KL done", flush=True)
+    del isc
+    dout = torch.empty((cfg.L, cfg.H, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    gb = torch.Generator(device="cuda").manual_seed(1)
+    for r0 in range(0, cfg.L, 8192):
+        dout[r0:r0 + 8192] = torch.randn((min(8192, cfg.L - r0), cfg.H, cfg.d_v), generator=gb, device="cuda")
+    dsa.sparse_mla_backward(q, kv, idx, out, lse, dout, cfg.sm_scale)
+    torch.cuda.synchronize()
+    print("[stage_run] sparse_mla_backward done", flush=True)
 
 
 if __name__ == "__main__":
