@@ -140,9 +140,12 @@ __device__ __forceinline__ v8i global_key_fragment(const uint8_t* __restrict__ k
   const int l = lane_id();
   int64_t key = key0 + 16 * f + (l & 15);
   key = key < n_k ? key : n_k - 1;
+  // plain loads: the two halves of a lane's 32 bytes come from two instructions that each
+  // touch half of every row, and the second must find the row in L2 (with streaming loads
+  // it was fetched from HBM twice)
   const v4i* p = reinterpret_cast<const v4i*>(k8 + key * IDX_DIM + 32 * (l >> 4));
-  const v4i lo = __builtin_nontemporal_load(p);
-  const v4i hi = __builtin_nontemporal_load(p + 1);
+  const v4i lo = p[0];
+  const v4i hi = p[1];
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 

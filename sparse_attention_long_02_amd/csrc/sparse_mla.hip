@@ -430,25 +430,35 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
                                                           const float* __restrict__ part_lse, int n_split,
                                                           int H, int d_v, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
+  constexpr int MAX_SPLIT = 16, PER = MDV / 128;  // the bf16 path: d_v = 512
   const int64_t qh = blockIdx.x;  // qrow * H + head
   const int64_t qrow = qh / H;
   const int head = (int)(qh % H);
+  // the splits' weights first, then every partial value this thread needs, all loads issued
+  // before any is used
+  float ls[MAX_SPLIT];
+#pragma unroll
+  for (int s = 0; s < MAX_SPLIT; ++s) ls[s] = s < n_split ? part_lse[(qrow * n_split + s) * H + head] : -INFINITY;
+  float po[MAX_SPLIT][PER];
+#pragma unroll
+  for (int s = 0; s < MAX_SPLIT; ++s)
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      po[s][j] = s < n_split ? part_o[((qrow * n_split + s) * H + head) * d_v + threadIdx.x + 128 * j] : 0.f;
   float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, part_lse[(qrow * n_split + s) * H + head]);
-  float den = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float ls = part_lse[(qrow * n_split + s) * H + head];
-    den += mx == -INFINITY ? 0.f : exp2f((ls - mx) * LOG2E);
+#pragma unroll
+  for (int s = 0; s < MAX_SPLIT; ++s) mx = fmaxf(mx, ls[s]);
+  float den = 0.f, acc[PER] = {};
+#pragma unroll
+  for (int s = 0; s < MAX_SPLIT; ++s) {
+    const float wgt = (s < n_split && mx != -INFINITY) ? exp2f((ls[s] - mx) * LOG2E) : 0.f;
+    den += wgt;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] += wgt * po[s][j];
   }
-  for (int d = threadIdx.x; d < d_v; d += 128) {
-    float acc = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float ls = part_lse[(qrow * n_split + s) * H + head];
-      const float wgt = mx == -INFINITY ? 0.f : exp2f((ls - mx) * LOG2E);
-      acc += wgt * part_o[((qrow * n_split + s) * H + head) * d_v + d];
-    }
-    out[qh * d_v + d] = f32_to_bf16_bits(den > 0.f ? acc / den : 0.f);
-  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    out[qh * d_v + threadIdx.x + 128 * j] = f32_to_bf16_bits(den > 0.f ? acc[j] / den : 0.f);
   if (lse && threadIdx.x == 0) lse[qh] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 

@@ -159,3 +159,32 @@ def test_decode_small_batch():
         o, l = O.sparse_mqa(qf, kvf, kvf[:, :512], g_idx[b][None], cfg.sm_scale)
         assert np.abs(got[b] - o[0]).max() <= ATOL_BF16, b
         assert np.allclose(lse[b].cpu().numpy(), l[0], atol=1e-3, rtol=1e-4)
+
+
+def test_decode_long_rows_selection():
+    """Decode over long caches (the sampled-threshold selection of long rows) equals the
+    stage entry points' selection of the same scores bit for bit, including sequences whose
+    query is all zero (every score ties: the sampled threshold brackets nothing and the
+    whole-row select runs) and short contexts (every key kept)."""
+    cfg = S.CONFIGS["decode_64x128k"].with_(L=40000, batch=12)
+    _say("[decode, long rows] B=12, n_k_max=40000")
+    inp = S.make_decode(cfg)
+    ctx_l = [40000, 39999, 20000, 16385, 2049, 2048, 1, 40000, 33333, 40000, 17000, 25000]
+    ctx = torch.tensor(ctx_l, dtype=torch.int32, device="cuda")
+    qi, qs, w = dev_u8(inp.qi), dev_f32(inp.q_scale), dev_f32(inp.w)
+    qi = qi.clone()
+    qi[7] = 0
+    qi[9] = 0
+    kc, kcs = dev_u8(inp.ki), dev_f32(inp.k_scale)
+    q, kvc = dev_bf16(inp.q), dev_bf16(inp.kv)
+    idx, out, lse = dsa.forward_decode(ctx, qi, qs, w, kc, kcs, q, kvc, cfg.k, cfg.sm_scale, cfg.d_v)
+    qpos = ctx - 1
+    scores = dsa.indexer(qi[:, None], qs[:, None], kc, kcs, w[:, None], q_pos=qpos)
+    ref_idx = dsa.topk(scores, cfg.k, q_pos=qpos)[:, 0]
+    torch.cuda.synchronize()
+    diff = (idx != ref_idx).any(dim=1).nonzero().flatten().tolist()
+    assert not diff, f"sequences {diff} differ"
+    g = idx.cpu().numpy()
+    assert np.array_equal(g[7], np.arange(cfg.k))      # all ties: the lowest indices
+    assert np.array_equal(g[6][:1], [0]) and np.all(g[6][1:] == -1)
+    assert np.array_equal(g[5], np.arange(2048))
