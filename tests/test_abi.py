@@ -141,6 +141,47 @@ def test_chunk_validation(L):
     assert call(**dict(f32, nq=70000, ws=FAKE, wsb=1 << 42)) == dsa.DSA_ERR_UNSUPPORTED
 
 
+def test_training_stage_validation(L):
+    # dsa_indexer_scores_at
+    sa = dict(qi=FAKE, qs=FAKE, ki=FAKE, ks=FAKE, w=FAKE, idx=FAKE, B=2, nq=64, nk=4096, H_I=64, d_I=128, k=2048,
+              dt=dsa.DSA_FP8_E4M3, sc=FAKE, st=None)
+    order = list(sa)
+    call = lambda **kw: L.dsa_indexer_scores_at(*[kw.get(n, sa[n]) for n in order])
+    assert call(idx=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(k=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H_I=32) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(ki=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG        # misaligned FP8 keys
+    assert call(dt=dsa.DSA_F32, H_I=2, d_I=32, nq=70000) == dsa.DSA_ERR_INVALID_ARG
+    # dsa_indexer_kl
+    kl = dict(q=FAKE, kv=FAKE, idx=FAKE, lse=FAKE, sc=FAKE, B=1, nq=64, nk=4096, H=128, dqk=576, k=2048, sm=0.04,
+              dt=dsa.DSA_BF16, out=FAKE, p=None, st=None)
+    order = list(kl)
+    call = lambda **kw: L.dsa_indexer_kl(*[kw.get(n, kl[n]) for n in order])
+    assert call(lse=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=100) == dsa.DSA_ERR_UNSUPPORTED               # bf16 path: k a multiple of 32
+    assert call(idx=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG        # bf16 path reads ids 16 bytes at a time
+    assert call(dt=dsa.DSA_FP8_E4M3) == dsa.DSA_ERR_UNSUPPORTED
+    # dsa_sparse_mla_backward
+    bw = dict(q=FAKE, kv=FAKE, v=None, idx=FAKE, out=FAKE, lse=FAKE, do=FAKE, B=1, nq=4096, nk=4096, H=128,
+              dqk=576, dv=512, k=2048, sm=0.04, dt=dsa.DSA_BF16, dq=FAKE, dkv=FAKE, dvo=None, ws=None, wsb=0,
+              st=None)
+    order = list(bw)
+    call = lambda **kw: L.dsa_sparse_mla_backward(*[kw.get(n, bw[n]) for n in order])
+    assert call(do=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(out=None) == dsa.DSA_ERR_INVALID_ARG            # bf16 path needs the forward output
+    assert call(v=FAKE) == dsa.DSA_ERR_UNSUPPORTED              # bf16 path: V inside kv
+    need = L.dsa_workspace_size(dsa.DSA_OP_MLA_BWD, 1, 4096, 4096, 128, 512, 2048, dsa.DSA_BF16)
+    assert need == 4096 * (576 * 128 + 512 * 128 + 2 * 2048 * 128) * 2
+    assert call() == dsa.DSA_ERR_WORKSPACE
+    assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG
+    assert call(nk=1 << 23, ws=FAKE, wsb=need) == dsa.DSA_ERR_UNSUPPORTED   # 32-bit dkv offsets
+    f32 = dict(dt=dsa.DSA_F32, H=4, dqk=64, dv=64, k=64, v=FAKE, out=None)
+    assert call(**f32) == dsa.DSA_ERR_INVALID_ARG                # separate V needs d_v_out
+    # passes of at most 4096 queries bound the workspace
+    assert L.dsa_workspace_size(dsa.DSA_OP_MLA_BWD, 1, 131072, 131072, 128, 512, 2048, dsa.DSA_BF16) == need
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
