@@ -15,7 +15,7 @@
 //   * keys are processed in chunks of 32 gathered rows.  The rows go straight from HBM to
 //     LDS with 16-byte direct loads (no staging registers; the latent half of a row is one
 //     wave-wide 1 KB load from a scalar address) into a ring of four buffers: while chunk c
-//     is finished, chunks c+2 and c+3 are in flight;
+//     is finished, chunk c+2 is in flight (a third chunk in flight measured slower);
 //   * per chunk, the logits of chunk c+1 are formed while the softmax of chunk c runs on
 //     the VALU between those MFMAs, then O^T += V^T P^T for chunk c;
 //   * after the softmax each lane already holds P^T in the B-operand layout of the PV
@@ -235,7 +235,7 @@ __device__ __forceinline__ v16f mla_logits(const v8bf* Qt, const uint8_t* buf) {
 // grid.x = n_q * n_split, grid.y = B.  One block of 4 waves per query (and key split);
 // wave w owns heads 32w .. 32w+31 over all 576 values (S^T) and all 512 output values
 // (O^T).  Pipeline over chunks of 32 selected rows, 4 LDS buffers: in the step of chunk
-// c, chunks c+2 and c+3 are in flight, the logits of chunk c+1 are formed while the
+// c, chunk c+2 is in flight, the logits of chunk c+1 are formed while the
 // softmax of chunk c runs, then O^T += V^T P^T for chunk c.
 __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
@@ -289,13 +289,12 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   uint8_t* bufs[NBUF] = {buf0, buf1, buf2, buf3};
   VMCNT(0);  // the Q^T operands are in registers before the chunk loads start
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < 2; ++j)
     if (j < n) gather_chunk(lds_addr(bufs[j]), kvb, ids, c_lo + j, nk, wv, l);
 
   v16f S_cur = {};
   if (n > 0) {
-    if (n >= 3) VMCNT(2 * LOADS_PER_CHUNK);
-    else if (n == 2) VMCNT(LOADS_PER_CHUNK);
+    if (n >= 2) VMCNT(LOADS_PER_CHUNK);
     else VMCNT(0);
     block_barrier();
     S_cur = mla_logits(Qt, buf0);
@@ -306,17 +305,17 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     for (int j = 0; j < NBUF; ++j) {
       const int c = base + j;
       if (c < n) {
-        // chunk c+1 has landed (every wave's loads), and chunk c-1's buffer is free
-        if (c + 2 < n) VMCNT(LOADS_PER_CHUNK);
-        else VMCNT(0);
+        // chunk c+1 has landed (every wave's loads; they are the only ones in flight), and
+        // chunk c-2's buffer is free
+        VMCNT(0);
         LGKM0();
         block_barrier();
-        // chunk c+3's loads go out one every four logit MFMAs (none past the last chunk)
-        const ChunkIds gi = chunk_ids(ids, c_lo + min(c + 3, n - 1), wv, l);
+        // chunk c+2's loads go out one every four logit MFMAs (none past the last chunk)
+        const ChunkIds gi = chunk_ids(ids, c_lo + min(c + 2, n - 1), wv, l);
         // (through a vector register and back, so that it is formed in scalar registers)
-        const uint32_t gon32 = __builtin_amdgcn_readfirstlane(opaque(c + 3 < n ? -1 : 0));
+        const uint32_t gon32 = __builtin_amdgcn_readfirstlane(opaque(c + 2 < n ? -1 : 0));
         const uint64_t gon = ((uint64_t)gon32 << 32) | gon32;
-        const uint32_t gbuf = lds_addr(bufs[(j + 3) % NBUF]);
+        const uint32_t gbuf = lds_addr(bufs[(j + 2) % NBUF]);
         // online softmax of chunk c (base 2, lazily rescaled) interleaved with the logits
         // of chunk c+1 (formed from a stale buffer on the last chunk, and then unused):
         // lane holds head l%32 and keys 8(r/4) + 4g + r%4 of S^T
