@@ -95,6 +95,22 @@ const char* dsa_status_string(int status) {
 
 const char* dsa_last_error(void) { return g_err; }
 
+// FP8 prefill selection: dense scores of a chunk of query rows into the workspace (rows of
+// dense_ld floats), ranked chunk by chunk.  A chunk spans up to 16384 rows (two waves of
+// 16-row blocks per CU) and its scores at most 8 GiB.
+static int64_t dense_ld(int64_t n_k) { return n_k > 0 ? (n_k + 63) / 64 * 64 : 64; }
+static int64_t dense_chunk_rows(int64_t n_rows, int64_t ld) {
+  int64_t rows = ((int64_t)8 << 30) / (ld * (int64_t)sizeof(float)) / 16 * 16;
+  rows = rows < 16384 ? rows : 16384;
+  rows = rows > 16 ? rows : 16;
+  const int64_t pad = dsa::dense_rows_pad(n_rows);
+  return rows < pad ? rows : pad;
+}
+static size_t dense_scores_bytes(int64_t n_rows, int64_t n_k) {
+  const int64_t ld = dense_ld(n_k);
+  return align256((size_t)dsa::dense_rows_pad(dense_chunk_rows(n_rows, ld)) * ld * sizeof(float));
+}
+
 size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_v,
                           int32_t k, int32_t dtype) {
   if (B <= 0 || n_q < 0 || n_k < 0 || H <= 0 || d_v <= 0 || k <= 0) return 0;
@@ -104,9 +120,9 @@ size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32
     case DSA_OP_PREFILL:
       if (dtype == DSA_F32)  // fp32 path ranks materialised scores
         return align256((size_t)n_q * n_k * sizeof(float)) + dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
-      return dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
+      return dense_scores_bytes(n_q, n_k) + dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
     case DSA_OP_SELECT:
-      return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : 0;
+      return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : dense_scores_bytes(n_q, n_k);
     case DSA_OP_DECODE:
       return align256(decode_scores_bytes(B, n_k)) + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
     case DSA_OP_MLA_BWD:
@@ -173,10 +189,26 @@ static int select_prefill(const void* q_idx, const float* q_scale, const void* k
                           const float* w, int64_t L, int32_t H_I, int32_t d_I, int32_t k, int32_t idx_dtype,
                           int32_t* idx, void* ws, size_t ws_bytes, hipStream_t s) {
   if (idx_dtype == DSA_FP8_E4M3) {
-    SUPPORT(k <= 2048, "fused selection keeps at most 2048 keys (k = %d)", k);
-    dsa::PrefillTopkArgs pa{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, 1, L, L,
-                            nullptr, k, idx};
-    return hip_status(dsa::launch_prefill_topk(pa, s), "prefill indexer/top-k launch");
+    // chunks of query rows: dense scores into the workspace, then the ordered row top-k
+    SUPPORT(k <= 2048, "FP8 selection keeps at most 2048 keys (k = %d)", k);
+    const int64_t ld = dense_ld(L);
+    const int64_t rows = dense_chunk_rows(L, ld);
+    const size_t need = dense_scores_bytes(L, L);
+    if (!ws || ws_bytes < need)
+      return fail(DSA_ERR_WORKSPACE, "FP8 selection needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+    float* scores = (float*)ws;
+    for (int64_t r0 = 0; r0 < L; r0 += rows) {
+      const int64_t n = rows < L - r0 ? rows : L - r0;
+      dsa::DenseIdxArgs da{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, 1, L, L,
+                           nullptr, r0, n, scores, ld};
+      int st = hip_status(dsa::launch_idx_dense(da, s), "prefill dense indexer launch");
+      if (st) return st;
+      dsa::TopkArgs ta{scores, ld, 1, n, L, nullptr, 0, r0, k, idx, dsa::dense_rows_pad(n), L, r0};
+      st = hip_status(dsa::launch_topk_ordered(ta, s), "prefill top-k launch");
+      if (st) return st;
+    }
+    return DSA_OK;
   }
   SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
   const size_t need = align256((size_t)L * L * sizeof(float));
@@ -222,7 +254,7 @@ int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_i
   SUPPORT(idx_dtype != DSA_FP8_E4M3 || k <= 2048, "fused selection keeps at most 2048 keys");
   const bool f32 = idx_dtype == DSA_F32;
   if (f32) SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
-  const size_t s_bytes = f32 ? align256((size_t)L * L * sizeof(float)) : 0;
+  const size_t s_bytes = f32 ? align256((size_t)L * L * sizeof(float)) : dense_scores_bytes(L, L);
   const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(1, L, H, d_v, k, attn_dtype);
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "dsa_forward_prefill needs %zu workspace bytes (got %zu)", need, ws_bytes);

@@ -32,8 +32,13 @@ struct TopkArgs {
   int64_t row_begin;
   int32_t k;
   int32_t* idx;
+  int64_t score_rows = 0;  // score rows per sequence (0: n_rows)
+  int64_t out_rows = 0;    // idx rows per sequence (0: n_rows); row i goes to idx row out_row0 + i
+  int64_t out_row0 = 0;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// the same selection by the ordered-candidate kernel (any row length up to TOPK_MAX_N, k <= 2048)
+hipError_t launch_topk_ordered(const TopkArgs& a, hipStream_t st);
 constexpr int64_t TOPK_MAX_N = 262144;
 
 struct MlaArgs {
@@ -70,6 +75,26 @@ struct PrefillTopkArgs {
   int32_t* idx;
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
+
+// dense FP8 index scores of rows row_begin .. row_begin + n_rows - 1 of each of B sequences
+// (row r of sequence b at position (q_pos ? q_pos[b] : 0) + r) into a padded workspace:
+// row i of sequence b at scores + (b * rows_pad + i) * ld, rows_pad = n_rows rounded up to
+// 16, ld a multiple of 64 covering the keys the rows see rounded up to 64; keys past a
+// row's position score -inf, columns past its last 64-key tile are not written.
+struct DenseIdxArgs {
+  const uint8_t* q8;
+  const float* qs;
+  const uint8_t* k8;
+  const float* ks;
+  const float* w;
+  int64_t B, n_q, n_k;
+  const int32_t* q_pos;
+  int64_t row_begin, n_rows;
+  float* scores;
+  int64_t ld;
+};
+inline int64_t dense_rows_pad(int64_t n_rows) { return (n_rows + 15) / 16 * 16; }
+hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st);
 
 // backward of the sparse attention; dkv (and dv when v is separate, fp32 path) are
 // zeroed and accumulated

@@ -1,0 +1,199 @@
+// Dense FP8 lightning-indexer scores of a block of query rows, written to a padded score
+// workspace that the row top-k then ranks (prefill selection).
+//
+// The score of query t and key s is the weighted sum over the 64 indexer heads of ReLU'd
+// FP8 dot products (53ai.com V3.2-Exp summary, section 创新架构; juhe.plus explainer,
+// section 第一步：Lightning Indexer), formed exactly as in indexer_tile.h so that every
+// kernel produces the same bits.  Only the grouping differs, chosen so that the matrix
+// cores do nearly all the work:
+//   * a block of 4 waves owns 16 consecutive query rows, 4 per wave, all 64 heads of each
+//     (the A operands of 16 FP8 MFMAs per 16-key fragment, 128 registers);
+//   * a 64-key tile is scored as 4 fragments.  Fragment f takes the tile's keys 4c + f
+//     (c = 0..15), so after the four fragments lane c of each lane group holds 4 adjacent
+//     keys and writes them with one 16-byte store;
+//   * the weighted head sums of the 4 rows run as two chains (one per head half) of four
+//     16x16x32 f16 MFMAs.  The A operand of row j carries that row's weights in output rows
+//     4j .. 4j+3 and zeros elsewhere, so lane group g ends the chain holding row g's sum;
+//     the zero rows add exact zeros, so each sum is the same single MFMA sum as in the
+//     other kernels;
+//   * key tiles (8 KB + 64 key scales) arrive by direct global->LDS loads into a ring of
+//     DN_SLOTS slots, DN_SLOTS-2 tiles ahead; one block barrier per tile.
+// Rows and columns of the workspace are padded (rows to 16 per block, columns to whole
+// 64-key tiles), so every store is in bounds and every wave issues exactly one store per
+// tile; the explicit load waits below count on that.
+#include "dsa_kernels.h"
+#include "indexer_tile.h"
+#include "lds_dma.h"
+
+namespace dsa {
+
+constexpr int DN_WAVES = 4;
+constexpr int DN_SLOTS = 6;
+constexpr int DN_TILE_BYTES = KEY_TILE * IDX_DIM;            // 8192
+constexpr int DN_SLOT_BYTES = DN_TILE_BYTES + KEY_TILE * 4;  // + the tile's key scales
+
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+
+// LDS layout of a tile: row rho (0..63) holds key 4 (rho % 16) + rho / 16 of the tile, its
+// 16-byte unit u stored at unit u ^ (rho & 7); the 64 key scales follow in key order.
+// Wave w loads rows 16w .. 16w+15 (two 1 KB direct loads); wave 3 also loads the scales.
+struct DenseDma {
+  uint32_t off[2];  // byte offset of this lane's unit within its key row, plus 128 * key
+};
+__device__ __forceinline__ DenseDma dense_dma_lane(int wv, int lane) {
+  DenseDma d;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rho = 16 * wv + 8 * i + (lane >> 3);
+    const int key = 4 * (rho & 15) + (rho >> 4);
+    d.off[i] = (uint32_t)(key * IDX_DIM + 16 * ((lane & 7) ^ (rho & 7)));
+  }
+  return d;
+}
+__device__ __forceinline__ void dense_tile_load(uint32_t slot, const uint8_t* __restrict__ kb,
+                                                const float* __restrict__ ksb, int64_t key0, int64_t n_k,
+                                                const DenseDma& d, int wv, int lane) {
+  // keys past n_k - 1 read row n_k - 1 (their scores are masked)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t key = key0 + (d.off[i] >> 7);
+    const int64_t kc = key < n_k ? key : n_k - 1;
+    dma16_all(kb + kc * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
+  }
+  if (wv == 3) {
+    const int64_t key = key0 + lane;
+    dma4_vaddr(ksb + (key < n_k ? key : n_k - 1), slot + DN_TILE_BYTES);
+  }
+}
+
+// B operand of fragment f: LDS rows 16f + c (keys 4c + f), contraction bytes 32g .. 32g+31.
+__device__ __forceinline__ v8i dense_fragment(const uint8_t* tile, int f, int lane) {
+  typedef __attribute__((address_space(3))) const v4i lds_v4i;
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  const int rho = 16 * f + (lane & 15);
+  const int g = lane >> 4;
+  const lds_u8* row = (lds_u8*)tile + rho * IDX_DIM;
+  const v4i lo = *(lds_v4i*)(row + 16 * ((2 * g) ^ (rho & 7)));
+  const v4i hi = *(lds_v4i*)(row + 16 * ((2 * g + 1) ^ (rho & 7)));
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// grid.x = B * n_grp (16-row groups, longest first within each sequence); 256 threads.
+// Row i (0 <= i < n_rows) of sequence b is query row row_begin + i, at position
+// (q_pos ? q_pos[b] : 0) + row_begin + i; its scores go to row b * 16 n_grp + i of
+// `scores` (ld floats apart, ld a multiple of 64 and at least the tiles the row needs).
+// Keys past the position (or past n_k - 1) score -inf.
+__global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
+    const float* __restrict__ ks, const float* __restrict__ w, int B, int64_t n_q, int64_t n_k,
+    const int32_t* __restrict__ q_pos, int64_t row_begin, int64_t n_rows, int64_t n_grp,
+    float* __restrict__ scores, int64_t ld) {
+  __shared__ __align__(16) uint8_t ring[DN_SLOTS * DN_SLOT_BYTES];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int b = (int)(blockIdx.x % B);
+  const int64_t grp = n_grp - 1 - (int64_t)(blockIdx.x / B);
+  const int64_t pos0 = (q_pos ? (int64_t)q_pos[b] : 0) + row_begin;
+  const int64_t i0 = 16 * grp;
+  const int64_t i_last = i0 + 15 < n_rows ? i0 + 15 : n_rows - 1;
+  int64_t n_vis = pos0 + i_last + 1;
+  n_vis = n_vis < n_k ? n_vis : n_k;
+  n_vis = n_vis > 0 ? n_vis : 0;
+  const int ntiles = (int)((n_vis + KEY_TILE - 1) / KEY_TILE);
+
+  const uint8_t* kb = k8 + (size_t)b * n_k * IDX_DIM;
+  const float* ksb = ks + (size_t)b * n_k;
+  const uint32_t ring0 = lds_addr(ring);
+  const DenseDma dl = dense_dma_lane(wv, lane);
+#pragma unroll
+  for (int t = 0; t < DN_SLOTS - 1; ++t)
+    if (t < ntiles) dense_tile_load(ring0 + t * DN_SLOT_BYTES, kb, ksb, (int64_t)t * KEY_TILE, n_k, dl, wv, lane);
+
+  // this wave's rows i0 + 4wv + j; padding rows score the last real row
+  const int g = lane >> 4, c = lane & 15, rq = c >> 2;
+  v8i A[4][4];
+  v8h_t W[2][4];
+  float cmx = 0.f;
+  int64_t lim = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = i0 + 4 * wv + j;
+    const int64_t qrow = (int64_t)b * n_q + row_begin + (i < n_rows ? i : n_rows - 1);
+    const uint8_t* qr = q8 + qrow * IDX_HEADS * IDX_DIM;
+    const float* qsr = qs + qrow * IDX_HEADS;
+    const float* wr = w + qrow * IDX_HEADS;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const v4i* p = reinterpret_cast<const v4i*>(qr + (16 * hb + c) * IDX_DIM + 32 * g);
+      const v4i lo = p[0], hi = p[1];
+      A[j][hb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    const float cm = row_cmax(qsr, wr);
+    const float inv = cm > 0.f ? 1.f / cm : 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int h = 32 * hh + 16 * (e >> 2) + 4 * g + (e & 3);
+        W[hh][j][e] = rq == j ? head_weight_f16(wr[h], qsr[h], inv) : (_Float16)0.f;
+      }
+    if (g == j) {
+      cmx = __fmul_rn(cm, UNSCALE);
+      const int64_t p = pos0 + i;
+      lim = p < n_k - 1 ? p : n_k - 1;
+    }
+  }
+  float* srow = scores + ((int64_t)b * 16 * n_grp + i0 + 4 * wv + g) * ld + 4 * c;
+
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t has landed once at most the loads of tiles t+1 .. t+DN_SLOTS-2 and the stores
+    // of tiles t-DN_SLOTS+1 .. t-1 are outstanding (vector-memory operations complete in
+    // issue order); outside the steady state wait for everything
+    if (t >= DN_SLOTS - 1 && t + DN_SLOTS - 2 < ntiles) {
+      if (wv == 3) VMCNT(3 * (DN_SLOTS - 2) + DN_SLOTS - 1);
+      else VMCNT(2 * (DN_SLOTS - 2) + DN_SLOTS - 1);
+    } else {
+      VMCNT(0);
+    }
+    LGKM0();
+    block_barrier();
+    if (t + DN_SLOTS - 1 < ntiles)  // into the slot of tile t-1, which every wave is done with
+      dense_tile_load(ring0 + ((t + DN_SLOTS - 1) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb,
+                      (int64_t)(t + DN_SLOTS - 1) * KEY_TILE, n_k, dl, wv, lane);
+    const uint8_t* tile = ring + (t % DN_SLOTS) * DN_SLOT_BYTES;
+    float v[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const v8i bf = dense_fragment(tile, f, lane);
+      v4f d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4f x0 = mfma_fp8_scaled(A[j][0], bf);
+        const v4f x1 = mfma_fp8_scaled(A[j][1], bf);
+        const v4f x2 = mfma_fp8_scaled(A[j][2], bf);
+        const v4f x3 = mfma_fp8_scaled(A[j][3], bf);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(W[0][j], relu_pack(x0, x1), d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(W[1][j], relu_pack(x2, x3), d1, 0, 0, 0);
+      }
+      v[f] = __fadd_rn(d0[0], d1[0]);
+    }
+    typedef __attribute__((address_space(3))) const v4f lds_v4f;
+    const v4f kscale = *(lds_v4f*)((__attribute__((address_space(3))) const uint8_t*)tile + DN_TILE_BYTES + 16 * c);
+    const int64_t key = (int64_t)t * KEY_TILE + 4 * c;
+    v4f o;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      o[f] = key + f <= lim ? __fmul_rn(__fmul_rn(v[f], cmx), kscale[f]) : -INFINITY;
+    *reinterpret_cast<v4f*>(srow + (int64_t)t * KEY_TILE) = o;
+  }
+}
+
+hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st) {
+  const int64_t n_grp = (a.n_rows + 15) / 16;
+  if (n_grp <= 0) return hipSuccess;
+  hipLaunchKernelGGL(idx_dense_fp8_kernel, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8, a.qs,
+                     a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp, a.scores,
+                     a.ld);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -62,6 +62,15 @@ __device__ __forceinline__ float row_cmax(const float* __restrict__ qs, const fl
   return m;
 }
 
+// f16 head weight (w * q_scale) / max|c|: rounded to fp32, then to f16.  The empty asm keeps
+// the compiler from fusing the two roundings into one mixed-precision FMA (which rounds
+// differently now and then, and every kernel must produce the same weights).
+__device__ __forceinline__ _Float16 head_weight_f16(float w, float qs, float inv) {
+  float p = __fmul_rn(__fmul_rn(w, qs), inv);
+  asm volatile("" : "+v"(p));
+  return (_Float16)p;
+}
+
 __device__ __forceinline__ void load_idx_half(IdxHalf& Q, const uint8_t* __restrict__ q8,
                                               const float* __restrict__ qs, const float* __restrict__ w,
                                               int hh, float cmax) {
@@ -79,7 +88,7 @@ __device__ __forceinline__ void load_idx_half(IdxHalf& Q, const uint8_t* __restr
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int h = 32 * hh + 16 * (e >> 2) + 4 * g + (e & 3);
-    Q.wa[e] = (_Float16)__fmul_rn(__fmul_rn(w[h], qs[h]), inv);
+    Q.wa[e] = head_weight_f16(w[h], qs[h], inv);
   }
 }
 

@@ -6,6 +6,7 @@
 #pragma once
 
 #include "dsa_device.h"
+#include "lds_dma.h"
 
 namespace dsa {
 
@@ -32,8 +33,6 @@ constexpr float LN2 = 0.6931471805599453f;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-#define VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-#define LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 // D = A(32x16 bf16) * B(16x32 bf16) + C, fp32.  Lane l: row (A) / column (B) l%32,
 // contraction elements 8*(l/32) .. +7; C/D: column l%32, register r holds row
@@ -53,54 +52,6 @@ __device__ __forceinline__ int opaque(int x) {
 __device__ __forceinline__ uint32_t safe_row(int32_t s, uint32_t n_k) {
   return (uint32_t)s < n_k ? (uint32_t)s : 0u;
 }
-// Workgroup barrier that is also a compiler memory barrier (LDS accesses stay on their side),
-// with no wait-counter drain: the chunk loads stay in flight across it.
-__device__ __forceinline__ void block_barrier() {
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" : : : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-// One direct global->LDS load of 16 bytes per lane: lane i's bytes go to LDS address
-// lds + 16 i.  Issued from inline asm, so the compiler's wait-counter model does not see
-// it: the chunk ring is ordered by explicit vector-memory waits and barriers instead, and
-// the LDS reads of the logits keep exact LDS-counter waits (a direct load the compiler can
-// see would force every LDS wait behind it to zero).  No register is written; one wait
-// state separates the M0 write from the load that reads it.  M0 holds nothing else in
-// this file's kernels, so clobbering it is safe.  The exec mask is narrowed for the load
-// and restored; the AND sets SCC, which is therefore clobbered too.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16_saddr(const void* gbase, uint32_t voff, uint32_t lds, uint64_t on) {
-  uint64_t sv;
-  asm volatile(
-      "s_mov_b64 %0, exec\n\t"
-      "s_and_b64 exec, exec, %1\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %4\n\t"
-      "s_mov_b64 exec, %0"
-      : "=&s"(sv)
-      : "s"(on), "s"(lds), "v"(voff), "s"(gbase)
-      : "memory", "m0", "scc");
-}
-__device__ __forceinline__ void dma16_vaddr(const void* gaddr, uint32_t lds, uint64_t on) {
-  uint64_t sv;
-  asm volatile(
-      "s_mov_b64 %0, exec\n\t"
-      "s_and_b64 exec, exec, %1\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, off\n\t"
-      "s_mov_b64 exec, %0"
-      : "=&s"(sv)
-      : "s"(on), "s"(lds), "v"(gaddr)
-      : "memory", "m0", "scc");
-}
-#pragma clang diagnostic pop
 
 // The ids of this wave's eight rows of one chunk (read ahead of the loads that use them).
 struct ChunkIds {

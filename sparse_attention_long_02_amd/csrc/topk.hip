@@ -316,6 +316,236 @@ __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
   write_kept<TL_THREADS>(sel, tie, n, rem, k, out, wtot);
 }
 
+// ---------------------------------------------------------------------------------------
+// Ordered-candidate top-k (rows of any length, k <= TO_CAP / 2).  One 512-thread block per
+// row and about 33 KB of LDS, so four blocks share a CU and keep 128 KB of score loads in
+// flight:
+//   1. a threshold T: a row of at most TO_CAP keys takes every key; a longer row takes the
+//      sample key of rank about 1.5 k * TO_CAP / n among TO_CAP evenly spaced samples, so
+//      that about 1.5 k keys exceed it;
+//   2. one pass over the row collects the keys > T, with their positions, in ascending
+//      position order: each thread reads TO_PER consecutive scores and a block scan of the
+//      per-thread counts places them;
+//   3. if at least k and at most TO_CAP keys exceed T, the k-th largest key v* and every
+//      key equal to it are among the candidates: a radix select over the candidates gives
+//      v* and how many keys equal to v* are kept (the lowest positions), and an ordered
+//      pass over the candidates writes the kept positions ascending;
+//   4. otherwise (an unlucky sample, heavy ties) the exact select runs over the whole row
+//      and the ordered pass runs over the row itself.
+// The result is the full-sort definition either way.
+// ---------------------------------------------------------------------------------------
+constexpr int TO_THREADS = 512;
+constexpr int TO_CAP = 4096;
+constexpr int TO_PER = 8;
+constexpr int TO_STEP = TO_THREADS * TO_PER;
+
+// scores p0 .. p0+TO_PER-1 of a row (positions >= n read as -inf and are never taken)
+__device__ __forceinline__ void load_run(const float* __restrict__ srow, int64_t p0, int64_t n, bool vec,
+                                         float v[TO_PER]) {
+  if (vec && p0 + TO_PER <= n) {
+    const float4* p = reinterpret_cast<const float4*>(srow + p0);
+#pragma unroll
+    for (int q = 0; q < TO_PER / 4; ++q) {
+      const float4 x = p[q];
+      v[4 * q] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < TO_PER; ++e) v[e] = p0 + e < n ? srow[p0 + e] : -INFINITY;
+  }
+}
+
+// Keys > T (every key if `all`) in ascending position order into ckey/cpos (slots past
+// TO_CAP are counted, not stored).  Returns the count.
+__device__ uint32_t collect_ordered(const float* __restrict__ srow, int64_t n, bool vec, bool all, uint32_t T,
+                                    uint32_t* ckey, int32_t* cpos, uint32_t* wtot) {
+  const int tid = threadIdx.x;
+  uint32_t nc = 0;
+  for (int64_t s0 = 0; s0 < n; s0 += TO_STEP) {
+    const int64_t p0 = s0 + (int64_t)TO_PER * tid;
+    float v[TO_PER];
+    load_run(srow, p0, n, vec, v);
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < TO_PER; ++e) m |= (uint32_t)((p0 + e < n) & (all | (score_key(v[e]) > T))) << e;
+    uint32_t tot;
+    uint32_t slot = nc + block_excl_scan<TO_THREADS>((uint32_t)__popc(m), wtot, tot);
+#pragma unroll
+    for (int e = 0; e < TO_PER; ++e)
+      if ((m >> e) & 1u) {
+        if (slot < (uint32_t)TO_CAP) {
+          ckey[slot] = score_key(v[e]);
+          cpos[slot] = (int32_t)(p0 + e);
+        }
+        ++slot;
+      }
+    nc += tot;
+  }
+  __syncthreads();
+  return nc;
+}
+
+// Kept candidates (keys > v*, then the first `rem` keys equal to v* in position order)
+// written ascending to out, -1 padded to k.
+__device__ void write_from_candidates(const uint32_t* ckey, const int32_t* cpos, uint32_t nc, uint32_t vstar,
+                                      uint32_t rem, int k, int32_t* __restrict__ out, uint32_t* wtot) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t m = (nc + TO_THREADS - 1) / TO_THREADS;
+  const uint32_t j0 = min(tid * m, nc), j1 = min(j0 + m, nc);
+  uint32_t ties = 0;
+  for (uint32_t j = j0; j < j1; ++j) ties += ckey[j] == vstar;
+  uint32_t tt;
+  const uint32_t tb = block_excl_scan<TO_THREADS>(ties, wtot, tt);
+  uint32_t kc = 0, tr = tb;
+  for (uint32_t j = j0; j < j1; ++j) {
+    const uint32_t u = ckey[j];
+    kc += (u > vstar) | ((u == vstar) & (tr < rem));
+    tr += u == vstar;
+  }
+  uint32_t tot;
+  uint32_t o = block_excl_scan<TO_THREADS>(kc, wtot, tot);
+  tr = tb;
+  for (uint32_t j = j0; j < j1; ++j) {
+    const uint32_t u = ckey[j];
+    const bool keep = (u > vstar) | ((u == vstar) & (tr < rem));
+    tr += u == vstar;
+    if (keep) {
+      if (o < (uint32_t)k) out[o] = cpos[j];
+      ++o;
+    }
+  }
+  for (int64_t j = (int64_t)tot + tid; j < k; j += TO_THREADS) out[j] = -1;
+}
+
+// Exact radix select of the k-th largest key of a whole row (8-bit digits, four passes).
+__device__ uint32_t select_row8(const float* __restrict__ srow, int64_t n, bool vec, int k, uint32_t* hist,
+                                uint32_t* wtot, uint32_t* s_digit, uint32_t* s_above, uint32_t& rem) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  rem = (uint32_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int j = tid; j < 256; j += TO_THREADS) hist[j] = 0;
+    __syncthreads();
+    for (int64_t s0 = 0; s0 < n; s0 += TO_STEP) {
+      const int64_t p0 = s0 + (int64_t)TO_PER * tid;
+      float v[TO_PER];
+      load_run(srow, p0, n, vec, v);
+#pragma unroll
+      for (int e = 0; e < TO_PER; ++e) {
+        const uint32_t u = score_key(v[e]);
+        if ((p0 + e < n) && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t above;
+    const uint32_t d = pick_digit<TO_THREADS>(hist, 256, rem, wtot, s_digit, s_above, above);
+    rem -= above;
+    prefix |= d << shift;
+    pmask |= 255u << shift;
+  }
+  return prefix;
+}
+
+// The kept keys of a whole row (keys > v*, then the first `rem` equal to v*) written ascending.
+__device__ void write_from_row(const float* __restrict__ srow, int64_t n, bool vec, uint32_t vstar, uint32_t rem,
+                               int k, int32_t* __restrict__ out, uint32_t* wtot) {
+  const int tid = threadIdx.x;
+  uint32_t o_base = 0, t_base = 0;
+  for (int64_t s0 = 0; s0 < n; s0 += TO_STEP) {
+    const int64_t p0 = s0 + (int64_t)TO_PER * tid;
+    float v[TO_PER];
+    load_run(srow, p0, n, vec, v);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < TO_PER; ++e) {
+      const uint32_t u = score_key(v[e]);
+      const bool in = p0 + e < n;
+      gt |= (uint32_t)(in & (u > vstar)) << e;
+      eq |= (uint32_t)(in & (u == vstar)) << e;
+    }
+    uint32_t tt;
+    const uint32_t tb = t_base + block_excl_scan<TO_THREADS>((uint32_t)__popc(eq), wtot, tt);
+    // ties of this thread that are still within the first `rem`
+    const uint32_t take = tb < rem ? min((uint32_t)__popc(eq), rem - tb) : 0u;
+    uint32_t keep = gt, left = take;
+#pragma unroll
+    for (int e = 0; e < TO_PER; ++e)
+      if (((eq >> e) & 1u) && left) {
+        keep |= 1u << e;
+        --left;
+      }
+    uint32_t tot;
+    uint32_t o = o_base + block_excl_scan<TO_THREADS>((uint32_t)__popc(keep), wtot, tot);
+#pragma unroll
+    for (int e = 0; e < TO_PER; ++e)
+      if ((keep >> e) & 1u) {
+        if (o < (uint32_t)k) out[o] = (int32_t)(p0 + e);
+        ++o;
+      }
+    o_base += tot;
+    t_base += tt;
+  }
+  for (int64_t j = (int64_t)o_base + tid; j < k; j += TO_THREADS) out[j] = -1;
+}
+
+// grid (n_rows, B), longest rows first.  Row i of sequence b: scores at
+// scores + (b * score_rows + i) * ld, position q_pos[b] + pos_offset + row_begin + i, output
+// row out_row0 + i of sequence b's out_rows rows.
+__global__ __launch_bounds__(TO_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void topk_ordered_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t score_rows, int64_t n_rows, int64_t n_k,
+    const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int k, int32_t* __restrict__ idx,
+    int64_t out_rows, int64_t out_row0) {
+  __shared__ uint32_t ckey[TO_CAP];  // samples first, then candidate keys
+  __shared__ int32_t cpos[TO_CAP];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wtot[TO_THREADS / WAVE];
+  __shared__ uint32_t s_digit, s_above;
+  const int64_t i = n_rows - 1 - (int64_t)blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + row_begin + i;
+  int64_t n = pos + 1 < n_k ? pos + 1 : n_k;
+  n = n > 0 ? n : 0;
+  const float* srow = scores + ((int64_t)b * score_rows + i) * ld;
+  int32_t* out = idx + ((int64_t)b * out_rows + out_row0 + i) * k;
+  const int tid = threadIdx.x;
+  if (n <= k) {  // every visible key is kept
+    for (int j = tid; j < k; j += TO_THREADS) out[j] = j < n ? j : -1;
+    return;
+  }
+  const bool vec = ((uintptr_t)srow & 15u) == 0;
+  const bool all = n <= TO_CAP;
+  uint32_t T = 0;
+  if (!all) {
+    for (int j = tid; j < TO_CAP; j += TO_THREADS) ckey[j] = score_key(srow[((int64_t)j * n) / TO_CAP]);
+    __syncthreads();
+    int64_t srank = (3 * (int64_t)k * TO_CAP + n) / (2 * n);  // about 1.5 k keys above
+    srank = srank < 1 ? 1 : srank > TO_CAP ? TO_CAP : srank;
+    uint32_t srem;
+    T = select_lds<TO_THREADS>(ckey, TO_CAP, (uint32_t)srank, hist, wtot, &s_digit, &s_above, srem);
+  }
+  const uint32_t nc = collect_ordered(srow, n, vec, all, T, ckey, cpos, wtot);
+  uint32_t vstar, rem;
+  if (nc >= (uint32_t)k && nc <= (uint32_t)TO_CAP) {
+    vstar = select_lds<TO_THREADS>(ckey, (int)nc, (uint32_t)k, hist, wtot, &s_digit, &s_above, rem);
+    write_from_candidates(ckey, cpos, nc, vstar, rem, k, out, wtot);
+  } else {
+    vstar = select_row8(srow, n, vec, k, hist, wtot, &s_digit, &s_above, rem);
+    write_from_row(srow, n, vec, vstar, rem, k, out, wtot);
+  }
+}
+
+hipError_t launch_topk_ordered(const TopkArgs& a, hipStream_t st) {
+  if (a.n_rows <= 0 || a.B <= 0) return hipSuccess;
+  dim3 grid((unsigned)a.n_rows, (unsigned)a.B);
+  hipLaunchKernelGGL(topk_ordered_kernel, grid, dim3(TO_THREADS), 0, st, a.scores, a.ld_scores,
+                     a.score_rows ? a.score_rows : a.n_rows, a.n_rows, a.n_k, a.q_pos, a.pos_offset, a.row_begin,
+                     a.k, a.idx, a.out_rows ? a.out_rows : a.n_rows, a.out_row0);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   dim3 grid((unsigned)a.n_rows, (unsigned)a.B);
   if (a.n_k >= TL_MIN_N && a.k <= TL_CAP / 4)
