@@ -178,9 +178,16 @@ int dsa_sparse_mla_backward(const void* q, const void* kv, const void* v, const 
 
 /*
  * dsa_select_prefill -- stages 1 and 2 for one sequence of L tokens (query t at position
- * t): lightning-indexer scores feed a per-row streaming top-k on chip, so the L x L
- * score matrix is never stored (FP8 path).  The fp32 path ranks a materialised score
- * matrix held in the workspace.
+ * t).  FP8 path: the L x L score matrix is never stored.  Each row's scores are compared
+ * on chip with a threshold set from that row's scores at every 32nd key, and only the keys
+ * above it (about 1.7 k per row) are written, to a candidate list whose top-k is the
+ * row's selection.  A row whose list cannot decide it (fewer than k keys above the
+ * threshold, or more than the list holds: heavy ties, adversarial keys) is selected again
+ * by a streaming top-k fused with the indexer.  The result is the full-sort definition in
+ * every case.  The workspace holds the per-row sample scores and candidate lists of one
+ * chunk of up to 16384 rows at a time (about 1 GiB at L = 131072); for L > 262144 the
+ * streaming kernel selects every row and no workspace is needed.  The fp32 path ranks a
+ * materialised score matrix held in the workspace.
  *
  *   q_idx [L, H_I, d_I], q_scale [L, H_I], k_idx [L, d_I], k_scale [L], w [L, H_I]
  *   idx   [L, k] int32 output, ascending, -1 padded
@@ -194,8 +201,8 @@ int dsa_select_prefill(const void* q_idx, const float* q_scale, const void* k_id
 
 /*
  * dsa_forward_prefill -- the whole layer for one sequence of L tokens, query t at
- * position t: indexer -> top-k -> sparse attention.  The L x L score matrix is never
- * stored: the indexer feeds a per-row streaming top-k on chip.
+ * position t: indexer -> top-k -> sparse attention.  The selection is dsa_select_prefill's
+ * (the L x L score matrix is never stored).
  *
  *   q_idx [L, H_I, d_I], q_scale [L, H_I], k_idx [L, d_I], k_scale [L], w [L, H_I]
  *   q [L, H, d_qk], kv [L, d_qk], v [L, d_v] or NULL

@@ -68,13 +68,88 @@ size_t decode_scores_bytes(int64_t B, int64_t n_k) { return (size_t)B * n_k * si
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// the fp32 chunk path ranks materialised scores; the FP8 path selects on chip
-size_t chunk_scores_bytes(int64_t B, int64_t n_q, int64_t n_k, int32_t attn_dtype) {
-  return attn_dtype == DSA_F32 ? align256((size_t)B * n_q * n_k * sizeof(float)) : 0;
-}
 
 // largest key count of the fused selection (32-bit byte offsets within a sequence's keys)
 constexpr int64_t FUSED_MAX_KEYS = ((int64_t)1 << 25) - 1;
+
+// FP8 selection by threshold filtering (see topk.hip): per chunk of query rows (up to 16384
+// rows over all sequences), a 1-in-SEL_SAMPLE_STRIDE key sample of every row's scores, each row's
+// threshold from its sample, the filtering indexer's candidate lists, and the top-k of each
+// list; then the streaming exact selection for the rows whose list did not decide them.
+// Workspace: the per-row redo bytes of all rows, then one chunk's thresholds, counts,
+// sample rows and candidate lists (about 1 GiB for 16384 rows of 128K keys).
+struct SelWs {
+  uint8_t* redo;
+  float* thr;
+  uint32_t* cnt;
+  float* samp;
+  uint2* cand;
+};
+static int64_t sel_chunk_rows(int64_t B, int64_t n_rows) {
+  const int64_t pad = dsa::dense_rows_pad(n_rows);
+  int64_t rows = 16384 / B / 16 * 16;
+  rows = rows > 16 ? rows : 16;
+  return pad < rows ? pad : rows;
+}
+static size_t sel_ws_bytes(int64_t B, int64_t n_q, int64_t n_k, SelWs* ws_out = nullptr, void* base = nullptr) {
+  const int64_t rp = sel_chunk_rows(B, n_q);
+  const size_t o_thr = align256((size_t)B * n_q);
+  const size_t o_cnt = o_thr + align256((size_t)B * rp * 4);
+  const size_t o_samp = o_cnt + align256((size_t)B * rp * 4);
+  const size_t o_cand = o_samp + align256((size_t)B * rp * dsa::sel_sample_ld(n_k) * sizeof(float));
+  const size_t total = o_cand + align256((size_t)B * rp * dsa::SEL_CAND_PITCH * sizeof(uint2));
+  if (ws_out) {
+    char* p = (char*)base;
+    *ws_out = SelWs{(uint8_t*)p, (float*)(p + o_thr), (uint32_t*)(p + o_cnt), (float*)(p + o_samp),
+                    (uint2*)(p + o_cand)};
+  }
+  return total;
+}
+// the filtered path covers keys up to TOPK_MAX_N (its sample select runs in LDS); longer
+// contexts use the streaming exact selection alone, which needs no workspace
+static bool sel_filtered(int64_t n_k) { return n_k <= dsa::TOPK_MAX_N; }
+static size_t sel_bytes(int64_t B, int64_t n_q, int64_t n_k) {
+  return sel_filtered(n_k) ? sel_ws_bytes(B, n_q, n_k) : 0;
+}
+
+// rows 0 .. n_q - 1 of each of B sequences (row r at position (q_pos ? q_pos[b] : 0) + r)
+static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks, const float* w,
+                      int64_t B, int64_t n_q, int64_t n_k, const int32_t* q_pos, int32_t k, int32_t* idx, void* ws,
+                      size_t ws_bytes, hipStream_t s) {
+  SUPPORT(n_k <= FUSED_MAX_KEYS, "FP8 selection supports up to %lld keys", (long long)FUSED_MAX_KEYS);
+  dsa::PrefillTopkArgs pa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, k, idx};
+  if (!sel_filtered(n_k)) return hip_status(dsa::launch_prefill_topk(pa, s), "indexer/top-k launch");
+  SelWs sw;
+  const size_t need = sel_ws_bytes(B, n_q, n_k, &sw, ws);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "FP8 selection needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  const int64_t rows = sel_chunk_rows(B, n_q);
+  const int64_t ld_s = dsa::sel_sample_ld(n_k);
+  for (int64_t r0 = 0; r0 < n_q; r0 += rows) {
+    const int64_t n = rows < n_q - r0 ? rows : n_q - r0;
+    const int64_t rp = dsa::dense_rows_pad(n);
+    dsa::DenseIdxArgs sa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, sw.samp, ld_s, dsa::SEL_SAMPLE_STRIDE};
+    int st = hip_status(dsa::launch_idx_dense(sa, s), "key-sample indexer launch");
+    if (st) return st;
+    dsa::SelThresholdArgs ta{sw.samp, ld_s, rp, B, n, n_k, q_pos, r0, k, sw.thr};
+    st = hip_status(dsa::launch_sel_threshold(ta, s), "threshold launch");
+    if (st) return st;
+    dsa::DenseIdxArgs fa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, nullptr, 0, 1, sw.thr, sw.cand, sw.cnt};
+    st = hip_status(dsa::launch_idx_dense(fa, s), "filtering indexer launch");
+    if (st) return st;
+    dsa::SelCandArgs ca{sw.cand, sw.cnt, rp, B, n, n_k, q_pos, r0, k, idx, n_q, r0, sw.redo};
+    st = hip_status(dsa::launch_sel_candidates(ca, s), "candidate top-k launch");
+    if (st) return st;
+  }
+  pa.redo = sw.redo;
+  return hip_status(dsa::launch_prefill_topk(pa, s), "exact selection of the remaining rows");
+}
+
+// the fp32 chunk path ranks materialised scores; the FP8 path filters on chip
+size_t chunk_scores_bytes(int64_t B, int64_t n_q, int64_t n_k, int32_t attn_dtype) {
+  return attn_dtype == DSA_F32 ? align256((size_t)B * n_q * n_k * sizeof(float)) : sel_bytes(B, n_q, n_k);
+}
 
 }  // namespace
 
@@ -95,22 +170,6 @@ const char* dsa_status_string(int status) {
 
 const char* dsa_last_error(void) { return g_err; }
 
-// FP8 prefill selection: dense scores of a chunk of query rows into the workspace (rows of
-// dense_ld floats), ranked chunk by chunk.  A chunk spans up to 16384 rows (two waves of
-// 16-row blocks per CU) and its scores at most 8 GiB.
-static int64_t dense_ld(int64_t n_k) { return n_k > 0 ? (n_k + 63) / 64 * 64 : 64; }
-static int64_t dense_chunk_rows(int64_t n_rows, int64_t ld) {
-  int64_t rows = ((int64_t)8 << 30) / (ld * (int64_t)sizeof(float)) / 16 * 16;
-  rows = rows < 16384 ? rows : 16384;
-  rows = rows > 16 ? rows : 16;
-  const int64_t pad = dsa::dense_rows_pad(n_rows);
-  return rows < pad ? rows : pad;
-}
-static size_t dense_scores_bytes(int64_t n_rows, int64_t n_k) {
-  const int64_t ld = dense_ld(n_k);
-  return align256((size_t)dsa::dense_rows_pad(dense_chunk_rows(n_rows, ld)) * ld * sizeof(float));
-}
-
 size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_v,
                           int32_t k, int32_t dtype) {
   if (B <= 0 || n_q < 0 || n_k < 0 || H <= 0 || d_v <= 0 || k <= 0) return 0;
@@ -120,9 +179,9 @@ size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32
     case DSA_OP_PREFILL:
       if (dtype == DSA_F32)  // fp32 path ranks materialised scores
         return align256((size_t)n_q * n_k * sizeof(float)) + dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
-      return dense_scores_bytes(n_q, n_k) + dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
+      return sel_bytes(1, n_q, n_k) + dsa::sparse_mla_ws_bytes(1, n_q, H, d_v, k, dtype);
     case DSA_OP_SELECT:
-      return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : dense_scores_bytes(n_q, n_k);
+      return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : sel_bytes(1, n_q, n_k);
     case DSA_OP_DECODE:
       return align256(decode_scores_bytes(B, n_k)) + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
     case DSA_OP_MLA_BWD:
@@ -189,26 +248,9 @@ static int select_prefill(const void* q_idx, const float* q_scale, const void* k
                           const float* w, int64_t L, int32_t H_I, int32_t d_I, int32_t k, int32_t idx_dtype,
                           int32_t* idx, void* ws, size_t ws_bytes, hipStream_t s) {
   if (idx_dtype == DSA_FP8_E4M3) {
-    // chunks of query rows: dense scores into the workspace, then the ordered row top-k
     SUPPORT(k <= 2048, "FP8 selection keeps at most 2048 keys (k = %d)", k);
-    const int64_t ld = dense_ld(L);
-    const int64_t rows = dense_chunk_rows(L, ld);
-    const size_t need = dense_scores_bytes(L, L);
-    if (!ws || ws_bytes < need)
-      return fail(DSA_ERR_WORKSPACE, "FP8 selection needs %zu workspace bytes (got %zu)", need, ws_bytes);
-    REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
-    float* scores = (float*)ws;
-    for (int64_t r0 = 0; r0 < L; r0 += rows) {
-      const int64_t n = rows < L - r0 ? rows : L - r0;
-      dsa::DenseIdxArgs da{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, 1, L, L,
-                           nullptr, r0, n, scores, ld};
-      int st = hip_status(dsa::launch_idx_dense(da, s), "prefill dense indexer launch");
-      if (st) return st;
-      dsa::TopkArgs ta{scores, ld, 1, n, L, nullptr, 0, r0, k, idx, dsa::dense_rows_pad(n), L, r0};
-      st = hip_status(dsa::launch_topk_ordered(ta, s), "prefill top-k launch");
-      if (st) return st;
-    }
-    return DSA_OK;
+    return select_fp8((const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, 1, L, L, nullptr, k, idx,
+                      ws, ws_bytes, s);
   }
   SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
   const size_t need = align256((size_t)L * L * sizeof(float));
@@ -254,7 +296,7 @@ int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_i
   SUPPORT(idx_dtype != DSA_FP8_E4M3 || k <= 2048, "fused selection keeps at most 2048 keys");
   const bool f32 = idx_dtype == DSA_F32;
   if (f32) SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
-  const size_t s_bytes = f32 ? align256((size_t)L * L * sizeof(float)) : dense_scores_bytes(L, L);
+  const size_t s_bytes = f32 ? align256((size_t)L * L * sizeof(float)) : sel_bytes(1, L, L);
   const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(1, L, H, d_v, k, attn_dtype);
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "dsa_forward_prefill needs %zu workspace bytes (got %zu)", need, ws_bytes);
@@ -356,9 +398,8 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
   if (need) REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   if (idx_dtype == DSA_FP8_E4M3) {
-    dsa::PrefillTopkArgs pa{(const uint8_t*)q_idx, q_scale, (const uint8_t*)k_cache, k_cache_scale, w,
-                            B, n_q, n_k_max, q_pos, k, idx};
-    st = hip_status(dsa::launch_prefill_topk(pa, s), "chunk indexer/top-k launch");
+    st = select_fp8((const uint8_t*)q_idx, q_scale, (const uint8_t*)k_cache, k_cache_scale, w, B, n_q, n_k_max,
+                    q_pos, k, idx, ws, s_bytes, s);
   } else {
     float* scores = (float*)ws;
     dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, n_q, n_k_max, q_pos, 0, H_I, d_I,

@@ -37,8 +37,6 @@ struct TopkArgs {
   int64_t out_row0 = 0;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-// the same selection by the ordered-candidate kernel (any row length up to TOPK_MAX_N, k <= 2048)
-hipError_t launch_topk_ordered(const TopkArgs& a, hipStream_t st);
 constexpr int64_t TOPK_MAX_N = 262144;
 
 struct MlaArgs {
@@ -73,6 +71,9 @@ struct PrefillTopkArgs {
   const int32_t* q_pos;
   int32_t k;
   int32_t* idx;
+  // null: every row.  Otherwise redo[b * n_q + r] != 0 marks the rows to select (a group of
+  // 4 rows runs if any of its rows is marked) and the rows below k are left alone.
+  const uint8_t* redo = nullptr;
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 
@@ -81,6 +82,16 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 // row i of sequence b at scores + (b * rows_pad + i) * ld, rows_pad = n_rows rounded up to
 // 16, ld a multiple of 64 covering the keys the rows see rounded up to 64; keys past a
 // row's position score -inf, columns past its last 64-key tile are not written.
+//
+// key_stride S > 1 scores the systematic sample of keys 0, S, 2S, ...: column j of a row
+// is key j*S, visible when j*S <= the row's position (ld then covers ceil(n_k / S) columns).
+//
+// Filter mode (cand != null): instead of storing the scores, each row appends the keys it
+// sees whose score is > thr[b * rows_pad + i], as (fp32 score bits, key index) pairs in
+// ascending key order, to its SEL_CAND_PITCH-slot list at
+// cand + (b * rows_pad + i) * SEL_CAND_PITCH (slots past SEL_CAND_CAP - 1 are counted, not
+// stored; slot SEL_CAND_CAP is scratch), and writes the number of such keys to
+// cnt[b * rows_pad + i].  key_stride must be 1.
 struct DenseIdxArgs {
   const uint8_t* q8;
   const float* qs;
@@ -92,9 +103,54 @@ struct DenseIdxArgs {
   int64_t row_begin, n_rows;
   float* scores;
   int64_t ld;
+  int32_t key_stride = 1;
+  const float* thr = nullptr;
+  uint2* cand = nullptr;
+  uint32_t* cnt = nullptr;
 };
 inline int64_t dense_rows_pad(int64_t n_rows) { return (n_rows + 15) / 16 * 16; }
 hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st);
+
+// Threshold-filtered selection (FP8 prefill and chunks): a row keeps its candidates when at
+// least k and at most SEL_CAND_CAP keys pass its threshold.
+constexpr int SEL_SAMPLE_STRIDE = 32;
+constexpr int SEL_CAND_CAP = 6144;
+constexpr int SEL_CAND_PITCH = SEL_CAND_CAP + 8;
+inline int64_t sel_sample_ld(int64_t n_k) {
+  const int64_t ns = (n_k + SEL_SAMPLE_STRIDE - 1) / SEL_SAMPLE_STRIDE;
+  return ns > 0 ? (ns + 63) / 64 * 64 : 64;
+}
+
+// Per row i of each sequence b (position q_pos[b] + row_begin + i, n = the keys it sees):
+// thr[b * rows_pad + i] = -inf (collect every key) when n <= SEL_CAND_CAP, else the sample
+// score of rank r = ceil(m + 5 sqrt(m) + 5), m = k * n_s / n, among the row's n_s visible
+// samples at samp + (b * rows_pad + i) * ld_s (-0 read as +0).
+struct SelThresholdArgs {
+  const float* samp;
+  int64_t ld_s, rows_pad, B, n_rows, n_k;
+  const int32_t* q_pos;
+  int64_t row_begin;
+  int32_t k;
+  float* thr;
+};
+hipError_t launch_sel_threshold(const SelThresholdArgs& a, hipStream_t st);
+
+// Per row: the top-k of its candidate list when k <= cnt <= SEL_CAND_CAP (written to idx
+// row out_row0 + i of sequence b's out_rows rows, ascending, -1 padded; redo byte 0), every
+// key when the row sees at most k (redo 0), else nothing (redo 1: the row's candidates do
+// not decide its top-k).  redo[b * out_rows + out_row0 + i].
+struct SelCandArgs {
+  const uint2* cand;
+  const uint32_t* cnt;
+  int64_t rows_pad, B, n_rows, n_k;
+  const int32_t* q_pos;
+  int64_t row_begin;
+  int32_t k;
+  int32_t* idx;
+  int64_t out_rows, out_row0;
+  uint8_t* redo;
+};
+hipError_t launch_sel_candidates(const SelCandArgs& a, hipStream_t st);
 
 // backward of the sparse attention; dkv (and dv when v is separate, fp32 path) are
 // zeroed and accumulated

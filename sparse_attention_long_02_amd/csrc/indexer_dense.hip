@@ -1,5 +1,10 @@
-// Dense FP8 lightning-indexer scores of a block of query rows, written to a padded score
-// workspace that the row top-k then ranks (prefill selection).
+// FP8 lightning-indexer scores of blocks of 16 query rows, for the threshold-filtered
+// selection of prefill rows (and, with a key stride, the key sample that sets the
+// thresholds).  Two modes:
+//   * store: the scores of a row (every key, or every S-th key) go to a padded workspace
+//     row; the selection uses it only for the 1-in-32 key sample;
+//   * filter: the scores are compared with the row's threshold and only the keys at or
+//     above it leave the chip, appended to the row's candidate list in ascending key order.
 //
 // The score of query t and key s is the weighted sum over the 64 indexer heads of ReLU'd
 // FP8 dot products (53ai.com V3.2-Exp summary, section 创新架构; juhe.plus explainer,
@@ -50,19 +55,20 @@ __device__ __forceinline__ DenseDma dense_dma_lane(int wv, int lane) {
   }
   return d;
 }
+// Key j of the launch is cache row j * stride; keys past n_keys - 1 (the last one the
+// launch may read) read that key (their scores are masked).
 __device__ __forceinline__ void dense_tile_load(uint32_t slot, const uint8_t* __restrict__ kb,
-                                                const float* __restrict__ ksb, int64_t key0, int64_t n_k,
-                                                const DenseDma& d, int wv, int lane) {
-  // keys past n_k - 1 read row n_k - 1 (their scores are masked)
+                                                const float* __restrict__ ksb, int64_t key0, int64_t n_keys,
+                                                int64_t stride, const DenseDma& d, int wv, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int64_t key = key0 + (d.off[i] >> 7);
-    const int64_t kc = key < n_k ? key : n_k - 1;
+    const int64_t kc = (key < n_keys ? key : n_keys - 1) * stride;
     dma16_all(kb + kc * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
   }
   if (wv == 3) {
     const int64_t key = key0 + lane;
-    dma4_vaddr(ksb + (key < n_k ? key : n_k - 1), slot + DN_TILE_BYTES);
+    dma4_vaddr(ksb + (key < n_keys ? key : n_keys - 1) * stride, slot + DN_TILE_BYTES);
   }
 }
 
@@ -80,14 +86,18 @@ __device__ __forceinline__ v8i dense_fragment(const uint8_t* tile, int f, int la
 
 // grid.x = B * n_grp (16-row groups, longest first within each sequence); 256 threads.
 // Row i (0 <= i < n_rows) of sequence b is query row row_begin + i, at position
-// (q_pos ? q_pos[b] : 0) + row_begin + i; its scores go to row b * 16 n_grp + i of
-// `scores` (ld floats apart, ld a multiple of 64 and at least the tiles the row needs).
-// Keys past the position (or past n_k - 1) score -inf.
+// (q_pos ? q_pos[b] : 0) + row_begin + i.  Launch key j is cache row j * stride and the row
+// sees it when j * stride <= min(position, n_k - 1).
+// Store mode: the row's scores go to row b * 16 n_grp + i of `scores` (ld floats apart, ld
+// a multiple of 64 covering the tiles the row needs); keys it does not see score -inf.
+// Filter mode: see DenseIdxArgs.
+template <bool FILTER>
 __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, int B, int64_t n_q, int64_t n_k,
-    const int32_t* __restrict__ q_pos, int64_t row_begin, int64_t n_rows, int64_t n_grp,
-    float* __restrict__ scores, int64_t ld) {
+    const int32_t* __restrict__ q_pos, int64_t row_begin, int64_t n_rows, int64_t n_grp, int stride,
+    float* __restrict__ scores, int64_t ld, const float* __restrict__ thr, uint2* __restrict__ cand,
+    uint32_t* __restrict__ cnt) {
   __shared__ __align__(16) uint8_t ring[DN_SLOTS * DN_SLOT_BYTES];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = (int)(blockIdx.x % B);
@@ -95,9 +105,10 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   const int64_t pos0 = (q_pos ? (int64_t)q_pos[b] : 0) + row_begin;
   const int64_t i0 = 16 * grp;
   const int64_t i_last = i0 + 15 < n_rows ? i0 + 15 : n_rows - 1;
-  int64_t n_vis = pos0 + i_last + 1;
-  n_vis = n_vis < n_k ? n_vis : n_k;
-  n_vis = n_vis > 0 ? n_vis : 0;
+  // launch keys 0 .. n_keys - 1 exist; the group's last row sees n_vis of them
+  const int64_t n_keys = (n_k + stride - 1) / stride;
+  int64_t lim_last = pos0 + i_last < n_k - 1 ? pos0 + i_last : n_k - 1;
+  const int64_t n_vis = lim_last >= 0 ? lim_last / stride + 1 : 0;
   const int ntiles = (int)((n_vis + KEY_TILE - 1) / KEY_TILE);
 
   const uint8_t* kb = k8 + (size_t)b * n_k * IDX_DIM;
@@ -106,7 +117,8 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   const DenseDma dl = dense_dma_lane(wv, lane);
 #pragma unroll
   for (int t = 0; t < DN_SLOTS - 1; ++t)
-    if (t < ntiles) dense_tile_load(ring0 + t * DN_SLOT_BYTES, kb, ksb, (int64_t)t * KEY_TILE, n_k, dl, wv, lane);
+    if (t < ntiles)
+      dense_tile_load(ring0 + t * DN_SLOT_BYTES, kb, ksb, (int64_t)t * KEY_TILE, n_keys, stride, dl, wv, lane);
 
   // this wave's rows i0 + 4wv + j; padding rows score the last real row
   const int g = lane >> 4, c = lane & 15, rq = c >> 2;
@@ -139,18 +151,63 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
     if (g == j) {
       cmx = __fmul_rn(cm, UNSCALE);
       const int64_t p = pos0 + i;
-      lim = p < n_k - 1 ? p : n_k - 1;
+      const int64_t lk = p < n_k - 1 ? p : n_k - 1;
+      lim = lk >= 0 ? lk / stride : -1;
     }
   }
-  float* srow = scores + ((int64_t)b * 16 * n_grp + i0 + 4 * wv + g) * ld + 4 * c;
+  const int64_t my_row = (int64_t)b * 16 * n_grp + i0 + 4 * wv + g;
+  float* srow = scores + my_row * ld + 4 * c;
+  // filter mode: this lane's row's threshold; the wave's four rows' lists and counts (the
+  // counts are wave-uniform, one per 16-lane group)
+  float thr_f = 0.f;
+  uint32_t cnt_g[4] = {0u, 0u, 0u, 0u};
+  uint2* wlist = nullptr;
+  if constexpr (FILTER) {
+    const int64_t i = i0 + 4 * wv + g;
+    thr_f = thr[(int64_t)b * 16 * n_grp + (i < n_rows ? i : n_rows - 1)];
+    wlist = cand + ((int64_t)b * 16 * n_grp + i0 + 4 * wv) * SEL_CAND_PITCH;
+  }
+  const uint32_t row_off = (uint32_t)g * SEL_CAND_PITCH;
+  // A tile's scores are compared with the threshold when the tile is done; appending the
+  // keys that pass runs one tile later, between the next tile's matrix-core products, so
+  // its scan / store chain overlaps them.  Keys 4c + f of the tile (row g of the wave) are
+  // appended in (c, f) order, i.e. ascending: a lane's first slot follows the row's earlier
+  // hits and the hits of the lanes below it in its 16-lane group (a scan within the DPP
+  // row).  Every lane stores four times per tile, lanes without a key to append into their
+  // row's scratch slot, so each wave issues exactly four stores per tile and the load
+  // waits below can count them.
+  auto append_tile = [&](const float (&sc)[4], uint32_t hit, uint32_t key32) {
+    const uint32_t h = (uint32_t)__builtin_popcount(hit);
+    uint32_t incl = h;
+    incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+    incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+    incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+    incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+    const uint32_t base = g == 0 ? cnt_g[0] : g == 1 ? cnt_g[1] : g == 2 ? cnt_g[2] : cnt_g[3];
+    const uint32_t first = row_off + base + incl - h;
+    const uint32_t end = row_off + (uint32_t)SEL_CAND_CAP;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const uint32_t o = first + (uint32_t)__builtin_popcount(hit & ((1u << f) - 1u));
+      const bool ok = ((hit >> f) & 1u) && o < end;
+      wlist[ok ? o : end] = make_uint2(__float_as_uint(sc[f]), key32 + f);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt_g[q] += (uint32_t)__builtin_amdgcn_readlane((int)incl, 16 * q + 15);
+  };
+  const int32_t lim32 = (int32_t)lim;
+  // the previous tile's pending append (none before tile 0)
+  float psc[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t phit = 0;
+  constexpr int STORES = FILTER ? 4 : 1;
 
   for (int t = 0; t < ntiles; ++t) {
     // tile t has landed once at most the loads of tiles t+1 .. t+DN_SLOTS-2 and the stores
-    // of tiles t-DN_SLOTS+1 .. t-1 are outstanding (vector-memory operations complete in
-    // issue order); outside the steady state wait for everything
+    // issued since its own loads (STORES per tile step) are outstanding (vector-memory
+    // operations complete in issue order); outside the steady state wait for everything
     if (t >= DN_SLOTS - 1 && t + DN_SLOTS - 2 < ntiles) {
-      if (wv == 3) VMCNT(3 * (DN_SLOTS - 2) + DN_SLOTS - 1);
-      else VMCNT(2 * (DN_SLOTS - 2) + DN_SLOTS - 1);
+      if (wv == 3) VMCNT(3 * (DN_SLOTS - 2) + STORES * (DN_SLOTS - 1));
+      else VMCNT(2 * (DN_SLOTS - 2) + STORES * (DN_SLOTS - 1));
     } else {
       VMCNT(0);
     }
@@ -158,7 +215,7 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
     block_barrier();
     if (t + DN_SLOTS - 1 < ntiles)  // into the slot of tile t-1, which every wave is done with
       dense_tile_load(ring0 + ((t + DN_SLOTS - 1) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb,
-                      (int64_t)(t + DN_SLOTS - 1) * KEY_TILE, n_k, dl, wv, lane);
+                      (int64_t)(t + DN_SLOTS - 1) * KEY_TILE, n_keys, stride, dl, wv, lane);
     const uint8_t* tile = ring + (t % DN_SLOTS) * DN_SLOT_BYTES;
     float v[4];
 #pragma unroll
@@ -175,24 +232,48 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
         d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(W[1][j], relu_pack(x2, x3), d1, 0, 0, 0);
       }
       v[f] = __fadd_rn(d0[0], d1[0]);
+      if constexpr (FILTER)
+        if (f == 0) append_tile(psc, phit, (uint32_t)(4 * c + (t - 1) * KEY_TILE));
     }
     typedef __attribute__((address_space(3))) const v4f lds_v4f;
     const v4f kscale = *(lds_v4f*)((__attribute__((address_space(3))) const uint8_t*)tile + DN_TILE_BYTES + 16 * c);
     const int64_t key = (int64_t)t * KEY_TILE + 4 * c;
-    v4f o;
+    if constexpr (!FILTER) {
+      v4f o;
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      o[f] = key + f <= lim ? __fmul_rn(__fmul_rn(v[f], cmx), kscale[f]) : -INFINITY;
-    *reinterpret_cast<v4f*>(srow + (int64_t)t * KEY_TILE) = o;
+      for (int f = 0; f < 4; ++f)
+        o[f] = key + f <= lim ? __fmul_rn(__fmul_rn(v[f], cmx), kscale[f]) : -INFINITY;
+      *reinterpret_cast<v4f*>(srow + (int64_t)t * KEY_TILE) = o;
+    } else {
+      phit = 0;
+      const int32_t vis = lim32 - (int32_t)key;  // filter mode: fewer than 2^31 keys
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        psc[f] = __fmul_rn(__fmul_rn(v[f], cmx), kscale[f]);
+        phit |= (uint32_t)((f <= vis) & (psc[f] > thr_f)) << f;
+      }
+    }
+  }
+  if constexpr (FILTER) {
+    if (ntiles > 0) append_tile(psc, phit, (uint32_t)(4 * c + (ntiles - 1) * KEY_TILE));
+    const int64_t i = i0 + 4 * wv + g;
+    const uint32_t total = g == 0 ? cnt_g[0] : g == 1 ? cnt_g[1] : g == 2 ? cnt_g[2] : cnt_g[3];
+    if (c == 0 && i < n_rows) cnt[my_row] = total;
   }
 }
 
 hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st) {
   const int64_t n_grp = (a.n_rows + 15) / 16;
   if (n_grp <= 0) return hipSuccess;
-  hipLaunchKernelGGL(idx_dense_fp8_kernel, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8, a.qs,
-                     a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp, a.scores,
-                     a.ld);
+  if (a.key_stride < 1 || (a.cand && a.key_stride != 1)) return hipErrorInvalidValue;
+  if (a.cand)
+    hipLaunchKernelGGL(idx_dense_fp8_kernel<true>, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8,
+                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp, 1,
+                       nullptr, (int64_t)0, a.thr, a.cand, a.cnt);
+  else
+    hipLaunchKernelGGL(idx_dense_fp8_kernel<false>, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8,
+                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp,
+                       a.key_stride, a.scores, a.ld, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

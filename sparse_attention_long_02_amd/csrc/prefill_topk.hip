@@ -397,10 +397,25 @@ __device__ __forceinline__ GroupGeom group_geom(int G, int B, int n_q, int n_k, 
   return g;
 }
 
+// With a redo list, a group runs only if one of its rows (from row_lo up) is marked.
+__device__ __forceinline__ bool group_skipped(const uint8_t* __restrict__ redo, const GroupGeom& g, int n_q,
+                                              int row_lo) {
+  if (!redo) return false;
+  const uint8_t* r = redo + (size_t)g.b * n_q;
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = g.row_hi - 4 + j;
+    if (row >= row_lo && row >= 0) any |= r[row] != 0;
+  }
+  return !any;
+}
+
 __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int B,
-    int n_q, int n_k, int row_lo, int k, int n_groups, int32_t* __restrict__ idx) {
+    int n_q, int n_k, int row_lo, int k, int n_groups, int32_t* __restrict__ idx,
+    const uint8_t* __restrict__ redo) {
   // ring of three tile pairs (pair p = tiles 2p, 2p+1) and their key scales
   __shared__ __align__(16) uint8_t tk0[TILE_BYTES];
   __shared__ __align__(16) uint8_t tk1[TILE_BYTES];
@@ -425,6 +440,7 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const TileDma dl = tile_dma_lane(wv, lane);
     for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
       const GroupGeom g = group_geom(G, B, n_q, n_k, q_pos);
+      if (group_skipped(redo, g, n_q, row_lo)) continue;
       if (g.n_keys <= k) continue;  // every row keeps all it sees: the owners write it
       const int row0 = g.row_hi - 4;
       const size_t rbase = (size_t)g.b * n_q;
@@ -489,6 +505,7 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const int r = wv - PF_SCORE_WAVES;
     for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
       const GroupGeom g = group_geom(G, B, n_q, n_k, q_pos);
+      if (group_skipped(redo, g, n_q, row_lo)) continue;
       const int my_row = g.row_hi - 4 + r;
       const bool valid = my_row >= row_lo;
       // last key this row sees (-1: none)
@@ -561,7 +578,7 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
   int64_t row_lo = 0;
   if (!a.q_pos) {
     row_lo = a.k < a.n_q ? a.k : a.n_q;
-    if (row_lo > 0)
+    if (row_lo > 0 && !a.redo)
       hipLaunchKernelGGL(prefill_fill_kernel, dim3((unsigned)row_lo, (unsigned)a.B), dim3(256), 0, st, row_lo,
                          a.n_q, a.n_k, a.k, a.idx);
   }
@@ -578,7 +595,7 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
     const int64_t blocks = n_groups < n_cu ? n_groups : n_cu;
     hipLaunchKernelGGL(prefill_idx_topk_kernel, dim3((unsigned)blocks), dim3(PF_WAVES * 64), 0, st, a.q8, a.qs,
                        a.k8, a.ks, a.w, a.q_pos, (int)a.B, (int)a.n_q, (int)a.n_k, (int)row_lo, a.k,
-                       (int)n_groups, a.idx);
+                       (int)n_groups, a.idx, a.redo);
   }
   return hipGetLastError();
 }

@@ -316,77 +316,8 @@ __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
   write_kept<TL_THREADS>(sel, tie, n, rem, k, out, wtot);
 }
 
-// ---------------------------------------------------------------------------------------
-// Ordered-candidate top-k (rows of any length, k <= TO_CAP / 2).  One 512-thread block per
-// row and about 33 KB of LDS, so four blocks share a CU and keep 128 KB of score loads in
-// flight:
-//   1. a threshold T: a row of at most TO_CAP keys takes every key; a longer row takes the
-//      sample key of rank about 1.5 k * TO_CAP / n among TO_CAP evenly spaced samples, so
-//      that about 1.5 k keys exceed it;
-//   2. one pass over the row collects the keys > T, with their positions, in ascending
-//      position order: each thread reads TO_PER consecutive scores and a block scan of the
-//      per-thread counts places them;
-//   3. if at least k and at most TO_CAP keys exceed T, the k-th largest key v* and every
-//      key equal to it are among the candidates: a radix select over the candidates gives
-//      v* and how many keys equal to v* are kept (the lowest positions), and an ordered
-//      pass over the candidates writes the kept positions ascending;
-//   4. otherwise (an unlucky sample, heavy ties) the exact select runs over the whole row
-//      and the ordered pass runs over the row itself.
-// The result is the full-sort definition either way.
-// ---------------------------------------------------------------------------------------
+// blocks that select over an LDS candidate list
 constexpr int TO_THREADS = 512;
-constexpr int TO_CAP = 4096;
-constexpr int TO_PER = 8;
-constexpr int TO_STEP = TO_THREADS * TO_PER;
-
-// scores p0 .. p0+TO_PER-1 of a row (positions >= n read as -inf and are never taken)
-__device__ __forceinline__ void load_run(const float* __restrict__ srow, int64_t p0, int64_t n, bool vec,
-                                         float v[TO_PER]) {
-  if (vec && p0 + TO_PER <= n) {
-    const float4* p = reinterpret_cast<const float4*>(srow + p0);
-#pragma unroll
-    for (int q = 0; q < TO_PER / 4; ++q) {
-      const float4 x = p[q];
-      v[4 * q] = x.x;
-      v[4 * q + 1] = x.y;
-      v[4 * q + 2] = x.z;
-      v[4 * q + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < TO_PER; ++e) v[e] = p0 + e < n ? srow[p0 + e] : -INFINITY;
-  }
-}
-
-// Keys > T (every key if `all`) in ascending position order into ckey/cpos (slots past
-// TO_CAP are counted, not stored).  Returns the count.
-__device__ uint32_t collect_ordered(const float* __restrict__ srow, int64_t n, bool vec, bool all, uint32_t T,
-                                    uint32_t* ckey, int32_t* cpos, uint32_t* wtot) {
-  const int tid = threadIdx.x;
-  uint32_t nc = 0;
-  for (int64_t s0 = 0; s0 < n; s0 += TO_STEP) {
-    const int64_t p0 = s0 + (int64_t)TO_PER * tid;
-    float v[TO_PER];
-    load_run(srow, p0, n, vec, v);
-    uint32_t m = 0;
-#pragma unroll
-    for (int e = 0; e < TO_PER; ++e) m |= (uint32_t)((p0 + e < n) & (all | (score_key(v[e]) > T))) << e;
-    uint32_t tot;
-    uint32_t slot = nc + block_excl_scan<TO_THREADS>((uint32_t)__popc(m), wtot, tot);
-#pragma unroll
-    for (int e = 0; e < TO_PER; ++e)
-      if ((m >> e) & 1u) {
-        if (slot < (uint32_t)TO_CAP) {
-          ckey[slot] = score_key(v[e]);
-          cpos[slot] = (int32_t)(p0 + e);
-        }
-        ++slot;
-      }
-    nc += tot;
-  }
-  __syncthreads();
-  return nc;
-}
 
 // Kept candidates (keys > v*, then the first `rem` keys equal to v* in position order)
 // written ascending to out, -1 padded to k.
@@ -420,129 +351,110 @@ __device__ void write_from_candidates(const uint32_t* ckey, const int32_t* cpos,
   for (int64_t j = (int64_t)tot + tid; j < k; j += TO_THREADS) out[j] = -1;
 }
 
-// Exact radix select of the k-th largest key of a whole row (8-bit digits, four passes).
-__device__ uint32_t select_row8(const float* __restrict__ srow, int64_t n, bool vec, int k, uint32_t* hist,
-                                uint32_t* wtot, uint32_t* s_digit, uint32_t* s_above, uint32_t& rem) {
+// ---------------------------------------------------------------------------------------
+// Threshold-filtered selection.  The filtering indexer keeps, for each row, only the keys
+// whose score reaches a threshold set from a systematic 1-in-SEL_SAMPLE_STRIDE key sample,
+// so the row's top-k is decided from a short candidate list and no full score row is ever
+// stored.  The threshold is the sample of rank r = ceil(m + 5 sqrt(m) + 5), m = k n_s / n
+// (the expected number of samples among the row's top k): with r far above m the
+// candidates almost always include the whole top-k, and with cap / stride samples expected
+// above the cap's boundary, almost never overflow the SEL_CAND_CAP slots.  Either miss is
+// detected exactly (fewer than k candidates, or more than the cap) and the row is
+// recomputed by the streaming exact selection, so the result never depends on the sample.
+// ---------------------------------------------------------------------------------------
+constexpr int TH_THREADS = 256;
+constexpr int TH_MAX = (int)(TOPK_MAX_N / SEL_SAMPLE_STRIDE);
+
+__global__ __launch_bounds__(TH_THREADS) void sel_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
+                                                                   int64_t rows_pad, int64_t n_rows, int64_t n_k,
+                                                                   const int32_t* __restrict__ q_pos,
+                                                                   int64_t row_begin, int k,
+                                                                   float* __restrict__ thr) {
+  __shared__ uint32_t keys[TH_MAX];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wtot[TH_THREADS / WAVE];
+  __shared__ uint32_t s_digit, s_above;
+  const int64_t i = n_rows - 1 - (int64_t)blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + row_begin + i;
+  int64_t n = pos + 1 < n_k ? pos + 1 : n_k;
+  n = n > 0 ? n : 0;
+  float* out = thr + (int64_t)b * rows_pad + i;
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-  rem = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int j = tid; j < 256; j += TO_THREADS) hist[j] = 0;
-    __syncthreads();
-    for (int64_t s0 = 0; s0 < n; s0 += TO_STEP) {
-      const int64_t p0 = s0 + (int64_t)TO_PER * tid;
-      float v[TO_PER];
-      load_run(srow, p0, n, vec, v);
-#pragma unroll
-      for (int e = 0; e < TO_PER; ++e) {
-        const uint32_t u = score_key(v[e]);
-        if ((p0 + e < n) && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-      }
-    }
-    __syncthreads();
-    uint32_t above;
-    const uint32_t d = pick_digit<TO_THREADS>(hist, 256, rem, wtot, s_digit, s_above, above);
-    rem -= above;
-    prefix |= d << shift;
-    pmask |= 255u << shift;
+  if (n <= SEL_CAND_CAP) {  // the list holds every key the row sees
+    if (tid == 0) *out = -INFINITY;
+    return;
   }
-  return prefix;
+  const int ns = (int)((n - 1) / SEL_SAMPLE_STRIDE + 1);
+  const float m = (float)k * (float)ns / (float)n;
+  int r = (int)ceilf(m + 5.f * sqrtf(m) + 5.f);
+  r = r < ns ? r : ns;
+  const float* srow = samp + ((int64_t)b * rows_pad + i) * ld_s;
+  for (int j = tid; j < ns; j += TH_THREADS) keys[j] = score_key(srow[j]);
+  __syncthreads();
+  uint32_t rem;
+  const uint32_t T = select_lds<TH_THREADS>(keys, ns, (uint32_t)r, hist, wtot, &s_digit, &s_above, rem);
+  // the filter keeps the keys scoring strictly above this sample (the key is mapped back to
+  // its fp32 value; a -0 sample was read as +0, and the two compare equal anyway)
+  if (tid == 0) *out = __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
 }
 
-// The kept keys of a whole row (keys > v*, then the first `rem` equal to v*) written ascending.
-__device__ void write_from_row(const float* __restrict__ srow, int64_t n, bool vec, uint32_t vstar, uint32_t rem,
-                               int k, int32_t* __restrict__ out, uint32_t* wtot) {
-  const int tid = threadIdx.x;
-  uint32_t o_base = 0, t_base = 0;
-  for (int64_t s0 = 0; s0 < n; s0 += TO_STEP) {
-    const int64_t p0 = s0 + (int64_t)TO_PER * tid;
-    float v[TO_PER];
-    load_run(srow, p0, n, vec, v);
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int e = 0; e < TO_PER; ++e) {
-      const uint32_t u = score_key(v[e]);
-      const bool in = p0 + e < n;
-      gt |= (uint32_t)(in & (u > vstar)) << e;
-      eq |= (uint32_t)(in & (u == vstar)) << e;
-    }
-    uint32_t tt;
-    const uint32_t tb = t_base + block_excl_scan<TO_THREADS>((uint32_t)__popc(eq), wtot, tt);
-    // ties of this thread that are still within the first `rem`
-    const uint32_t take = tb < rem ? min((uint32_t)__popc(eq), rem - tb) : 0u;
-    uint32_t keep = gt, left = take;
-#pragma unroll
-    for (int e = 0; e < TO_PER; ++e)
-      if (((eq >> e) & 1u) && left) {
-        keep |= 1u << e;
-        --left;
-      }
-    uint32_t tot;
-    uint32_t o = o_base + block_excl_scan<TO_THREADS>((uint32_t)__popc(keep), wtot, tot);
-#pragma unroll
-    for (int e = 0; e < TO_PER; ++e)
-      if ((keep >> e) & 1u) {
-        if (o < (uint32_t)k) out[o] = (int32_t)(p0 + e);
-        ++o;
-      }
-    o_base += tot;
-    t_base += tt;
-  }
-  for (int64_t j = (int64_t)o_base + tid; j < k; j += TO_THREADS) out[j] = -1;
-}
-
-// grid (n_rows, B), longest rows first.  Row i of sequence b: scores at
-// scores + (b * score_rows + i) * ld, position q_pos[b] + pos_offset + row_begin + i, output
-// row out_row0 + i of sequence b's out_rows rows.
-__global__ __launch_bounds__(TO_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void topk_ordered_kernel(
-    const float* __restrict__ scores, int64_t ld, int64_t score_rows, int64_t n_rows, int64_t n_k,
-    const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int k, int32_t* __restrict__ idx,
-    int64_t out_rows, int64_t out_row0) {
-  __shared__ uint32_t ckey[TO_CAP];  // samples first, then candidate keys
-  __shared__ int32_t cpos[TO_CAP];
+__global__ __launch_bounds__(TO_THREADS) void sel_candidates_kernel(
+    const uint2* __restrict__ cand, const uint32_t* __restrict__ cnt, int64_t rows_pad, int64_t n_rows, int64_t n_k,
+    const int32_t* __restrict__ q_pos, int64_t row_begin, int k, int32_t* __restrict__ idx, int64_t out_rows,
+    int64_t out_row0, uint8_t* __restrict__ redo) {
+  __shared__ uint32_t ckey[SEL_CAND_CAP];
+  __shared__ int32_t cpos[SEL_CAND_CAP];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wtot[TO_THREADS / WAVE];
   __shared__ uint32_t s_digit, s_above;
   const int64_t i = n_rows - 1 - (int64_t)blockIdx.x;
   const int b = blockIdx.y;
-  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + row_begin + i;
+  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + row_begin + i;
   int64_t n = pos + 1 < n_k ? pos + 1 : n_k;
   n = n > 0 ? n : 0;
-  const float* srow = scores + ((int64_t)b * score_rows + i) * ld;
-  int32_t* out = idx + ((int64_t)b * out_rows + out_row0 + i) * k;
+  const int64_t orow = (int64_t)b * out_rows + out_row0 + i;
+  int32_t* out = idx + orow * k;
   const int tid = threadIdx.x;
   if (n <= k) {  // every visible key is kept
     for (int j = tid; j < k; j += TO_THREADS) out[j] = j < n ? j : -1;
+    if (tid == 0) redo[orow] = 0;
     return;
   }
-  const bool vec = ((uintptr_t)srow & 15u) == 0;
-  const bool all = n <= TO_CAP;
-  uint32_t T = 0;
-  if (!all) {
-    for (int j = tid; j < TO_CAP; j += TO_THREADS) ckey[j] = score_key(srow[((int64_t)j * n) / TO_CAP]);
-    __syncthreads();
-    int64_t srank = (3 * (int64_t)k * TO_CAP + n) / (2 * n);  // about 1.5 k keys above
-    srank = srank < 1 ? 1 : srank > TO_CAP ? TO_CAP : srank;
-    uint32_t srem;
-    T = select_lds<TO_THREADS>(ckey, TO_CAP, (uint32_t)srank, hist, wtot, &s_digit, &s_above, srem);
+  const int64_t r = (int64_t)b * rows_pad + i;
+  const uint32_t c = cnt[r];
+  if (c < (uint32_t)k || c > (uint32_t)SEL_CAND_CAP) {  // the list does not decide the row
+    if (tid == 0) redo[orow] = 1;
+    return;
   }
-  const uint32_t nc = collect_ordered(srow, n, vec, all, T, ckey, cpos, wtot);
-  uint32_t vstar, rem;
-  if (nc >= (uint32_t)k && nc <= (uint32_t)TO_CAP) {
-    vstar = select_lds<TO_THREADS>(ckey, (int)nc, (uint32_t)k, hist, wtot, &s_digit, &s_above, rem);
-    write_from_candidates(ckey, cpos, nc, vstar, rem, k, out, wtot);
-  } else {
-    vstar = select_row8(srow, n, vec, k, hist, wtot, &s_digit, &s_above, rem);
-    write_from_row(srow, n, vec, vstar, rem, k, out, wtot);
+  const uint2* cr = cand + r * SEL_CAND_PITCH;
+  for (uint32_t j = tid; j < c; j += TO_THREADS) {
+    const uint2 e = cr[j];
+    ckey[j] = score_key(__uint_as_float(e.x));
+    cpos[j] = (int32_t)e.y;
   }
+  __syncthreads();
+  uint32_t rem;
+  const uint32_t vstar = select_lds<TO_THREADS>(ckey, (int)c, (uint32_t)k, hist, wtot, &s_digit, &s_above, rem);
+  write_from_candidates(ckey, cpos, c, vstar, rem, k, out, wtot);
+  if (tid == 0) redo[orow] = 0;
 }
 
-hipError_t launch_topk_ordered(const TopkArgs& a, hipStream_t st) {
+hipError_t launch_sel_threshold(const SelThresholdArgs& a, hipStream_t st) {
   if (a.n_rows <= 0 || a.B <= 0) return hipSuccess;
-  dim3 grid((unsigned)a.n_rows, (unsigned)a.B);
-  hipLaunchKernelGGL(topk_ordered_kernel, grid, dim3(TO_THREADS), 0, st, a.scores, a.ld_scores,
-                     a.score_rows ? a.score_rows : a.n_rows, a.n_rows, a.n_k, a.q_pos, a.pos_offset, a.row_begin,
-                     a.k, a.idx, a.out_rows ? a.out_rows : a.n_rows, a.out_row0);
+  if ((a.n_k + SEL_SAMPLE_STRIDE - 1) / SEL_SAMPLE_STRIDE > TH_MAX || a.ld_s < sel_sample_ld(a.n_k))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sel_threshold_kernel, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(TH_THREADS), 0, st, a.samp,
+                     a.ld_s, a.rows_pad, a.n_rows, a.n_k, a.q_pos, a.row_begin, a.k, a.thr);
+  return hipGetLastError();
+}
+
+hipError_t launch_sel_candidates(const SelCandArgs& a, hipStream_t st) {
+  if (a.n_rows <= 0 || a.B <= 0) return hipSuccess;
+  if (a.k > SEL_CAND_CAP) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sel_candidates_kernel, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(TO_THREADS), 0, st, a.cand,
+                     a.cnt, a.rows_pad, a.n_rows, a.n_k, a.q_pos, a.row_begin, a.k, a.idx, a.out_rows, a.out_row0,
+                     a.redo);
   return hipGetLastError();
 }
 

@@ -54,13 +54,18 @@ def test_fused_selection_equals_topk_of_scores(c2):
     del scores
 
 
-@pytest.mark.parametrize("case", ["repeated_keys", "zero_rows", "zero_prefix", "small_k"])
+@pytest.mark.parametrize("case", ["repeated_keys", "zero_rows", "zero_prefix", "small_k", "sample_low",
+                                  "sample_high"])
 def test_fused_selection_ties(case):
-    """Heavy ties: repeated key rows (identical scores), all-zero query rows (every score
-    0), a run of all-zero keys longer than the candidate buffer (every buffer cut ends in
-    the exact tie-breaking selection), and a small k (many compactions)."""
-    _say(f"[fused ties] {case}")
-    cfg = S.CONFIGS["prefill_8k"].with_(L=6000)
+    """Heavy ties and inputs that defeat the key sample, at L = 12288 (rows past 6144 keys
+    take a sampled threshold): repeated key rows (identical scores), all-zero query rows
+    (every score 0), a run of all-zero keys, a small k, and keys whose every 32nd row (the
+    sampled ones) scores 0 (the threshold falls below far more keys than the candidate
+    list holds) or repeats one key at 4x its scale (a threshold set among many equal
+    samples).  Rows whose candidate list cannot decide them go to the streaming exact
+    selection; either way the result must be the top-k of the stored scores."""
+    _say(f"[selection ties] {case}")
+    cfg = S.CONFIGS["prefill_8k"].with_(L=12288)
     inp = S.make_prefill(cfg)
     qi, qs, ki, ks, w = indexer_inputs_dev(inp)
     k = cfg.k
@@ -69,23 +74,33 @@ def test_fused_selection_ties(case):
         ks = ks[torch.arange(cfg.L, device="cuda") % 37].contiguous()
     elif case == "zero_rows":
         qi = qi.clone()
-        qi[3000:3100] = 0
+        qi[9000:9100] = 0
         ki = ki.clone()
         ki[100:2500] = 0
     elif case == "zero_prefix":
         ki = ki.clone()
-        ki[:5000] = 0
+        ki[:9000] = 0
+    elif case == "sample_low":
+        ki = ki.clone()
+        ki[::32] = 0
+    elif case == "sample_high":
+        ki = ki.clone()
+        ks = ks.clone()
+        big = int(torch.argmax(ks))
+        ki[::32] = ki[big]
+        ks[::32] = ks[big] * 4
     else:
         k = 96
-    fused = dsa.select_prefill(qi, qs, ki, ks, w, k)
+    sel = dsa.select_prefill(qi, qs, ki, ks, w, k)
     scores = dsa.indexer(qi, qs, ki, ks, w)
     ref = dsa.topk(scores, k)
     torch.cuda.synchronize()
-    diff = (fused != ref).any(dim=1).nonzero().flatten().tolist()
+    diff = (sel != ref).any(dim=1).nonzero().flatten().tolist()
     assert not diff, f"{len(diff)} rows differ, first {diff[:5]}"
     if case == "zero_rows":   # an all-zero query row scores 0 everywhere: the first k keys win
-        row = fused[3050].cpu().numpy()
+        row = sel[9050].cpu().numpy()
         assert np.array_equal(row, np.arange(k))
+    del scores
 
 
 def test_prefill_end_to_end_vs_oracle(c2):
