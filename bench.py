@@ -245,11 +245,16 @@ def main():
         "sparse_mla": {"ms": t_mla * 1e3, "gather_bytes": g_bytes, "hbm_frac": g_bytes / t_mla / PEAK_HBM,
                        "bf16_flop": f_mla, "mfma_frac": f_mla / t_mla / PEAK_BF16},
     }
+    f_traffic = recorded_traffic("idx_dense_fp8_kernel_filter", cfg.name)
+    n_chunks = -(-L // 16384)
+    stages["select"]["filter_kernel_traffic_bytes_per_step"] = f_traffic * n_chunks if f_traffic else None
     if t_sel >= t_mla:
+        # the selection stage as a whole (key sample, thresholds, filtering indexer and
+        # candidate top-k per chunk of 16384 rows): its work over its time per step
         a = f_idx / t_sel
-        roof = {"kernel": "prefill_idx_topk_kernel (FP8 indexer + streaming top-k)", "bound": "mfma",
-                "achieved": a / 1e12, "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s", "frac": a / PEAK_FP8,
-                "traffic": recorded_traffic("prefill_idx_topk_kernel", cfg.name)}
+        roof = {"kernel": "threshold-filtered FP8 selection (idx_dense_fp8_kernel + sel_* kernels, one step)",
+                "bound": "mfma", "achieved": a / 1e12, "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s",
+                "frac": a / PEAK_FP8, "traffic": stages["select"]["filter_kernel_traffic_bytes_per_step"]}
     else:
         a = g_bytes / t_mla
         roof = {"kernel": "sparse_mla_bf16_kernel (gathered KV rows)", "bound": "hbm",

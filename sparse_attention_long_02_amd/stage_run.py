@@ -5,8 +5,9 @@
 
 Order of the dispatches: one device-to-device copy of --copy-mib MiB (its FETCH_SIZE and
 WRITE_SIZE readings calibrate the counters against a known byte count), then
-dsa_select_prefill (fill kernel + fused indexer/top-k kernel), then dsa_sparse_mla on that
-selection.  With --training, then the sparse-stage indexer loss (dsa_indexer_scores_at,
+dsa_select_prefill (per chunk of rows: key-sample indexer, thresholds, filtering indexer,
+candidate top-k; then the streaming selection of any undecided rows), then dsa_sparse_mla on
+that selection.  With --training, then the sparse-stage indexer loss (dsa_indexer_scores_at,
 dsa_indexer_kl) and dsa_sparse_mla_backward for seeded output gradients, as the benchmark
 runs them.  Inputs are the seeded synthetic tensors the benchmark uses.
 """

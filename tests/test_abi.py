@@ -127,8 +127,11 @@ def test_chunk_validation(L):
     assert call(nkm=1 << 25) == dsa.DSA_ERR_UNSUPPORTED
     assert call(it=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED       # fp32 indexer with bf16 attention
     assert call(kc=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG          # misaligned FP8 cache
-    # the FP8 path stores no scores; 4 x 512 queries need no split-key workspace either
-    assert L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 512, 131072, 128, 512, 2048, dsa.DSA_BF16) == 0
+    # the FP8 selection keeps per-row key-sample scores and candidate lists, never score rows:
+    # required, and far below the B x n_q x n_k floats the scores would take
+    sel = L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 512, 131072, 128, 512, 2048, dsa.DSA_BF16)
+    assert 0 < sel < 4 * 512 * 131072 * 4 // 4
+    assert call(nq=512) == dsa.DSA_ERR_WORKSPACE
     # one query per sequence splits keys over blocks: workspace required
     need = L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 1, 131072, 128, 512, 2048, dsa.DSA_BF16)
     assert need > 0 and call(nq=1) == dsa.DSA_ERR_WORKSPACE
