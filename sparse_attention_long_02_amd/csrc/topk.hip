@@ -102,26 +102,62 @@ __device__ void select_row(const float* __restrict__ srow, int64_t n, int k, uin
   vstar = prefix;
 }
 
-// Exact radix select of the rank-th largest of n keys held in LDS (8-bit digits).
+// Exact radix select of the rank-th largest of n keys held in LDS (1 <= rank <= n).  The
+// bits every key shares (found by a block-wide AND / OR) are skipped; the rest are resolved
+// in digits of up to 8 bits from the top.  Candidate lists span a narrow range of scores,
+// so this drops a pass and, with it, a pass whose few busy bins would serialise the LDS
+// atomics.  Returns v*; rem = how many keys equal to v* are kept.
 template <int NT>
 __device__ uint32_t select_lds(const uint32_t* keys, int n, uint32_t rank, uint32_t* hist, uint32_t* wtot,
                                uint32_t* s_digit, uint32_t* s_above, uint32_t& rem) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
+  if (tid == 0) {
+    hist[0] = 0xFFFFFFFFu;
+    hist[1] = 0u;
+  }
+  __syncthreads();
+  uint32_t ka = 0xFFFFFFFFu, ko = 0u;
+  for (int i = tid; i < n; i += NT) {
+    ka &= keys[i];
+    ko |= keys[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ka &= (uint32_t)__shfl_xor((int)ka, off, WAVE);
+    ko |= (uint32_t)__shfl_xor((int)ko, off, WAVE);
+  }
+  if ((tid & (WAVE - 1)) == 0) {
+    atomicAnd(&hist[0], ka);
+    atomicOr(&hist[1], ko);
+  }
+  __syncthreads();
+  ka = hist[0];
+  ko = hist[1];
+  __syncthreads();
   rem = rank;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int j = tid; j < 256; j += NT) hist[j] = 0;
+  const uint32_t diff = ka ^ ko;
+  if (diff == 0u) return ka;  // every key is equal
+  int top = 32 - __clz(diff);  // bits below `top` vary
+  uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
+  uint32_t prefix = ka & pmask;
+  while (top > 0) {
+    const int width = top < 8 ? top : 8;
+    const int shift = top - width;
+    const int nb = 1 << width;
+    const uint32_t dmask = (uint32_t)nb - 1u;
+    for (int j = tid; j < nb; j += NT) hist[j] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const uint32_t u = keys[i];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
     }
     __syncthreads();
     uint32_t above;
-    const uint32_t d = pick_digit<NT>(hist, 256, rem, wtot, s_digit, s_above, above);
+    const uint32_t d = pick_digit<NT>(hist, nb, rem, wtot, s_digit, s_above, above);
     rem -= above;
     prefix |= d << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
+    top = shift;
   }
   return prefix;
 }
@@ -320,9 +356,10 @@ __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
 constexpr int TO_THREADS = 512;
 
 // Kept candidates (keys > v*, then the first `rem` keys equal to v* in position order)
-// written ascending to out, -1 padded to k.
-__device__ void write_from_candidates(const uint32_t* ckey, const int32_t* cpos, uint32_t nc, uint32_t vstar,
-                                      uint32_t rem, int k, int32_t* __restrict__ out, uint32_t* wtot) {
+// written ascending to out, -1 padded to k; pos(j) is candidate j's key index.
+template <typename Pos>
+__device__ void write_from_candidates(const uint32_t* ckey, Pos pos, uint32_t nc, uint32_t vstar, uint32_t rem,
+                                      int k, int32_t* __restrict__ out, uint32_t* wtot) {
   const uint32_t tid = threadIdx.x;
   const uint32_t m = (nc + TO_THREADS - 1) / TO_THREADS;
   const uint32_t j0 = min(tid * m, nc), j1 = min(j0 + m, nc);
@@ -344,7 +381,7 @@ __device__ void write_from_candidates(const uint32_t* ckey, const int32_t* cpos,
     const bool keep = (u > vstar) | ((u == vstar) & (tr < rem));
     tr += u == vstar;
     if (keep) {
-      if (o < (uint32_t)k) out[o] = cpos[j];
+      if (o < (uint32_t)k) out[o] = pos(j);
       ++o;
     }
   }
@@ -365,12 +402,14 @@ __device__ void write_from_candidates(const uint32_t* ckey, const int32_t* cpos,
 constexpr int TH_THREADS = 256;
 constexpr int TH_MAX = (int)(TOPK_MAX_N / SEL_SAMPLE_STRIDE);
 
+// The row's sample keys live in dynamic LDS of ceil(n_k / SEL_SAMPLE_STRIDE) words (16 KB at
+// 131072 keys), so that many blocks share a CU.
 __global__ __launch_bounds__(TH_THREADS) void sel_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
                                                                    int64_t rows_pad, int64_t n_rows, int64_t n_k,
                                                                    const int32_t* __restrict__ q_pos,
                                                                    int64_t row_begin, int k,
                                                                    float* __restrict__ thr) {
-  __shared__ uint32_t keys[TH_MAX];
+  extern __shared__ uint32_t keys[];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wtot[TH_THREADS / WAVE];
   __shared__ uint32_t s_digit, s_above;
@@ -403,8 +442,9 @@ __global__ __launch_bounds__(TO_THREADS) void sel_candidates_kernel(
     const uint2* __restrict__ cand, const uint32_t* __restrict__ cnt, int64_t rows_pad, int64_t n_rows, int64_t n_k,
     const int32_t* __restrict__ q_pos, int64_t row_begin, int k, int32_t* __restrict__ idx, int64_t out_rows,
     int64_t out_row0, uint8_t* __restrict__ redo) {
+  // the candidates' score keys in LDS (24 KB, so several blocks share a CU); their key
+  // indices are read back from the list when the kept ones are written
   __shared__ uint32_t ckey[SEL_CAND_CAP];
-  __shared__ int32_t cpos[SEL_CAND_CAP];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wtot[TO_THREADS / WAVE];
   __shared__ uint32_t s_digit, s_above;
@@ -428,15 +468,11 @@ __global__ __launch_bounds__(TO_THREADS) void sel_candidates_kernel(
     return;
   }
   const uint2* cr = cand + r * SEL_CAND_PITCH;
-  for (uint32_t j = tid; j < c; j += TO_THREADS) {
-    const uint2 e = cr[j];
-    ckey[j] = score_key(__uint_as_float(e.x));
-    cpos[j] = (int32_t)e.y;
-  }
+  for (uint32_t j = tid; j < c; j += TO_THREADS) ckey[j] = score_key(__uint_as_float(cr[j].x));
   __syncthreads();
   uint32_t rem;
   const uint32_t vstar = select_lds<TO_THREADS>(ckey, (int)c, (uint32_t)k, hist, wtot, &s_digit, &s_above, rem);
-  write_from_candidates(ckey, cpos, c, vstar, rem, k, out, wtot);
+  write_from_candidates(ckey, [cr](uint32_t j) { return (int32_t)cr[j].y; }, c, vstar, rem, k, out, wtot);
   if (tid == 0) redo[orow] = 0;
 }
 
@@ -444,7 +480,8 @@ hipError_t launch_sel_threshold(const SelThresholdArgs& a, hipStream_t st) {
   if (a.n_rows <= 0 || a.B <= 0) return hipSuccess;
   if ((a.n_k + SEL_SAMPLE_STRIDE - 1) / SEL_SAMPLE_STRIDE > TH_MAX || a.ld_s < sel_sample_ld(a.n_k))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sel_threshold_kernel, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(TH_THREADS), 0, st, a.samp,
+  const size_t lds = (size_t)((a.n_k + SEL_SAMPLE_STRIDE - 1) / SEL_SAMPLE_STRIDE) * sizeof(uint32_t);
+  hipLaunchKernelGGL(sel_threshold_kernel, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(TH_THREADS), lds, st, a.samp,
                      a.ld_s, a.rows_pad, a.n_rows, a.n_k, a.q_pos, a.row_begin, a.k, a.thr);
   return hipGetLastError();
 }
