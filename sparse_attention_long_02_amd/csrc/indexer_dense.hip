@@ -116,7 +116,7 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   const uint32_t ring0 = lds_addr(ring);
   const DenseDma dl = dense_dma_lane(wv, lane);
 #pragma unroll
-  for (int t = 0; t < DN_SLOTS - 1; ++t)
+  for (int t = 0; t < DN_SLOTS - 2; ++t)
     if (t < ntiles)
       dense_tile_load(ring0 + t * DN_SLOT_BYTES, kb, ksb, (int64_t)t * KEY_TILE, n_keys, stride, dl, wv, lane);
 
@@ -201,21 +201,8 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   uint32_t phit = 0;
   constexpr int STORES = FILTER ? 4 : 1;
 
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t has landed once at most the loads of tiles t+1 .. t+DN_SLOTS-2 and the stores
-    // issued since its own loads (STORES per tile step) are outstanding (vector-memory
-    // operations complete in issue order); outside the steady state wait for everything
-    if (t >= DN_SLOTS - 1 && t + DN_SLOTS - 2 < ntiles) {
-      if (wv == 3) VMCNT(3 * (DN_SLOTS - 2) + STORES * (DN_SLOTS - 1));
-      else VMCNT(2 * (DN_SLOTS - 2) + STORES * (DN_SLOTS - 1));
-    } else {
-      VMCNT(0);
-    }
-    LGKM0();
-    block_barrier();
-    if (t + DN_SLOTS - 1 < ntiles)  // into the slot of tile t-1, which every wave is done with
-      dense_tile_load(ring0 + ((t + DN_SLOTS - 1) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb,
-                      (int64_t)(t + DN_SLOTS - 1) * KEY_TILE, n_keys, stride, dl, wv, lane);
+  // one 64-key tile: scores, then the store (store mode) or the compare (filter mode)
+  auto tile_step = [&](int t) {
     const uint8_t* tile = ring + (t % DN_SLOTS) * DN_SLOT_BYTES;
     float v[4];
 #pragma unroll
@@ -253,6 +240,34 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
         phit |= (uint32_t)((f <= vis) & (psc[f] > thr_f)) << f;
       }
     }
+  };
+
+  // Two tiles per block barrier.  At each step the slots of the previous step's two tiles are
+  // refilled with the tiles four ahead (the ring holds the step's two tiles and four in
+  // flight).
+  for (int t = 0; t < ntiles; t += 2) {
+    // tiles t and t+1 have landed once at most the loads of tiles t+2 and t+3 and the stores
+    // of the two steps since their own loads (STORES per tile) are outstanding
+    // (vector-memory operations complete in issue order); outside the steady state wait
+    // for everything
+    if (t >= 4 && t + 3 < ntiles) {
+      if (wv == 3) VMCNT(2 * 3 + 4 * STORES);
+      else VMCNT(2 * 2 + 4 * STORES);
+    } else {
+      VMCNT(0);
+    }
+    LGKM0();
+    block_barrier();
+    // into the slots of tiles t-2 and t-1, which every wave is done with
+    if (t + 4 < ntiles)
+      dense_tile_load(ring0 + ((t + 4) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb, (int64_t)(t + 4) * KEY_TILE, n_keys,
+                      stride, dl, wv, lane);
+    if (t + 5 < ntiles)
+      dense_tile_load(ring0 + ((t + 5) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb, (int64_t)(t + 5) * KEY_TILE, n_keys,
+                      stride, dl, wv, lane);
+    const int t_end = t + 2 < ntiles ? t + 2 : ntiles;
+#pragma nounroll
+    for (int u = t; u < t_end; ++u) tile_step(u);
   }
   if constexpr (FILTER) {
     if (ntiles > 0) append_tile(psc, phit, (uint32_t)(4 * c + (ntiles - 1) * KEY_TILE));
