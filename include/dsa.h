@@ -257,8 +257,9 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
  *   q [B, n_q, H, d_qk], kv_cache [B, n_k_max, d_qk], v_cache [B, n_k_max, d_v] or NULL
  *   idx [B, n_q, k] int32 (output: S_t ascending, -1 padded), out [B, n_q, H, d_v],
  *   lse [B, n_q, H] or NULL
- * idx_dtype / attn_dtype: DSA_FP8_E4M3 with DSA_BF16 (the indexer and the streaming
- * top-k fused on chip: no score matrix, k <= 2048, n_k_max < 2^25), or DSA_F32 with
+ * idx_dtype / attn_dtype: DSA_FP8_E4M3 with DSA_BF16 (dsa_select_prefill's threshold
+ * filter per sequence: no score matrix, k <= 2048, n_k_max < 2^25; the workspace holds
+ * key-sample scores and candidate lists for up to 16384 rows at a time), or DSA_F32 with
  * DSA_F32 (materialised scores in the workspace, n_q <= 65535).  Selection and
  * attention of a row do not depend on the other rows of the call: a prefill cut into
  * chunks returns what the one-shot prefill returns, bit for bit.

@@ -293,7 +293,7 @@ int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_i
   if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out), "bf16 operands must be 16-byte aligned");
   SUPPORT(idx_dtype == attn_dtype || (idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16),
           "prefill pairs an FP8 indexer with bf16 attention, or fp32 with fp32");
-  SUPPORT(idx_dtype != DSA_FP8_E4M3 || k <= 2048, "fused selection keeps at most 2048 keys");
+  SUPPORT(idx_dtype != DSA_FP8_E4M3 || k <= 2048, "FP8 selection keeps at most 2048 keys");
   const bool f32 = idx_dtype == DSA_F32;
   if (f32) SUPPORT(L <= 16384, "fp32 prefill supports L <= 16384");
   const size_t s_bytes = f32 ? align256((size_t)L * L * sizeof(float)) : sel_bytes(1, L, L);
@@ -383,8 +383,8 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
           "a chunk pairs an FP8 indexer with bf16 attention, or fp32 with fp32");
   if (idx_dtype == DSA_FP8_E4M3) {
     REQUIRE(aligned16(q_idx) && aligned16(k_cache), "FP8 operands must be 16-byte aligned");
-    SUPPORT(k <= 2048, "fused selection keeps at most 2048 keys (k = %d)", k);
-    SUPPORT(n_k_max <= FUSED_MAX_KEYS, "fused selection supports n_k_max <= %lld", (long long)FUSED_MAX_KEYS);
+    SUPPORT(k <= 2048, "FP8 selection keeps at most 2048 keys (k = %d)", k);
+    SUPPORT(n_k_max <= FUSED_MAX_KEYS, "FP8 selection supports n_k_max <= %lld", (long long)FUSED_MAX_KEYS);
     REQUIRE(B * ((n_q + 3) / 4) <= 2147483647LL, "B * n_q too large");
   } else {
     SUPPORT(n_k_max <= dsa::TOPK_MAX_N, "fp32 chunk supports n_k_max <= %lld", (long long)dsa::TOPK_MAX_N);

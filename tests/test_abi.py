@@ -123,7 +123,7 @@ def test_chunk_validation(L):
     assert call(qpos=None) == dsa.DSA_ERR_INVALID_ARG           # positions are required
     assert call(nq=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(B=65536) == dsa.DSA_ERR_INVALID_ARG
-    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED               # fused selection keeps <= 2048
+    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED               # FP8 selection keeps <= 2048
     assert call(nkm=1 << 25) == dsa.DSA_ERR_UNSUPPORTED
     assert call(it=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED       # fp32 indexer with bf16 attention
     assert call(kc=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG          # misaligned FP8 cache

@@ -86,18 +86,18 @@ def test_prefill_full_size_sampled_rows(name, n_random):
     _say(f"  attention max-abs on the GPU's selection {err:.3e}")
     assert err <= ATOL_BF16
     assert np.allclose(g_lse, l_ref, atol=1e-3, rtol=1e-4)
-    # per row: the library's scores within tolerance of the oracle's, and the fused
+    # per row: the library's scores within tolerance of the oracle's, and the
     # selection bit-identical to the top-k of those scores
     worst_rel = 0.0
     for j, t in enumerate(rows):
         t = int(t)
         s_row = dsa.indexer(qi, qs, ki_d, ks_d, w, row_begin=t, n_rows=1)
         sel = dsa.topk(s_row, k, q_pos=torch.tensor([t], dtype=torch.int32, device="cuda"))
-        assert np.array_equal(sel[0].cpu().numpy(), g_idx[j]), f"fused selection differs at row {t}"
+        assert np.array_equal(sel[0].cpu().numpy(), g_idx[j]), f"selection differs at row {t}"
         ok, rel = _indexer_ok(s_row[0].cpu().numpy().astype(np.float64), qhat[j], wf[j], khat, t, cfg.d_I)
         worst_rel = max(worst_rel, rel)
         assert ok, (t, rel)
-    _say(f"  indexer worst error / bound {worst_rel:.3e}; fused selection == top-k(indexer) on all rows")
+    _say(f"  indexer worst error / bound {worst_rel:.3e}; selection == top-k(indexer) on all rows")
 
 
 def test_decode_full_size_sampled_sequences():

@@ -39,24 +39,25 @@ def c2():
     return cfg, inp
 
 
-def test_fused_selection_equals_topk_of_scores(c2):
-    """The fused indexer + streaming top-k selects exactly the top-k of the scores that
+def test_selection_equals_topk_of_scores(c2):
+    """The prefill selection (threshold-filtered indexer + candidate top-k, streaming
+    re-selection of undecided rows) selects exactly the top-k of the scores that
     dsa_indexer writes (bit-identical scores, same tie rule), on every row of L = 8192."""
     cfg, inp = c2
-    _say("[fused == topk(indexer)] L=8192")
+    _say("[selection == topk(indexer)] L=8192")
     qi, qs, ki, ks, w = indexer_inputs_dev(inp)
-    fused = dsa.select_prefill(qi, qs, ki, ks, w, cfg.k)
+    sel = dsa.select_prefill(qi, qs, ki, ks, w, cfg.k)
     scores = dsa.indexer(qi, qs, ki, ks, w)
     ref = dsa.topk(scores, cfg.k)
     torch.cuda.synchronize()
-    diff = (fused != ref).any(dim=1).nonzero().flatten().tolist()
+    diff = (sel != ref).any(dim=1).nonzero().flatten().tolist()
     assert not diff, f"{len(diff)} rows differ, first {diff[:5]}"
     del scores
 
 
 @pytest.mark.parametrize("case", ["repeated_keys", "zero_rows", "zero_prefix", "small_k", "sample_low",
                                   "sample_high"])
-def test_fused_selection_ties(case):
+def test_selection_ties(case):
     """Heavy ties and inputs that defeat the key sample, at L = 12288 (rows past 6144 keys
     take a sampled threshold): repeated key rows (identical scores), all-zero query rows
     (every score 0), a run of all-zero keys, a small k, and keys whose every 32nd row (the
