@@ -27,11 +27,18 @@
  *
  * Conventions
  * -----------
- *   * Every pointer argument is a DEVICE pointer unless stated otherwise; all arrays
- *     are dense row-major with the innermost dimension contiguous (no strides except
- *     the documented ld_scores).  The caller owns every buffer, including the
- *     workspace (size it with dsa_workspace_size); the library allocates nothing and
- *     keeps no pointer after a call returns.
+ *   * Every pointer argument is a DEVICE pointer unless stated otherwise; arrays are
+ *     row-major with the innermost dimension contiguous.  Strides are in elements and
+ *     are documented per argument: ld_scores; ld_q (between the head rows of q), ld_kv
+ *     and ld_v (between key rows); and, for the per-sequence caches of decode and
+ *     chunks, the sequence strides kc_seq_stride (key rows of the indexer key cache and
+ *     its scales), kv_seq_stride and v_seq_stride (elements).  Every other array is
+ *     dense.  A row stride must be >= the row's width, and a sequence stride must be
+ *     >= rows x row stride (sequences do not overlap); bf16 row and sequence strides must
+ *     be multiples of 8 elements (16-byte rows).  Violations return DSA_ERR_INVALID_ARG.
+ *     The caller owns every buffer, including the workspace (size it with
+ *     dsa_workspace_size); the library allocates nothing and keeps no pointer after a
+ *     call returns.
  *   * All work is enqueued on `stream` (0 = the null stream); calls return before the
  *     GPU finishes.  Buffers must stay alive until the stream has passed the work.
  *   * Return value: DSA_OK (0) or a negative dsa_status.  Arguments are validated on
@@ -60,7 +67,7 @@ extern "C" {
 
 typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 enum dsa_status {
   DSA_OK = 0,
@@ -74,7 +81,7 @@ enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 };
 
 enum dsa_op { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2,
               DSA_OP_PREFILL = 3, DSA_OP_DECODE = 4, DSA_OP_SELECT = 5, DSA_OP_CHUNK = 6,
-              DSA_OP_MLA_BWD = 7 };
+              DSA_OP_MLA_BWD = 7, DSA_OP_KL_DENSE = 8 };
 
 /* DSA_ABI_VERSION of the loaded library. */
 int dsa_abi_version(void);
@@ -134,20 +141,26 @@ int dsa_topk(const float* scores, int64_t ld_scores, int64_t B, int64_t n_rows, 
              size_t ws_bytes, dsa_stream_t stream);
 
 /*
- * dsa_sparse_mla -- attention of every query head over its selected keys (stage 3).
+ * dsa_sparse_mla -- attention of every query head over its selected keys (stage 3): the
+ * core attention runs only over the k kept key-value entries, in MLA's MQA mode where one
+ * latent key-value row serves every query head (paperbridge.wiki summary, section
+ * DeepSeek Sparse Attention; 53ai.com V3.2-Exp summary, section 创新架构 and Figure 1).
  *
- *   q    [B, n_q, H, d_qk]   bf16 or fp32 (dtype)
- *   kv   [B, n_k, d_qk]      shared key/latent rows (MQA)
- *   v    [B, n_k, d_v] or NULL: NULL means V = kv[:, :, 0:d_v]
+ *   q    [B, n_q, H] rows of d_qk values, ld_q elements apart (ld_q >= d_qk): element
+ *        (b, t, h, d) at q[((b * n_q + t) * H + h) * ld_q + d]; bf16 or fp32 (dtype)
+ *   kv   [B, n_k] rows of d_qk values, ld_kv apart: the shared key/latent rows (MQA);
+ *        (b, s, d) at kv[(b * n_k + s) * ld_kv + d]
+ *   v    [B, n_k] rows of d_v values, ld_v apart, or NULL: NULL means V = kv[.., 0:d_v]
+ *        (ld_v is then ignored)
  *   idx  [B, n_q, k] int32   selected keys (-1 entries are ignored, anywhere)
- *   out  [B, n_q, H, d_v]    output, same dtype as q
+ *   out  [B, n_q, H, d_v]    dense output, same dtype as q
  *   lse  [B, n_q, H] fp32 or NULL: natural-log sum-exp of the scaled logits
  * Workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA, B, n_q, n_k, H, d_v, k, dtype).
  */
-int dsa_sparse_mla(const void* q, const void* kv, const void* v, const int32_t* idx,
-                   int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_qk, int32_t d_v,
-                   int32_t k, float sm_scale, int32_t dtype, void* out, float* lse, void* ws,
-                   size_t ws_bytes, dsa_stream_t stream);
+int dsa_sparse_mla(const void* q, int64_t ld_q, const void* kv, int64_t ld_kv, const void* v,
+                   int64_t ld_v, const int32_t* idx, int64_t B, int64_t n_q, int64_t n_k, int32_t H,
+                   int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t dtype, void* out,
+                   float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * dsa_sparse_mla_backward -- gradients of dsa_sparse_mla for the sparse training stage
@@ -201,41 +214,56 @@ int dsa_select_prefill(const void* q_idx, const float* q_scale, const void* k_id
 
 /*
  * dsa_forward_prefill -- the whole layer for one sequence of L tokens, query t at
- * position t: indexer -> top-k -> sparse attention.  The selection is dsa_select_prefill's
- * (the L x L score matrix is never stored).
+ * position t: the lightning indexer scores every preceding token, the top-k of those
+ * scores are kept, and the attention runs over the kept keys only (53ai.com V3.2-Exp
+ * summary, section 创新架构 and Figure 1; juhe.plus explainer, sections 第一步：Lightning
+ * Indexer and 第二步：Fine-grained Token Selection).  The selection is
+ * dsa_select_prefill's (the L x L score matrix is never stored); the attention is
+ * dsa_sparse_mla's.
  *
- *   q_idx [L, H_I, d_I], q_scale [L, H_I], k_idx [L, d_I], k_scale [L], w [L, H_I]
- *   q [L, H, d_qk], kv [L, d_qk], v [L, d_v] or NULL
+ *   q_idx [L, H_I, d_I], q_scale [L, H_I], k_idx [L, d_I], k_scale [L], w [L, H_I] (dense)
+ *   q [L, H] rows of d_qk values ld_q apart; kv [L] rows of d_qk values ld_kv apart;
+ *   v [L] rows of d_v values ld_v apart, or NULL (V = kv[:, 0:d_v], ld_v ignored)
  *   idx [L, k] int32 (output: the selection), out [L, H, d_v], lse [L, H] or NULL
  * idx_dtype: DSA_FP8_E4M3 or DSA_F32; attn_dtype: DSA_BF16 or DSA_F32.
  * Workspace: dsa_workspace_size(DSA_OP_PREFILL, 1, L, L, H, d_v, k, attn_dtype).
  */
 int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_idx,
-                        const float* k_scale, const float* w, const void* q, const void* kv,
-                        const void* v, int64_t L, int32_t H_I, int32_t d_I, int32_t H,
-                        int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
-                        int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out,
-                        float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+                        const float* k_scale, const float* w, const void* q, int64_t ld_q,
+                        const void* kv, int64_t ld_kv, const void* v, int64_t ld_v, int64_t L,
+                        int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k,
+                        float sm_scale, int32_t idx_dtype, int32_t attn_dtype, int32_t* idx,
+                        void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
- * dsa_forward_decode -- the whole layer for B sequences with one new token each.
+ * dsa_forward_decode -- the whole layer for B sequences with one new token each.  In the
+ * decode stage too the indexer scans every previous token and the attention runs over the
+ * top-k only, which is what lowers the per-token decode cost (yunpan.plus article, section
+ * 1.1 DSA; 53ai.com V3.2-Exp summary, section 创新架构).
  * Sequence b holds ctx_len[b] cached rows (1 <= ctx_len[b] <= n_k_max, device int32);
  * its query sits at position ctx_len[b] - 1 (its own row is already in the caches)
  * and sees every cached row.
  *
- *   q_idx [B, H_I, d_I], q_scale [B, H_I], w [B, H_I]
- *   k_cache [B, n_k_max, d_I], k_cache_scale [B, n_k_max]
- *   q [B, H, d_qk], kv_cache [B, n_k_max, d_qk], v_cache [B, n_k_max, d_v] or NULL
- *   idx [B, k] int32 (output), out [B, H, d_v], lse [B, H] or NULL
+ *   q_idx [B, H_I, d_I], q_scale [B, H_I], w [B, H_I] (dense)
+ *   k_cache        codes of sequence b, row s: k_cache + (b * kc_seq_stride + s) * d_I
+ *                  (rows of d_I bytes; kc_seq_stride >= n_k_max rows)
+ *   k_cache_scale  fp32, sequence b row s at k_cache_scale[b * kc_seq_stride + s]
+ *   q              [B, H] rows of d_qk values, ld_q elements apart
+ *   kv_cache       sequence b row s at kv_cache + b * kv_seq_stride + s * ld_kv (elements;
+ *                  kv_seq_stride >= n_k_max * ld_kv)
+ *   v_cache        likewise with ld_v / v_seq_stride, or NULL (V = kv[.., 0:d_v]; ld_v and
+ *                  v_seq_stride ignored)
+ *   idx [B, k] int32 (output), out [B, H, d_v] (dense), lse [B, H] or NULL
  * Workspace: dsa_workspace_size(DSA_OP_DECODE, B, 1, n_k_max, H, d_v, k, attn_dtype).
  */
 int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx,
                        const float* q_scale, const float* w, const void* k_cache,
-                       const float* k_cache_scale, const void* q, const void* kv_cache,
-                       const void* v_cache, int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk,
-                       int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype,
-                       int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
-                       size_t ws_bytes, dsa_stream_t stream);
+                       const float* k_cache_scale, int64_t kc_seq_stride, const void* q,
+                       int64_t ld_q, const void* kv_cache, int64_t ld_kv, int64_t kv_seq_stride,
+                       const void* v_cache, int64_t ld_v, int64_t v_seq_stride, int32_t H_I,
+                       int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k,
+                       float sm_scale, int32_t idx_dtype, int32_t attn_dtype, int32_t* idx,
+                       void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * dsa_forward_chunk -- the whole layer for a chunk of n_q new tokens in each of B
@@ -252,10 +280,11 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
  * (idx all -1, out 0, lse -inf).  Rows whose position leaves at most k visible keys keep
  * all of them.
  *
- *   q_idx [B, n_q, H_I, d_I], q_scale [B, n_q, H_I], w [B, n_q, H_I]
- *   k_cache [B, n_k_max, d_I], k_cache_scale [B, n_k_max]
- *   q [B, n_q, H, d_qk], kv_cache [B, n_k_max, d_qk], v_cache [B, n_k_max, d_v] or NULL
- *   idx [B, n_q, k] int32 (output: S_t ascending, -1 padded), out [B, n_q, H, d_v],
+ *   q_idx [B, n_q, H_I, d_I], q_scale [B, n_q, H_I], w [B, n_q, H_I] (dense)
+ *   k_cache, k_cache_scale, kc_seq_stride; kv_cache, ld_kv, kv_seq_stride; v_cache, ld_v,
+ *   v_seq_stride: the per-sequence caches, laid out as for dsa_forward_decode
+ *   q [B, n_q, H] rows of d_qk values, ld_q elements apart
+ *   idx [B, n_q, k] int32 (output: S_t ascending, -1 padded), out [B, n_q, H, d_v] (dense),
  *   lse [B, n_q, H] or NULL
  * idx_dtype / attn_dtype: DSA_FP8_E4M3 with DSA_BF16 (dsa_select_prefill's threshold
  * filter per sequence: no score matrix, k <= 2048, n_k_max < 2^25; the workspace holds
@@ -268,11 +297,13 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
  */
 int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max,
                       const void* q_idx, const float* q_scale, const float* w,
-                      const void* k_cache, const float* k_cache_scale, const void* q,
-                      const void* kv_cache, const void* v_cache, int32_t H_I, int32_t d_I,
-                      int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
-                      int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out,
-                      float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+                      const void* k_cache, const float* k_cache_scale, int64_t kc_seq_stride,
+                      const void* q, int64_t ld_q, const void* kv_cache, int64_t ld_kv,
+                      int64_t kv_seq_stride, const void* v_cache, int64_t ld_v,
+                      int64_t v_seq_stride, int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk,
+                      int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype,
+                      int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                      size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * dsa_indexer_scores_at -- lightning-indexer scores of the listed keys only (the scores the
@@ -316,6 +347,37 @@ int dsa_indexer_kl(const void* q, const void* kv, const int32_t* idx, const floa
                    float* p_out, dsa_stream_t stream);
 
 /*
+ * dsa_indexer_kl_dense -- forward of the indexer's KL-alignment loss in the dense warm-up
+ * stage, where the indexer learns to match the main attention's distribution over every
+ * preceding token while the rest of the model is frozen (juhe.plus explainer, section
+ * 阶段一：Dense Warm-up; 53ai.com V3.2-Exp summary, section 持续预训练).  For query row t of
+ * sequence b at position pos = (q_pos ? q_pos[b] : 0) + t, over its keys s = 0 .. n-1,
+ * n = min(pos + 1, n_k):
+ *     lse_h   = ln sum_s exp(sm_scale q_h . kv_s)                 (dense attention, head h)
+ *     p_t(s)  = (1/H) sum_h exp(sm_scale q_h . kv_s - lse_h)      (heads summed, L1-normalised)
+ *     KL_t    = sum_s p_t(s) (ln p_t(s) - ln softmax_s(I[t, :n])(s))
+ * with I the lightning-indexer scores (the same scores dsa_indexer writes, bit for bit).
+ * Nothing of size L x L is stored: the workspace holds the score rows of a chunk of query
+ * rows at a time.
+ *
+ *   q_idx, q_scale, k_idx, k_scale, w: indexer operands as for dsa_indexer (B sequences,
+ *                n_q query rows, n_k keys; idx_dtype DSA_FP8_E4M3 or DSA_F32)
+ *   q [B, n_q, H, d_qk], kv [B, n_k, d_qk]: attention operands (attn_dtype DSA_BF16 with
+ *                H = 128, d_qk = 576; or DSA_F32 with H <= 64, d_qk <= 256, n_k <= 4096), dense
+ *   q_pos [B] int32 or NULL (device)
+ *   kl  [B, n_q] fp32 output (0 for a row that sees no key)
+ *   lse [B, n_q, H] fp32 output or NULL: the dense attention's lse (-inf for such a row)
+ * Workspace: dsa_workspace_size(DSA_OP_KL_DENSE, B, n_q, n_k, H, 0, 1, attn_dtype) (the score
+ * rows of up to 2^28 / (B n_k) query rows per pass, at least one).
+ */
+int dsa_indexer_kl_dense(const void* q_idx, const float* q_scale, const void* k_idx,
+                         const float* k_scale, const float* w, const void* q, const void* kv,
+                         int64_t B, int64_t n_q, int64_t n_k, const int32_t* q_pos, int32_t H_I,
+                         int32_t d_I, int32_t H, int32_t d_qk, float sm_scale, int32_t idx_dtype,
+                         int32_t attn_dtype, float* kl, float* lse, void* ws, size_t ws_bytes,
+                         dsa_stream_t stream);
+
+/*
  * dsa_fp8_quantize_rows -- FP8 E4M3FN quantisation of the indexer operands, the step
  * before the lightning indexer (the indexer runs in FP8: 53ai.com V3.2-Exp summary,
  * section 创新架构; juhe.plus explainer, section 第一步：Lightning Indexer).  Per row of
@@ -345,12 +407,14 @@ int dsa_fp8_quantize_rows(const void* x, int32_t x_dtype, int64_t n_rows, int64_
  *   k_new        [B, n_new, d_I] (dtype DSA_BF16 or DSA_F32)
  *   pos          [B] int32, device: first cache row of each sequence's new keys; rows at
  *                or past n_k_max (or below 0) are skipped on the device
- *   k_cache      [B, n_k_max, d_I] uint8, k_cache_scale [B, n_k_max] fp32 (updated in place)
+ *   k_cache      uint8 codes, sequence b row s at k_cache + (b * kc_seq_stride + s) * d_I;
+ *   k_cache_scale fp32, sequence b row s at k_cache_scale[b * kc_seq_stride + s]
+ *                (kc_seq_stride >= n_k_max rows; updated in place)
  * Buffers are device memory owned by the caller; nothing is allocated.
  */
 int dsa_kcache_append(const void* k_new, int32_t dtype, int64_t B, int64_t n_new, int32_t d_I,
-                      const int32_t* pos, int64_t n_k_max, uint8_t* k_cache,
-                      float* k_cache_scale, dsa_stream_t stream);
+                      const int32_t* pos, int64_t n_k_max, int64_t kc_seq_stride,
+                      uint8_t* k_cache, float* k_cache_scale, dsa_stream_t stream);
 
 #ifdef __cplusplus
 }

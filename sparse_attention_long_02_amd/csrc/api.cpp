@@ -64,6 +64,26 @@ int check_attn_shape(int32_t H, int32_t d_qk, int32_t d_v, int32_t k, int32_t dt
   return DSA_OK;
 }
 
+// Element strides of the attention operands: a row stride covers the row's width; bf16
+// rows start 16-byte aligned (the kernels load 16-byte units), so bf16 strides are
+// multiples of 8 elements.  A sequence stride covers its n_rows rows.
+int check_ld(const char* name, int64_t ld, int64_t width, int32_t dtype) {
+  REQUIRE(ld >= width, "%s (%lld) must be >= the row width %lld", name, (long long)ld, (long long)width);
+  if (dtype == DSA_BF16) REQUIRE(ld % 8 == 0, "%s (%lld) must be a multiple of 8 elements", name, (long long)ld);
+  return DSA_OK;
+}
+int check_seq(const char* name, int64_t bs, int64_t n_rows, int64_t ld, int32_t dtype) {
+  REQUIRE(bs >= n_rows * ld, "%s (%lld) must be >= %lld rows x %lld", name, (long long)bs, (long long)n_rows,
+          (long long)ld);
+  if (dtype == DSA_BF16) REQUIRE(bs % 8 == 0, "%s (%lld) must be a multiple of 8 elements", name, (long long)bs);
+  return DSA_OK;
+}
+#define CHECK(x)            \
+  do {                      \
+    const int st_ = (x);    \
+    if (st_) return st_;    \
+  } while (0)
+
 size_t decode_scores_bytes(int64_t B, int64_t n_k) { return (size_t)B * n_k * sizeof(float); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -113,11 +133,12 @@ static size_t sel_bytes(int64_t B, int64_t n_q, int64_t n_k) {
 }
 
 // rows 0 .. n_q - 1 of each of B sequences (row r at position (q_pos ? q_pos[b] : 0) + r)
+// (kbs: key rows between the sequences of k8 / ks; 0 means n_k)
 static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks, const float* w,
                       int64_t B, int64_t n_q, int64_t n_k, const int32_t* q_pos, int32_t k, int32_t* idx, void* ws,
-                      size_t ws_bytes, hipStream_t s) {
+                      size_t ws_bytes, hipStream_t s, int64_t kbs = 0) {
   SUPPORT(n_k <= FUSED_MAX_KEYS, "FP8 selection supports up to %lld keys", (long long)FUSED_MAX_KEYS);
-  dsa::PrefillTopkArgs pa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, k, idx};
+  dsa::PrefillTopkArgs pa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, k, idx, nullptr, kbs};
   if (!sel_filtered(n_k)) return hip_status(dsa::launch_prefill_topk(pa, s), "indexer/top-k launch");
   SelWs sw;
   const size_t need = sel_ws_bytes(B, n_q, n_k, &sw, ws);
@@ -129,13 +150,14 @@ static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, con
   for (int64_t r0 = 0; r0 < n_q; r0 += rows) {
     const int64_t n = rows < n_q - r0 ? rows : n_q - r0;
     const int64_t rp = dsa::dense_rows_pad(n);
-    dsa::DenseIdxArgs sa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, sw.samp, ld_s, dsa::SEL_SAMPLE_STRIDE};
+    dsa::DenseIdxArgs sa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, sw.samp, ld_s, dsa::SEL_SAMPLE_STRIDE,
+                         nullptr, nullptr, nullptr, kbs};
     int st = hip_status(dsa::launch_idx_dense(sa, s), "key-sample indexer launch");
     if (st) return st;
     dsa::SelThresholdArgs ta{sw.samp, ld_s, rp, B, n, n_k, q_pos, r0, k, sw.thr};
     st = hip_status(dsa::launch_sel_threshold(ta, s), "threshold launch");
     if (st) return st;
-    dsa::DenseIdxArgs fa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, nullptr, 0, 1, sw.thr, sw.cand, sw.cnt};
+    dsa::DenseIdxArgs fa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, nullptr, 0, 1, sw.thr, sw.cand, sw.cnt, kbs};
     st = hip_status(dsa::launch_idx_dense(fa, s), "filtering indexer launch");
     if (st) return st;
     dsa::SelCandArgs ca{sw.cand, sw.cnt, rp, B, n, n_k, q_pos, r0, k, idx, n_q, r0, sw.redo};
@@ -146,12 +168,34 @@ static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, con
   return hip_status(dsa::launch_prefill_topk(pa, s), "exact selection of the remaining rows");
 }
 
+// dense warm-up KL: query rows per pass, so that one pass's score rows take at most 2^28
+// floats (1 GiB)
+static int64_t kl_dense_rows(int64_t B, int64_t n_q, int64_t n_k) {
+  int64_t r = ((int64_t)1 << 28) / (B * (n_k > 0 ? n_k : 1));
+  r = r < 1 ? 1 : r;
+  r = r < 65535 ? r : 65535;
+  return r < n_q ? r : n_q;
+}
+static size_t kl_dense_ws_bytes(int64_t B, int64_t n_q, int64_t n_k) {
+  return align256((size_t)B * kl_dense_rows(B, n_q, n_k) * n_k * sizeof(float));
+}
+
 // the fp32 chunk path ranks materialised scores; the FP8 path filters on chip
 size_t chunk_scores_bytes(int64_t B, int64_t n_q, int64_t n_k, int32_t attn_dtype) {
   return attn_dtype == DSA_F32 ? align256((size_t)B * n_q * n_k * sizeof(float)) : sel_bytes(B, n_q, n_k);
 }
 
 }  // namespace
+
+namespace dsa {
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+}  // namespace dsa
 
 extern "C" {
 
@@ -188,6 +232,8 @@ size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32
       return dsa::sparse_mla_bwd_ws_bytes(B, n_q, k, dtype);
     case DSA_OP_CHUNK:
       return chunk_scores_bytes(B, n_q, n_k, dtype) + dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, dtype);
+    case DSA_OP_KL_DENSE:
+      return kl_dense_ws_bytes(B, n_q, n_k);
     default:
       return 0;
   }
@@ -228,19 +274,24 @@ int dsa_topk(const float* scores, int64_t ld_scores, int64_t B, int64_t n_rows, 
   return hip_status(dsa::launch_topk(a, (hipStream_t)stream), "dsa_topk launch");
 }
 
-int dsa_sparse_mla(const void* q, const void* kv, const void* v, const int32_t* idx, int64_t B, int64_t n_q,
-                   int64_t n_k, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t dtype,
-                   void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+int dsa_sparse_mla(const void* q, int64_t ld_q, const void* kv, int64_t ld_kv, const void* v, int64_t ld_v,
+                   const int32_t* idx, int64_t B, int64_t n_q, int64_t n_k, int32_t H, int32_t d_qk, int32_t d_v,
+                   int32_t k, float sm_scale, int32_t dtype, void* out, float* lse, void* ws, size_t ws_bytes,
+                   dsa_stream_t stream) {
   REQUIRE(q && kv && idx && out, "null pointer argument");
   REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k > 0, "B, n_q, n_k must be positive");
   int st = check_attn_shape(H, d_qk, d_v, k, dtype, v != nullptr);
   if (st) return st;
+  CHECK(check_ld("ld_q", ld_q, d_qk, dtype));
+  CHECK(check_ld("ld_kv", ld_kv, d_qk, dtype));
+  if (v) CHECK(check_ld("ld_v", ld_v, d_v, dtype));
   if (dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out), "bf16 operands must be 16-byte aligned");
   REQUIRE(n_q * H <= 2147483647LL, "n_q * H too large");
   const size_t need = dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, dtype);
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "dsa_sparse_mla needs %zu workspace bytes (got %zu)", need, ws_bytes);
-  dsa::MlaArgs a{q, kv, v, idx, B, n_q, n_k, H, d_qk, d_v, k, sm_scale, dtype, out, lse, ws, ws_bytes};
+  dsa::MlaArgs a{q, kv, v, idx, B, n_q, n_k, H, d_qk, d_v, k, sm_scale, dtype, out, lse, ws, ws_bytes,
+                 ld_q, ld_kv, v ? ld_v : 0, n_k * ld_kv, v ? n_k * ld_v : 0};
   return hip_status(dsa::launch_sparse_mla(a, (hipStream_t)stream), "dsa_sparse_mla launch");
 }
 
@@ -279,16 +330,19 @@ int dsa_select_prefill(const void* q_idx, const float* q_scale, const void* k_id
 }
 
 int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
-                        const float* w, const void* q, const void* kv, const void* v, int64_t L, int32_t H_I,
-                        int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
-                        int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
-                        size_t ws_bytes, dsa_stream_t stream) {
+                        const float* w, const void* q, int64_t ld_q, const void* kv, int64_t ld_kv, const void* v,
+                        int64_t ld_v, int64_t L, int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v,
+                        int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out,
+                        float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
   REQUIRE(q_idx && q_scale && k_idx && k_scale && w && q && kv && idx && out, "null pointer argument");
   REQUIRE(L > 0 && L <= 2147483647LL, "L must be in [1, 2^31)");
   int st = check_indexer_shape(H_I, d_I, idx_dtype);
   if (st) return st;
   st = check_attn_shape(H, d_qk, d_v, k, attn_dtype, v != nullptr);
   if (st) return st;
+  CHECK(check_ld("ld_q", ld_q, d_qk, attn_dtype));
+  CHECK(check_ld("ld_kv", ld_kv, d_qk, attn_dtype));
+  if (v) CHECK(check_ld("ld_v", ld_v, d_v, attn_dtype));
   if (idx_dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_idx), "FP8 operands must be 16-byte aligned");
   if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out), "bf16 operands must be 16-byte aligned");
   SUPPORT(idx_dtype == attn_dtype || (idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16),
@@ -304,15 +358,32 @@ int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_i
   st = select_prefill(q_idx, q_scale, k_idx, k_scale, w, L, H_I, d_I, k, idx_dtype, idx, ws, s_bytes, s);
   if (st) return st;
   dsa::MlaArgs a{q, kv, v, idx, 1, L, L, H, d_qk, d_v, k, sm_scale, attn_dtype, out, lse,
-                 (char*)ws + s_bytes, ws_bytes - s_bytes};
+                 (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v ? ld_v : 0, L * ld_kv, v ? L * ld_v : 0};
   return hip_status(dsa::launch_sparse_mla(a, s), "prefill sparse attention launch");
 }
 
+// Strides of the per-sequence caches and of q (decode and chunks).
+static int check_cache_strides(int64_t n_k_max, int64_t kc_seq_stride, const void* v_cache, int64_t ld_q, int64_t ld_kv,
+                        int64_t kv_seq_stride, int64_t ld_v, int64_t v_seq_stride, int32_t d_qk, int32_t d_v,
+                        int32_t attn_dtype) {
+  REQUIRE(kc_seq_stride >= n_k_max, "kc_seq_stride (%lld) must be >= n_k_max (%lld)", (long long)kc_seq_stride,
+          (long long)n_k_max);
+  CHECK(check_ld("ld_q", ld_q, d_qk, attn_dtype));
+  CHECK(check_ld("ld_kv", ld_kv, d_qk, attn_dtype));
+  CHECK(check_seq("kv_seq_stride", kv_seq_stride, n_k_max, ld_kv, attn_dtype));
+  if (v_cache) {
+    CHECK(check_ld("ld_v", ld_v, d_v, attn_dtype));
+    CHECK(check_seq("v_seq_stride", v_seq_stride, n_k_max, ld_v, attn_dtype));
+  }
+  return DSA_OK;
+}
+
 int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx, const float* q_scale,
-                       const float* w, const void* k_cache, const float* k_cache_scale, const void* q,
-                       const void* kv_cache, const void* v_cache, int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk,
-                       int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype, int32_t* idx,
-                       void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+                       const float* w, const void* k_cache, const float* k_cache_scale, int64_t kc_seq_stride,
+                       const void* q, int64_t ld_q, const void* kv_cache, int64_t ld_kv, int64_t kv_seq_stride,
+                       const void* v_cache, int64_t ld_v, int64_t v_seq_stride, int32_t H_I, int32_t d_I, int32_t H,
+                       int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype,
+                       int32_t* idx, void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
   REQUIRE(ctx_len && q_idx && q_scale && w && k_cache && k_cache_scale && q && kv_cache && idx && out,
           "null pointer argument");
   REQUIRE(B > 0 && B <= 65535 && n_k_max > 0, "B in [1, 65535] and n_k_max > 0 required");
@@ -320,6 +391,8 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
   if (st) return st;
   st = check_attn_shape(H, d_qk, d_v, k, attn_dtype, v_cache != nullptr);
   if (st) return st;
+  CHECK(check_cache_strides(n_k_max, kc_seq_stride, v_cache, ld_q, ld_kv, kv_seq_stride, ld_v, v_seq_stride, d_qk,
+                            d_v, attn_dtype));
   SUPPORT(n_k_max <= dsa::TOPK_MAX_N, "decode supports n_k_max <= %lld", (long long)dsa::TOPK_MAX_N);
   if (idx_dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_cache), "FP8 operands must be 16-byte aligned");
   if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv_cache) && aligned16(out), "bf16 operands must be 16-byte aligned");
@@ -332,14 +405,15 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
   float* scores = (float*)ws;
   // the query of sequence b is its row 0, at position ctx_len[b] - 1
   dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, H_I, d_I,
-                      idx_dtype, 0, 1, scores, n_k_max};
+                      idx_dtype, 0, 1, scores, n_k_max, kc_seq_stride};
   st = hip_status(dsa::launch_indexer(ia, s), "decode indexer launch");
   if (st) return st;
   dsa::TopkArgs ta{scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx};
   st = hip_status(dsa::launch_topk(ta, s), "decode top-k launch");
   if (st) return st;
   dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, 1, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
-                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes};
+                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v_cache ? ld_v : 0,
+                 kv_seq_stride, v_cache ? v_seq_stride : 0};
   return hip_status(dsa::launch_sparse_mla(a, s), "decode sparse attention launch");
 }
 
@@ -357,20 +431,25 @@ int dsa_fp8_quantize_rows(const void* x, int32_t x_dtype, int64_t n_rows, int64_
 }
 
 int dsa_kcache_append(const void* k_new, int32_t dtype, int64_t B, int64_t n_new, int32_t d_I, const int32_t* pos,
-                      int64_t n_k_max, uint8_t* k_cache, float* k_cache_scale, dsa_stream_t stream) {
+                      int64_t n_k_max, int64_t kc_seq_stride, uint8_t* k_cache, float* k_cache_scale,
+                      dsa_stream_t stream) {
   REQUIRE(k_new && pos && k_cache && k_cache_scale, "null pointer argument");
   REQUIRE(dtype == DSA_BF16 || dtype == DSA_F32, "dtype must be DSA_BF16 or DSA_F32 (got %d)", dtype);
   REQUIRE(B > 0 && B <= 65535 && n_new > 0 && d_I > 0 && n_k_max > 0, "B in [1, 65535], n_new, d_I, n_k_max > 0");
   REQUIRE(n_new <= (int64_t)4 * 2147483647, "n_new too large");
-  dsa::QuantArgs a{k_new, dtype, B, n_new, d_I, d_I, pos, n_k_max, k_cache, d_I, k_cache_scale, 1, 1};
+  REQUIRE(kc_seq_stride >= n_k_max, "kc_seq_stride (%lld) must be >= n_k_max (%lld)", (long long)kc_seq_stride,
+          (long long)n_k_max);
+  dsa::QuantArgs a{k_new, dtype, B, n_new, d_I, d_I, pos, n_k_max, k_cache, d_I, k_cache_scale, 1, 1, kc_seq_stride};
   return hip_status(dsa::launch_fp8_quant_rows(a, (hipStream_t)stream), "key-cache append launch");
 }
 
 int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max, const void* q_idx,
                       const float* q_scale, const float* w, const void* k_cache, const float* k_cache_scale,
-                      const void* q, const void* kv_cache, const void* v_cache, int32_t H_I, int32_t d_I, int32_t H,
-                      int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype,
-                      int32_t* idx, void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+                      int64_t kc_seq_stride, const void* q, int64_t ld_q, const void* kv_cache, int64_t ld_kv,
+                      int64_t kv_seq_stride, const void* v_cache, int64_t ld_v, int64_t v_seq_stride, int32_t H_I,
+                      int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
+                      int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                      size_t ws_bytes, dsa_stream_t stream) {
   REQUIRE(q_pos && q_idx && q_scale && w && k_cache && k_cache_scale && q && kv_cache && idx && out,
           "null pointer argument");
   REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k_max > 0, "B in [1, 65535], n_q > 0 and n_k_max > 0 required");
@@ -381,6 +460,8 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
   if (st) return st;
   SUPPORT(idx_dtype == attn_dtype || (idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16),
           "a chunk pairs an FP8 indexer with bf16 attention, or fp32 with fp32");
+  CHECK(check_cache_strides(n_k_max, kc_seq_stride, v_cache, ld_q, ld_kv, kv_seq_stride, ld_v, v_seq_stride, d_qk,
+                            d_v, attn_dtype));
   if (idx_dtype == DSA_FP8_E4M3) {
     REQUIRE(aligned16(q_idx) && aligned16(k_cache), "FP8 operands must be 16-byte aligned");
     SUPPORT(k <= 2048, "FP8 selection keeps at most 2048 keys (k = %d)", k);
@@ -399,11 +480,11 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
   hipStream_t s = (hipStream_t)stream;
   if (idx_dtype == DSA_FP8_E4M3) {
     st = select_fp8((const uint8_t*)q_idx, q_scale, (const uint8_t*)k_cache, k_cache_scale, w, B, n_q, n_k_max,
-                    q_pos, k, idx, ws, s_bytes, s);
+                    q_pos, k, idx, ws, s_bytes, s, kc_seq_stride);
   } else {
     float* scores = (float*)ws;
     dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, n_q, n_k_max, q_pos, 0, H_I, d_I,
-                        idx_dtype, 0, n_q, scores, n_k_max};
+                        idx_dtype, 0, n_q, scores, n_k_max, kc_seq_stride};
     st = hip_status(dsa::launch_indexer(ia, s), "chunk indexer launch");
     if (st) return st;
     dsa::TopkArgs ta{scores, n_k_max, B, n_q, n_k_max, q_pos, 0, 0, k, idx};
@@ -411,7 +492,8 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
   }
   if (st) return st;
   dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, n_q, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
-                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes};
+                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v_cache ? ld_v : 0,
+                 kv_seq_stride, v_cache ? v_seq_stride : 0};
   return hip_status(dsa::launch_sparse_mla(a, s), "chunk sparse attention launch");
 }
 
@@ -451,6 +533,46 @@ int dsa_indexer_kl(const void* q, const void* kv, const int32_t* idx, const floa
   }
   dsa::KlArgs a{q, kv, idx, lse, idx_scores, B, n_q, n_k, H, d_qk, k, sm_scale, dtype, kl, p_out};
   return hip_status(dsa::launch_indexer_kl(a, (hipStream_t)stream), "dsa_indexer_kl launch");
+}
+
+int dsa_indexer_kl_dense(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                         const float* w, const void* q, const void* kv, int64_t B, int64_t n_q, int64_t n_k,
+                         const int32_t* q_pos, int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, float sm_scale,
+                         int32_t idx_dtype, int32_t attn_dtype, float* kl, float* lse, void* ws, size_t ws_bytes,
+                         dsa_stream_t stream) {
+  REQUIRE(q_idx && q_scale && k_idx && k_scale && w && q && kv && kl, "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k > 0, "B in [1, 65535] and n_q, n_k > 0 required");
+  REQUIRE(n_q <= 2147483647LL && n_k <= 2147483647LL, "n_q, n_k must be < 2^31");
+  CHECK(check_indexer_shape(H_I, d_I, idx_dtype));
+  REQUIRE(H > 0 && d_qk > 0, "H and d_qk must be positive");
+  if (attn_dtype == DSA_BF16) {
+    SUPPORT(H == 128 && d_qk == 576, "bf16 dense KL loss needs H = 128, d_qk = 576");
+    REQUIRE(aligned16(q) && aligned16(kv), "bf16 operands must be 16-byte aligned");
+  } else if (attn_dtype == DSA_F32) {
+    SUPPORT(H <= 64 && d_qk <= 256 && n_k <= dsa::KL_DENSE_F32_MAX_N,
+            "fp32 dense KL loss needs H <= 64, d_qk <= 256, n_k <= %lld", (long long)dsa::KL_DENSE_F32_MAX_N);
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "dense KL attention dtype %d is not DSA_BF16 or DSA_F32", attn_dtype);
+  }
+  if (idx_dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_idx), "FP8 operands must be 16-byte aligned");
+  const size_t need = kl_dense_ws_bytes(B, n_q, n_k);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "dsa_indexer_kl_dense needs %zu workspace bytes (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  float* scores = (float*)ws;
+  const int64_t rows = kl_dense_rows(B, n_q, n_k);
+  for (int64_t r0 = 0; r0 < n_q; r0 += rows) {
+    const int64_t nr = rows < n_q - r0 ? rows : n_q - r0;
+    dsa::IndexerArgs ia{q_idx, q_scale, k_idx, k_scale, w, B, n_q, n_k, q_pos, 0, H_I, d_I, idx_dtype, r0, nr,
+                        scores, n_k};
+    int st = hip_status(dsa::launch_indexer(ia, s), "dense KL indexer launch");
+    if (st) return st;
+    dsa::KlDenseArgs ka{q, kv, scores, n_k, q_pos, r0, nr, B, n_q, n_k, H, d_qk, sm_scale, attn_dtype, kl, lse};
+    st = hip_status(dsa::launch_indexer_kl_dense(ka, s), "dense KL launch");
+    if (st) return st;
+  }
+  return DSA_OK;
 }
 
 int dsa_sparse_mla_backward(const void* q, const void* kv, const void* v, const int32_t* idx, const void* out,

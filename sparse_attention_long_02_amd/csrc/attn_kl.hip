@@ -360,6 +360,264 @@ __global__ __launch_bounds__(256) void indexer_kl_f32_kernel(
   if (threadIdx.x == 0) kl[qrow] = acc;
 }
 
+// ---------------------------------------------------------------------------------------
+// KL loss of the dense warm-up: every key s <= pos(t), the attention's own dense lse
+// ---------------------------------------------------------------------------------------
+// Per query row t (position pos, keys 0 .. n-1 with n = min(pos + 1, n_k)):
+//     LSE_I   = ln sum_{s<n} exp(I[t,s])                (the index scores of the whole row)
+//     lse_h   = ln sum_{s<n} exp(sm_scale q_h . kv_s)     (dense attention, every head)
+//     p(s)    = (1/H) sum_h exp(sm_scale q_h . kv_s - lse_h)
+//     KL_t    = sum_{s<n} p(s) (ln p(s) - I[t,s] + LSE_I)
+// The score row comes from the caller's workspace (written by the indexer just before);
+// the rows of kv are contiguous, so chunk c of a row is keys 32c .. 32c+31.
+
+// The ids of a dense chunk (see kl_ids): keys are their own ids.
+__device__ __forceinline__ KlIds dense_ids(int c, int wv, int lane) {
+  return KlIds{c * KC + 8 * wv + (lane & 7), c * KC + 8 * wv + (lane >> 3)};
+}
+
+// log2-domain log-sum-exp of a block's values (NT threads): combines per-thread (m, s)
+__device__ __forceinline__ void merge_lse2(float& m, float& s, float om, float os) {
+  const float M = fmaxf(m, om);
+  s = (M == -INFINITY) ? 0.f : s * exp2f(m - M) + os * exp2f(om - M);
+  m = M;
+}
+
+// grid.x = rows of the launch, grid.y = B.  Row i of sequence b is query row row_begin + i
+// at position (q_pos ? q_pos[b] : 0) + row_begin + i; its index scores are at
+// isc + (b * n_rows + i) * ld_s.  Two sweeps over the keys, two chunk buffers each: the
+// first forms every head's lse (online, per lane, merged across lanes at the end), the
+// second the KL terms exactly as indexer_kl_bf16_kernel does for a selection.
+__global__ __launch_bounds__(KL_WAVES * 64, 2) void indexer_kl_dense_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const float* __restrict__ isc, int64_t ld_s,
+    const int32_t* __restrict__ q_pos, int64_t row_begin, int64_t n_rows, int64_t n_q, int64_t n_k,
+    float scale_log2, float* __restrict__ kl, float* __restrict__ lse_out) {
+  __shared__ __align__(16) uint8_t buf0[CHUNK_BYTES];
+  __shared__ __align__(16) uint8_t buf1[CHUNK_BYTES];
+  __shared__ float xs[2][KL_WAVES][KC];
+  __shared__ float red[2][KL_WAVES];
+
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.y;
+  const int64_t row = row_begin + blockIdx.x;
+  const int64_t qrow = (int64_t)b * n_q + row;
+  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + row;
+  const int64_t n64 = pos + 1 < n_k ? pos + 1 : n_k;
+  const int n = (int)(n64 > 0 ? n64 : 0);
+  const float* srow = isc + ((int64_t)b * n_rows + blockIdx.x) * ld_s;
+  const uint16_t* kvb = kv + (int64_t)b * n_k * MDQK;
+
+  if (n == 0) {  // no key before the query: no distribution (uniform over the block)
+    if (tid == 0) kl[qrow] = 0.f;
+    if (lse_out && tid < MH) lse_out[qrow * MH + tid] = -INFINITY;
+    return;
+  }
+
+  // ---- LSE_I over the whole score row (log2 units), every thread then the block
+  float mi = -INFINITY, si = 0.f;
+  for (int s = tid; s < n; s += KL_WAVES * 64) {
+    const float x = srow[s] * LOG2E;
+    if (x > mi) {
+      si = si * exp2f(mi - x) + 1.f;
+      mi = x;
+    } else {
+      si += exp2f(x - mi);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) merge_lse2(mi, si, __shfl_xor(mi, off, WAVE), __shfl_xor(si, off, WAVE));
+  if (l == 0) {
+    red[0][wv] = mi;
+    red[1][wv] = si;
+  }
+  __syncthreads();
+  float lsei2 = -INFINITY;
+  {
+    float m = red[0][0], sm = red[1][0];
+#pragma unroll
+    for (int w2 = 1; w2 < KL_WAVES; ++w2) merge_lse2(m, sm, red[0][w2], red[1][w2]);
+    lsei2 = m + log2f(sm);
+  }
+
+  // A operands of S = Q K^T: head 32w + l%32, values 16ds + 8g .. +7
+  v8bf Qa[D_STEPS];
+  {
+    const uint16_t* qh = q + (qrow * MH + 32 * wv + (l & 31)) * MDQK + 8 * g;
+#pragma unroll
+    for (int ds = 0; ds < D_STEPS; ++ds) Qa[ds] = *reinterpret_cast<const v8bf*>(qh + 16 * ds);
+#pragma unroll
+    for (int ds = 0; ds < D_STEPS; ++ds) asm volatile("" : "+v"(Qa[ds]));
+  }
+  const int nch = (n + KC - 1) / KC;
+  const uint32_t nk = (uint32_t)n;  // keys past the row's position read row 0 and are masked
+  const KOff ko = k_offsets();
+
+  // ---- sweep 1: every head's log2-sum-exp.  Lane l holds key 32c + l%32 and the 16 heads
+  // 32w + 8(r/4) + 4g + r%4; per lane and head a running reference m (moved only when a
+  // logit passes it by 8) and a sum of exp2(x - m).
+  float L2[16], sr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    L2[r] = -1e30f;  // finite: exp2(-inf - m) is 0, and no -inf - -inf arises
+    sr[r] = 0.f;
+  }
+  kl_gather(lds_addr(buf0), kvb, dense_ids(0, wv, l), nk, wv, l);
+  for (int c = 0; c < nch; ++c) {
+    VMCNT(0);
+    block_barrier();
+    if (c + 1 < nch) kl_gather(lds_addr((c & 1) ? buf0 : buf1), kvb, dense_ids(c + 1, wv, l), nk, wv, l);
+    v16f S = {};
+    const uint8_t* cur = (c & 1) ? buf1 : buf0;
+#pragma unroll
+    for (int ds = 0; ds < D_STEPS; ++ds) S = mfma_bf16_32x32x16(Qa[ds], k_frag(cur, k_off(ko, ds)), S);
+    const bool valid = c * KC + (l & 31) < n;
+    float x[16];
+    bool up = false;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = valid ? S[r] * scale_log2 : -INFINITY;
+      up |= x[r] > L2[r] + 8.f;
+    }
+    if (ballot(up)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float nm = fmaxf(L2[r], x[r]);
+        sr[r] *= exp2f(L2[r] - nm);
+        L2[r] = nm;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sr[r] += __builtin_amdgcn_exp2f(x[r] - L2[r]);
+  }
+  // merge over the 32 lanes of each half (they hold the same heads)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1)
+      merge_lse2(L2[r], sr[r], __shfl_xor(L2[r], off, WAVE), __shfl_xor(sr[r], off, WAVE));
+    L2[r] += log2f(sr[r]);
+  }
+  if (lse_out && (l & 31) == 0)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lse_out[qrow * MH + 32 * wv + 8 * (r >> 2) + 4 * g + (r & 3)] = L2[r] * LN2;
+
+  // ---- sweep 2: p(s) and the KL terms (wave 0 adds the four waves' head sums one chunk later)
+  VMCNT(0);
+  block_barrier();  // every wave is done with both buffers
+  kl_gather(lds_addr(buf0), kvb, dense_ids(0, wv, l), nk, wv, l);
+  float acc = 0.f;
+  float a_s = 0.f;
+  bool a_ok = false;
+  for (int c = 0; c < nch; ++c) {
+    VMCNT(0);
+    block_barrier();
+    if (c + 1 < nch) kl_gather(lds_addr((c & 1) ? buf0 : buf1), kvb, dense_ids(c + 1, wv, l), nk, wv, l);
+    const int key = c * KC + (l & 31);
+    const bool c_ok = key < n;
+    const float c_s = (wv == 0 && c_ok) ? srow[key] : 0.f;
+    v16f S = {};
+    const uint8_t* cur = (c & 1) ? buf1 : buf0;
+#pragma unroll
+    for (int ds = 0; ds < D_STEPS; ++ds) S = mfma_bf16_32x32x16(Qa[ds], k_frag(cur, k_off(ko, ds)), S);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ps += __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], scale_log2, -L2[r]));
+    ps += xor32(ps);
+    if (l < KC) xs[c & 1][wv][l] = ps;
+    if (wv == 0 && c > 0) {
+      const float* xx = xs[(c - 1) & 1][0];
+      const float p = (xx[l & 31] + xx[KC + (l & 31)] + xx[2 * KC + (l & 31)] + xx[3 * KC + (l & 31)]) * (1.f / MH);
+      if (l < KC && a_ok && p > 0.f) acc += p * ((log2f(p) - (a_s * LOG2E - lsei2)) * LN2);
+    }
+    a_ok = c_ok;
+    a_s = c_s;
+  }
+  VMCNT(0);
+  block_barrier();
+  if (wv == 0) {
+    const float* xx = xs[(nch - 1) & 1][0];
+    const float p = (xx[l & 31] + xx[KC + (l & 31)] + xx[2 * KC + (l & 31)] + xx[3 * KC + (l & 31)]) * (1.f / MH);
+    if (l < KC && a_ok && p > 0.f) acc += p * ((log2f(p) - (a_s * LOG2E - lsei2)) * LN2);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, WAVE);
+    if (l == 0) kl[qrow] = acc;
+  }
+}
+
+// fp32 operands (small shapes: H <= 64, d_qk <= 256, n_k <= KLD_F32_MAX_N): one block per
+// query row; each head's logits go through LDS, p accumulates there.
+constexpr int KLD_F32_MAX_N = 4096;
+__global__ __launch_bounds__(256) void indexer_kl_dense_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kv, const float* __restrict__ isc, int64_t ld_s,
+    const int32_t* __restrict__ q_pos, int64_t row_begin, int64_t n_rows, int64_t n_q, int64_t n_k, int H,
+    int d_qk, float sm_scale, float* __restrict__ kl, float* __restrict__ lse_out) {
+  __shared__ float red[4];
+  __shared__ float z[KLD_F32_MAX_N];
+  __shared__ float pp[KLD_F32_MAX_N];
+  const int b = blockIdx.y;
+  const int64_t row = row_begin + blockIdx.x;
+  const int64_t qrow = (int64_t)b * n_q + row;
+  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + row;
+  const int64_t n64 = pos + 1 < n_k ? pos + 1 : n_k;
+  const int n = (int)(n64 > 0 ? n64 : 0);
+  const float* srow = isc + ((int64_t)b * n_rows + blockIdx.x) * ld_s;
+  const float* kvb = kv + (int64_t)b * n_k * d_qk;
+  if (n == 0) {
+    if (threadIdx.x == 0) kl[qrow] = 0.f;
+    if (lse_out)
+      for (int h = threadIdx.x; h < H; h += 256) lse_out[qrow * H + h] = -INFINITY;
+    return;
+  }
+  float m = -INFINITY;
+  for (int s = threadIdx.x; s < n; s += 256) m = fmaxf(m, srow[s]);
+  m = block_reduce(m, red, true);
+  float sum = 0.f;
+  for (int s = threadIdx.x; s < n; s += 256) sum += expf(srow[s] - m);
+  sum = block_reduce(sum, red, false);
+  const float lsei = m + logf(sum);
+  for (int s = threadIdx.x; s < n; s += 256) pp[s] = 0.f;
+  for (int h = 0; h < H; ++h) {
+    const float* qh = q + (qrow * H + h) * d_qk;
+    float mh = -INFINITY;
+    for (int s = threadIdx.x; s < n; s += 256) {
+      const float* kr = kvb + (int64_t)s * d_qk;
+      float dot = 0.f;
+      for (int d = 0; d < d_qk; ++d) dot = __fmaf_rn(qh[d], kr[d], dot);
+      z[s] = dot * sm_scale;
+      mh = fmaxf(mh, z[s]);
+    }
+    mh = block_reduce(mh, red, true);
+    float sh = 0.f;
+    for (int s = threadIdx.x; s < n; s += 256) sh += expf(z[s] - mh);
+    sh = block_reduce(sh, red, false);
+    const float lh = mh + logf(sh);
+    if (lse_out && threadIdx.x == 0) lse_out[qrow * H + h] = lh;
+    for (int s = threadIdx.x; s < n; s += 256) pp[s] += expf(z[s] - lh);
+  }
+  float acc = 0.f;
+  for (int s = threadIdx.x; s < n; s += 256) {
+    const float p = pp[s] / (float)H;
+    if (p > 0.f) acc += p * (logf(p) - (srow[s] - lsei));
+  }
+  acc = block_reduce(acc, red, false);
+  if (threadIdx.x == 0) kl[qrow] = acc;
+}
+
+hipError_t launch_indexer_kl_dense(const KlDenseArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)a.n_rows, (unsigned)a.B);
+  if (a.dtype == DSA_F32) {
+    hipLaunchKernelGGL(indexer_kl_dense_f32_kernel, grid, dim3(256), 0, st, (const float*)a.q, (const float*)a.kv,
+                       a.scores, a.ld_s, a.q_pos, a.row_begin, a.n_rows, a.n_q, a.n_k, a.H, a.d_qk, a.sm_scale,
+                       a.kl, a.lse);
+  } else {
+    hipLaunchKernelGGL(indexer_kl_dense_bf16_kernel, grid, dim3(KL_WAVES * 64), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.kv, a.scores, a.ld_s, a.q_pos, a.row_begin, a.n_rows, a.n_q, a.n_k,
+                       a.sm_scale * LOG2E, a.kl, a.lse);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st) {
   dim3 grid((unsigned)a.n_q, (unsigned)a.B);
   if (a.dtype == DSA_F32) {

@@ -8,6 +8,9 @@
 
 namespace dsa {
 
+// Sets the calling thread's last-error message (dsa_last_error) and returns status.
+int set_error(int status, const char* fmt, ...);
+
 struct IndexerArgs {
   const void* q_idx;
   const float* q_scale;
@@ -21,6 +24,7 @@ struct IndexerArgs {
   int64_t row_begin, n_rows;
   float* scores;
   int64_t ld_scores;
+  int64_t k_bstride = 0;    // key rows between sequences of k_idx / k_scale (0: n_k)
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
 
@@ -52,6 +56,9 @@ struct MlaArgs {
   float* lse;
   void* ws;
   size_t ws_bytes;
+  // element strides (0: dense): between the head rows of q, the rows of kv and v, and the
+  // sequences of kv and v
+  int64_t ld_q = 0, ld_kv = 0, ld_v = 0, bs_kv = 0, bs_v = 0;
 };
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 // workspace of the bf16 kernel when it splits each query's keys over several blocks
@@ -74,6 +81,7 @@ struct PrefillTopkArgs {
   // null: every row.  Otherwise redo[b * n_q + r] != 0 marks the rows to select (a group of
   // 4 rows runs if any of its rows is marked) and the rows below k are left alone.
   const uint8_t* redo = nullptr;
+  int64_t k_bstride = 0;    // key rows between sequences of k8 / ks (0: n_k)
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 
@@ -107,6 +115,7 @@ struct DenseIdxArgs {
   const float* thr = nullptr;
   uint2* cand = nullptr;
   uint32_t* cnt = nullptr;
+  int64_t k_bstride = 0;    // key rows between sequences of k8 / ks (0: n_k)
 };
 inline int64_t dense_rows_pad(int64_t n_rows) { return (n_rows + 15) / 16 * 16; }
 hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st);
@@ -204,8 +213,29 @@ struct KlArgs {
 };
 hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st);
 
+// indexer KL loss of the dense warm-up (every key up to each row's position) for rows
+// row_begin .. row_begin + n_rows - 1 of each sequence, their index scores at
+// scores + (b * n_rows + i) * ld_s; writes kl [B, n_q] and the dense attention lse
+// [B, n_q, H] (or not, when null) of those rows
+struct KlDenseArgs {
+  const void* q;
+  const void* kv;
+  const float* scores;
+  int64_t ld_s;
+  const int32_t* q_pos;
+  int64_t row_begin, n_rows;
+  int64_t B, n_q, n_k;
+  int32_t H, d_qk;
+  float sm_scale;
+  int32_t dtype;
+  float* kl;
+  float* lse;
+};
+hipError_t launch_indexer_kl_dense(const KlDenseArgs& a, hipStream_t st);
+constexpr int64_t KL_DENSE_F32_MAX_N = 4096;
+
 // FP8 E4M3FN row quantiser: rows of `groups` groups; group b's row i (source row
-// b * n_per + i, ld_x elements apart) goes to destination row b * dst_per + base + i,
+// b * n_per + i, ld_x elements apart) goes to destination row b * dst_stride + base + i,
 // base = pos ? pos[b] : 0 (rows outside [0, dst_per) skipped); its scale is written
 // `repeat` times at scale[dst_row * scale_stride + r].
 struct QuantArgs {
@@ -219,6 +249,7 @@ struct QuantArgs {
   float* scale;
   int64_t scale_stride;
   int32_t repeat;
+  int64_t dst_stride = 0;  // destination rows between groups (0: dst_per)
 };
 hipError_t launch_fp8_quant_rows(const QuantArgs& a, hipStream_t st);
 

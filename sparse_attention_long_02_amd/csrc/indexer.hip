@@ -16,7 +16,7 @@ namespace dsa {
 
 __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
-    const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k,
+    const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int64_t n_rows,
     float* __restrict__ scores, int64_t ld) {
   __shared__ __align__(16) uint8_t tiles[2][KEY_TILE * IDX_DIM];
@@ -34,8 +34,8 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
   const int ntiles = (int)((n_vis + KEY_TILE - 1) / KEY_TILE);
 
   const int64_t row = row_begin + i;
-  const uint8_t* kb8 = k8 + (int64_t)b * n_k * IDX_DIM;
-  const float* ksb = ks + (int64_t)b * n_k;
+  const uint8_t* kb8 = k8 + (int64_t)b * kbs * IDX_DIM;
+  const float* ksb = ks + (int64_t)b * kbs;
   IdxRow Q;
   if (active) {
     const int64_t qrow = (int64_t)b * n_q + row;
@@ -72,7 +72,7 @@ constexpr int SPLIT_TILES = 32;  // 2048 keys per block, 8 tiles per wave
 
 __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
-    const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k,
+    const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int64_t n_rows,
     float* __restrict__ scores, int64_t ld) {
   const int b = blockIdx.z;
@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
   const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + row_begin + i;
   const int64_t row = row_begin + i;
   const int64_t qrow = (int64_t)b * n_q + row;
-  const uint8_t* kb8 = k8 + (int64_t)b * n_k * IDX_DIM;
-  const float* ksb = ks + (int64_t)b * n_k;
+  const uint8_t* kb8 = k8 + (int64_t)b * kbs * IDX_DIM;
+  const float* ksb = ks + (int64_t)b * kbs;
   float* srow = scores + ((int64_t)b * n_rows + i) * ld;
   const int64_t t0 = (int64_t)blockIdx.x * SPLIT_TILES;
   int64_t n_vis = pos + 1 < n_k ? pos + 1 : n_k;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
 // fp32 indexer: one thread per (row, key).
 __global__ __launch_bounds__(256) void idx_scores_f32(
     const float* __restrict__ q, const float* __restrict__ qs, const float* __restrict__ kk,
-    const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k,
+    const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t pos_offset, int H_I, int d_I, int64_t row_begin, int64_t n_rows,
     float* __restrict__ scores, int64_t ld) {
   const int b = blockIdx.z;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void idx_scores_f32(
   }
   const int64_t qrow = (int64_t)b * n_q + row_begin + i;
   const float* qr = q + qrow * H_I * d_I;
-  const float* kr = kk + ((int64_t)b * n_k + key) * d_I;
+  const float* kr = kk + ((int64_t)b * kbs + key) * d_I;
   float acc = 0.f;
   for (int j = 0; j < H_I; ++j) {
     float dot = 0.f;
@@ -156,25 +156,26 @@ __global__ __launch_bounds__(256) void idx_scores_f32(
     const float c = __fmul_rn(w[qrow * H_I + j], qs[qrow * H_I + j]);
     acc = __fmaf_rn(c, fmaxf(dot, 0.f), acc);
   }
-  srow[key] = __fmul_rn(acc, ks[(int64_t)b * n_k + key]);
+  srow[key] = __fmul_rn(acc, ks[(int64_t)b * kbs + key]);
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
+  const int64_t kbs = a.k_bstride ? a.k_bstride : a.n_k;
   if (a.dtype == DSA_F32) {
     dim3 grid((unsigned)((a.n_k + 255) / 256), (unsigned)a.n_rows, (unsigned)a.B);
     hipLaunchKernelGGL(idx_scores_f32, grid, dim3(256), 0, st, (const float*)a.q_idx, a.q_scale,
-                       (const float*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, a.q_pos, a.pos_offset, a.H_I, a.d_I,
+                       (const float*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, kbs, a.q_pos, a.pos_offset, a.H_I, a.d_I,
                        a.row_begin, a.n_rows, a.scores, a.ld_scores);
   } else if (a.n_rows * a.B <= 512) {
     dim3 grid((unsigned)((a.n_k + SPLIT_TILES * KEY_TILE - 1) / (SPLIT_TILES * KEY_TILE)),
               (unsigned)a.n_rows, (unsigned)a.B);
     hipLaunchKernelGGL(idx_scores_fp8_split, grid, dim3(256), 0, st, (const uint8_t*)a.q_idx, a.q_scale,
-                       (const uint8_t*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, a.q_pos, a.pos_offset, a.row_begin,
+                       (const uint8_t*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, kbs, a.q_pos, a.pos_offset, a.row_begin,
                        a.n_rows, a.scores, a.ld_scores);
   } else {
     dim3 grid((unsigned)((a.n_rows + 3) / 4), (unsigned)a.B);
     hipLaunchKernelGGL(idx_scores_fp8_rows, grid, dim3(256), 0, st, (const uint8_t*)a.q_idx, a.q_scale,
-                       (const uint8_t*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, a.q_pos, a.pos_offset, a.row_begin,
+                       (const uint8_t*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, kbs, a.q_pos, a.pos_offset, a.row_begin,
                        a.n_rows, a.scores, a.ld_scores);
   }
   return hipGetLastError();

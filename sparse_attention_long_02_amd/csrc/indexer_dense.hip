@@ -94,7 +94,7 @@ __device__ __forceinline__ v8i dense_fragment(const uint8_t* tile, int f, int la
 template <bool FILTER>
 __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
-    const float* __restrict__ ks, const float* __restrict__ w, int B, int64_t n_q, int64_t n_k,
+    const float* __restrict__ ks, const float* __restrict__ w, int B, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t row_begin, int64_t n_rows, int64_t n_grp, int stride,
     float* __restrict__ scores, int64_t ld, const float* __restrict__ thr, uint2* __restrict__ cand,
     uint32_t* __restrict__ cnt) {
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   const int64_t n_vis = lim_last >= 0 ? lim_last / stride + 1 : 0;
   const int ntiles = (int)((n_vis + KEY_TILE - 1) / KEY_TILE);
 
-  const uint8_t* kb = k8 + (size_t)b * n_k * IDX_DIM;
-  const float* ksb = ks + (size_t)b * n_k;
+  const uint8_t* kb = k8 + (size_t)b * kbs * IDX_DIM;
+  const float* ksb = ks + (size_t)b * kbs;
   const uint32_t ring0 = lds_addr(ring);
   const DenseDma dl = dense_dma_lane(wv, lane);
 #pragma unroll
@@ -283,11 +283,11 @@ hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st) {
   if (a.key_stride < 1 || (a.cand && a.key_stride != 1)) return hipErrorInvalidValue;
   if (a.cand)
     hipLaunchKernelGGL(idx_dense_fp8_kernel<true>, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8,
-                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp, 1,
+                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.k_bstride ? a.k_bstride : a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp, 1,
                        nullptr, (int64_t)0, a.thr, a.cand, a.cnt);
   else
     hipLaunchKernelGGL(idx_dense_fp8_kernel<false>, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8,
-                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp,
+                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.k_bstride ? a.k_bstride : a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp,
                        a.key_stride, a.scores, a.ld, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }

@@ -414,7 +414,7 @@ __device__ __forceinline__ bool group_skipped(const uint8_t* __restrict__ redo, 
 __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int B,
-    int n_q, int n_k, int row_lo, int k, int n_groups, int32_t* __restrict__ idx,
+    int n_q, int n_k, int64_t kbs, int row_lo, int k, int n_groups, int32_t* __restrict__ idx,
     const uint8_t* __restrict__ redo) {
   // ring of three tile pairs (pair p = tiles 2p, 2p+1) and their key scales
   __shared__ __align__(16) uint8_t tk0[TILE_BYTES];
@@ -444,8 +444,8 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
       if (g.n_keys <= k) continue;  // every row keeps all it sees: the owners write it
       const int row0 = g.row_hi - 4;
       const size_t rbase = (size_t)g.b * n_q;
-      const uint8_t* kb = k8 + (size_t)g.b * n_k * IDX_DIM;
-      const float* ksb = ks + (size_t)g.b * n_k;
+      const uint8_t* kb = k8 + (size_t)g.b * kbs * IDX_DIM;
+      const float* ksb = ks + (size_t)g.b * kbs;
       IdxHalf Qh[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -594,7 +594,8 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
     const int64_t n_groups = a.B * ((n_rows + 3) / 4);
     const int64_t blocks = n_groups < n_cu ? n_groups : n_cu;
     hipLaunchKernelGGL(prefill_idx_topk_kernel, dim3((unsigned)blocks), dim3(PF_WAVES * 64), 0, st, a.q8, a.qs,
-                       a.k8, a.ks, a.w, a.q_pos, (int)a.B, (int)a.n_q, (int)a.n_k, (int)row_lo, a.k,
+                       a.k8, a.ks, a.w, a.q_pos, (int)a.B, (int)a.n_q, (int)a.n_k,
+                       a.k_bstride ? a.k_bstride : a.n_k, (int)row_lo, a.k,
                        (int)n_groups, a.idx, a.redo);
   }
   return hipGetLastError();

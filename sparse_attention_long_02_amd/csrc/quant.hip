@@ -69,11 +69,11 @@ __device__ __forceinline__ void load8(const void* x, int32_t dtype, int64_t i, f
   }
 }
 
-// Rows of group b: source row b * n_per + i, destination row b * dst_per + base + i with
-// base = pos ? pos[b] : 0; destination rows outside [0, dst_per) are skipped.
+// Rows of group b: source row b * n_per + i, destination row b * dst_stride + base + i with
+// base = pos ? pos[b] : 0; destination rows outside [0, dst_per) of their group are skipped.
 __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const void* __restrict__ x, int32_t dtype,
                                                              int64_t n_per, int64_t width, int64_t ld_x,
-                                                             const int32_t* __restrict__ pos, int64_t dst_per,
+                                                             const int32_t* __restrict__ pos, int64_t dst_per, int64_t dst_stride,
                                                              uint8_t* __restrict__ codes, int64_t ld_c,
                                                              float* __restrict__ scale, int64_t scale_stride,
                                                              int32_t repeat, bool vec) {
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const void* __restr
   const int64_t drow = base + i;
   if (drow < 0 || drow >= dst_per) return;
   const int64_t src = (b * n_per + i) * ld_x;
-  const int64_t dst = b * dst_per + drow;
+  const int64_t dst = b * dst_stride + drow;
 
   if (vec) {  // 8 values per lane per access (16-byte loads, 8-byte code stores)
     float amax = 0.f;
@@ -141,7 +141,7 @@ hipError_t launch_fp8_quant_rows(const QuantArgs& a, hipStream_t st) {
                    ((uintptr_t)a.codes & 7u) == 0 && a.ld_codes % 8 == 0;
   dim3 grid((unsigned)((a.n_per + 3) / 4), (unsigned)a.groups);
   hipLaunchKernelGGL(fp8_quant_rows_kernel, grid, dim3(256), 0, st, a.x, a.dtype, a.n_per, a.width, a.ld_x,
-                     a.pos, a.dst_per, a.codes, a.ld_codes, a.scale, a.scale_stride, a.repeat, vec);
+                     a.pos, a.dst_per, a.dst_stride ? a.dst_stride : a.dst_per, a.codes, a.ld_codes, a.scale, a.scale_stride, a.repeat, vec);
   return hipGetLastError();
 }
 

@@ -22,8 +22,9 @@
 //     product; V^T is read from the same row-major rows with the gfx950 transposing LDS
 //     read, so no transposed copy is stored;
 //   * fp32 online softmax in base 2 whose reference max moves only when a logit exceeds
-//     it by 8 (P then stays <= 256, exact enough in bf16), which keeps the rescale of the
-//     accumulators off the common path.
+//     it by 8 (P then stays <= 256), which keeps the rescale of the accumulators off the
+//     common path.  P enters the PV product rounded to bf16; O is divided by the sum of
+//     those rounded weights (lse by the fp32 sum), so a dominant key's rounding cancels.
 // Keys may be split over several blocks (decode): each writes a normalised partial O and
 // its lse, and a combine kernel merges them.
 #include "dsa_kernels.h"
@@ -203,6 +204,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+// acc + the two bf16 values of a packed pair, in fp32 (one v_dot2c_f32_bf16 against 1.0, 1.0)
+__device__ __forceinline__ float bf16_pair_sum(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                         acc, false);
+}
 
 // A operand of O^T = V^T P^T for latent values 32t .. 32t+31 (rows) and key step s: the
 // contraction slots j of lane group g = l/32 are keys 16s + 4g + 8(j/4) + j%4, the keys
@@ -239,8 +245,8 @@ __device__ __forceinline__ v16f mla_logits(const v8bf* Qt, const uint8_t* buf) {
 // softmax of chunk c runs, then O^T += V^T P^T for chunk c.
 __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-    int64_t n_q, int64_t n_k, int k, float scale_log2, int n_split, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int64_t n_q, int64_t n_k, int64_t ld_q, int64_t ld_kv, int64_t bs_kv, int k, float scale_log2, int n_split,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __align__(16) uint8_t buf0[CHUNK_BYTES];
   __shared__ __align__(16) uint8_t buf1[CHUNK_BYTES];
   __shared__ __align__(16) uint8_t buf2[CHUNK_BYTES];
@@ -254,12 +260,12 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   const int split = blockIdx.x % n_split;
   const int64_t qrow = (int64_t)b * n_q + qi;
   const int32_t* irow = idx + qrow * k;
-  const uint16_t* kvb = kv + (int64_t)b * n_k * MDQK;
+  const uint16_t* kvb = kv + (int64_t)b * bs_kv;
 
   // B operands of S^T: head 32w + l%32, values 16ds + 8g .. +7
   v8bf Qt[D_STEPS];
   {
-    const uint16_t* qh = q + (qrow * MH + 32 * wv + (l & 31)) * MDQK + 8 * g;
+    const uint16_t* qh = q + (qrow * MH + 32 * wv + (l & 31)) * ld_q + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < D_STEPS; ++ds) Qt[ds] = *reinterpret_cast<const v8bf*>(qh + 16 * ds);
     // held in registers for the whole row (never re-read from memory)
@@ -284,13 +290,15 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   v16f O[O_TILES];
 #pragma unroll
   for (int t = 0; t < O_TILES; ++t) O[t] = v16f{};
-  float m_ref = -INFINITY, l_run = 0.f;
+  // l_run: sum of the fp32 probabilities (for lse); l_bf: sum of the bf16-rounded ones that
+  // the PV product actually weighs, which normalises O (see the epilogue)
+  float m_ref = -INFINITY, l_run = 0.f, l_bf = 0.f;
 
   uint8_t* bufs[NBUF] = {buf0, buf1, buf2, buf3};
   VMCNT(0);  // the Q^T operands are in registers before the chunk loads start
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (j < n) gather_chunk(lds_addr(bufs[j]), kvb, ids, c_lo + j, nk, wv, l);
+    if (j < n) gather_chunk(lds_addr(bufs[j]), kvb, ids, c_lo + j, nk, wv, l, ld_kv);
 
   v16f S_cur = {};
   if (n > 0) {
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
         for (int ds = 0; ds < PART1; ++ds) {
           S_next = mfma_bf16_32x32x16(kf[ds % KRING], Qt[ds], S_next);
           kf[ds % KRING] = k_frag(bn, k_off(ko, ds + KRING));
-          if (ds % 4 == 1) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon);
+          if (ds % 4 == 1) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon, ld_kv);
         }
         float mx = fmaxf(fmaxf(S_cur[0], S_cur[1]), S_cur[2]);
 #pragma unroll
@@ -350,6 +358,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
           if (ballot(m_ref != -INFINITY)) {
             const float alpha = m_ref == -INFINITY ? 0.f : exp2f(m_ref - m_new);
             l_run *= alpha;
+            l_bf *= alpha;
             o_guard(O);
             // one tile at a time, each back in its accumulation registers before the next
 #pragma unroll
@@ -376,13 +385,18 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
         }
         ps += xor32(ps);
         l_run += ps;
+        float pb = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb = bf16_pair_sum(pk[i], pb);
+        pb += xor32(pb);
+        l_bf += pb;
         const v8bf P0 = __builtin_bit_cast(v8bf, v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
         const v8bf P1 = __builtin_bit_cast(v8bf, v4i{(int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]});
 #pragma unroll
         for (int ds = PART1; ds < D_STEPS; ++ds) {
           S_next = mfma_bf16_32x32x16(kf[ds % KRING], Qt[ds], S_next);
           if (ds + KRING < D_STEPS) kf[ds % KRING] = k_frag(bn, k_off(ko, ds + KRING));
-          if (ds % 4 == 1 && ds / 4 < LOADS_PER_CHUNK) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon);
+          if (ds % 4 == 1 && ds / 4 < LOADS_PER_CHUNK) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon, ld_kv);
         }
         const uint32_t bc = lds_addr(bufs[j]);
         pv_chunk(O, P0, P1, bc + opaque(vt_lane_offset(0)), bc + opaque(vt_lane_offset(1)));
@@ -396,8 +410,12 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   const int le = opaque(l);
   const int ge = le >> 5;
   const int64_t row_head = ((int64_t)b * n_q + qi) * MH + 32 * wv + (le & 31);
+  // O is normalised by the sum of the very bf16 weights its PV product used, so O is a
+  // convex combination of V rows with weights of exact sum 1: the rounding of a dominant
+  // weight cancels.  lse keeps the fp32 sum.  (When l_run > 0 the key that set m_ref has
+  // weight 1, so l_bf >= 1.)
   const bool nonempty = l_run > 0.f;
-  const float inv = nonempty ? 1.f / l_run : 0.f;
+  const float inv = nonempty ? 1.f / l_bf : 0.f;
   const float lse_v = nonempty ? (m_ref + log2f(l_run)) * LN2 : -INFINITY;
   if (n_split == 1) {
     uint16_t* orow = out + row_head * MDV + 4 * ge;
@@ -467,25 +485,26 @@ constexpr int F32_MAX_K = 4096;
 __global__ __launch_bounds__(64) void sparse_mla_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kv, const float* __restrict__ v,
     const int32_t* __restrict__ idx, int64_t n_q, int64_t n_k, int H, int d_qk, int d_v, int k,
-    float sm_scale, float* __restrict__ out, float* __restrict__ lse) {
+    int64_t ld_q, int64_t ld_kv, int64_t ld_v, int64_t bs_kv, int64_t bs_v, float sm_scale,
+    float* __restrict__ out, float* __restrict__ lse) {
   __shared__ float z[F32_MAX_K];
   const int lane = threadIdx.x;
   const int64_t qh = blockIdx.x;  // (b * n_q + t) * H + head
   const int b = blockIdx.y;
   const int64_t qrow = (int64_t)b * n_q + qh / H;
   const int head = (int)(qh % H);
-  const float* qv = q + (qrow * H + head) * d_qk;
+  const float* qv = q + (qrow * H + head) * ld_q;
   const int32_t* irow = idx + qrow * k;
-  const float* kvb = kv + (int64_t)b * n_k * d_qk;
-  const float* vb = v ? v + (int64_t)b * n_k * d_v : kvb;
-  const int64_t vstride = v ? d_v : d_qk;
+  const float* kvb = kv + (int64_t)b * bs_kv;
+  const float* vb = v ? v + (int64_t)b * bs_v : kvb;
+  const int64_t vstride = v ? ld_v : ld_kv;
   float mx = -INFINITY;
   for (int j = 0; j < k; ++j) {
     const int32_t s = irow[j];
     float zz = -INFINITY;
     if (s >= 0 && s < n_k) {
       float part = 0.f;
-      for (int d = lane; d < d_qk; d += 64) part = __fmaf_rn(qv[d], kvb[(int64_t)s * d_qk + d], part);
+      for (int d = lane; d < d_qk; d += 64) part = __fmaf_rn(qv[d], kvb[(int64_t)s * ld_kv + d], part);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
       zz = sm_scale * part;
@@ -526,11 +545,16 @@ size_t sparse_mla_ws_bytes(int64_t B, int64_t n_q, int32_t H, int32_t d_v, int32
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
+  const int64_t ld_q = a.ld_q ? a.ld_q : a.d_qk;
+  const int64_t ld_kv = a.ld_kv ? a.ld_kv : a.d_qk;
+  const int64_t ld_v = a.ld_v ? a.ld_v : a.d_v;
+  const int64_t bs_kv = a.bs_kv ? a.bs_kv : a.n_k * ld_kv;
+  const int64_t bs_v = a.bs_v ? a.bs_v : a.n_k * ld_v;
   if (a.dtype == DSA_F32) {
     dim3 grid((unsigned)(a.n_q * a.H), (unsigned)a.B);
     hipLaunchKernelGGL(sparse_mla_f32_kernel, grid, dim3(64), 0, st, (const float*)a.q, (const float*)a.kv,
-                       (const float*)a.v, a.idx, a.n_q, a.n_k, a.H, a.d_qk, a.d_v, a.k, a.sm_scale,
-                       (float*)a.out, a.lse);
+                       (const float*)a.v, a.idx, a.n_q, a.n_k, a.H, a.d_qk, a.d_v, a.k, ld_q, ld_kv, ld_v, bs_kv,
+                       bs_v, a.sm_scale, (float*)a.out, a.lse);
     return hipGetLastError();
   }
   const int s = sparse_mla_splits(a.B, a.n_q, a.k, a.dtype);
@@ -542,7 +566,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
   }
   dim3 grid((unsigned)(a.n_q * s), (unsigned)a.B);
   hipLaunchKernelGGL(sparse_mla_bf16_kernel, grid, dim3(MLA_WAVES * 64), 0, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.kv, a.idx, a.n_q, a.n_k, a.k, a.sm_scale * LOG2E, s,
+                     (const uint16_t*)a.kv, a.idx, a.n_q, a.n_k, ld_q, ld_kv, bs_kv, a.k, a.sm_scale * LOG2E, s,
                      (uint16_t*)a.out, a.lse, part_o, part_lse);
   if (s > 1)
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(a.B * a.n_q * a.H)), dim3(128), 0, st, part_o,

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 (DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_PREFILL, DSA_OP_DECODE, DSA_OP_SELECT, DSA_OP_CHUNK,
- DSA_OP_MLA_BWD) = range(8)
+ DSA_OP_MLA_BWD, DSA_OP_KL_DENSE) = range(9)
 
 _i64, _i32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -31,27 +31,29 @@ _SIGNATURES = {
     "dsa_indexer": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i32, _i32,
                                    _i64, _i64, _vp, _i64, _vp]),
     "dsa_topk": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i32, _vp, _vp, _sz, _vp]),
-    "dsa_sparse_mla": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32,
-                                      _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "dsa_sparse_mla": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _i32,
+                                      _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "dsa_select_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                           _sz, _vp]),
-    "dsa_forward_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
-                                           _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp,
-                                           _vp, _sz, _vp]),
-    "dsa_forward_decode": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
-                                          _vp, _vp, _vp, _sz, _vp]),
-    "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
-                                         _vp, _vp, _vp, _sz, _vp]),
+    "dsa_forward_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
+                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp,
+                                           _vp, _vp, _sz, _vp]),
+    "dsa_forward_decode": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                          _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
+                                         _vp, _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dsa_sparse_mla_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
                                                _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dsa_indexer_scores_at": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32,
                                              _i32, _vp, _vp]),
     "dsa_indexer_kl": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32,
                                       _vp, _vp, _vp]),
+    "dsa_indexer_kl_dense": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _i32,
+                                            _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "dsa_fp8_quantize_rows": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i32, _vp]),
-    "dsa_kcache_append": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp]),
+    "dsa_kcache_append": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i32, _vp, _i64, _i64, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -91,6 +93,61 @@ def _ptr(t: Optional[torch.Tensor]):
     if not t.is_contiguous():
         raise ValueError("libdsa takes contiguous tensors")
     return t.data_ptr()
+
+
+def _rows(t: Optional[torch.Tensor], n_row_dims: int = 1):
+    """(device pointer, row stride in elements) of a tensor whose innermost dimension is
+    contiguous and whose leading dimensions lay its rows out evenly (a padded view such
+    as x[..., :d] of a wider buffer).  ``n_row_dims`` leading-to-innermost dimensions
+    (before the last) must form one evenly strided run of rows."""
+    if t is None:
+        return None, 0
+    if not t.is_cuda:
+        raise ValueError("libdsa takes device tensors")
+    if t.stride(-1) != 1:
+        raise ValueError("the innermost dimension must be contiguous")
+    ld = t.stride(-2) if t.dim() >= 2 else t.shape[-1]
+    run = ld
+    for d in range(t.dim() - 2, t.dim() - 2 - n_row_dims, -1):
+        if d < 0:
+            break
+        if t.shape[d] > 1 and t.stride(d) != run:
+            raise ValueError("rows must be evenly strided")
+        run *= t.shape[d]
+    return t.data_ptr(), ld
+
+
+def _cache(t: Optional[torch.Tensor]):
+    """(device pointer, row stride, sequence stride) of a per-sequence cache [B, n, width]
+    whose rows are evenly strided within each sequence."""
+    if t is None:
+        return None, 0, 0
+    if not t.is_cuda:
+        raise ValueError("libdsa takes device tensors")
+    if t.dim() != 3 or t.stride(-1) != 1:
+        raise ValueError("caches are [B, n, width] with the innermost dimension contiguous")
+    ld, bs = t.stride(1), t.stride(0)
+    if t.shape[1] == 1:
+        ld = max(ld, t.shape[2])
+    if t.shape[0] == 1:
+        bs = max(bs, t.shape[1] * ld)
+    return t.data_ptr(), ld, bs
+
+
+def _key_cache(k_cache: torch.Tensor, k_cache_scale: torch.Tensor):
+    """(codes pointer, sequence stride in key rows) of an indexer key cache [B, n, d_I]
+    with dense rows, and its scales [B, n] on the same sequence stride."""
+    if not (k_cache.is_cuda and k_cache_scale.is_cuda):
+        raise ValueError("libdsa takes device tensors")
+    d_I = k_cache.shape[-1]
+    if k_cache.stride(-1) != 1 or k_cache.stride(-2) != d_I or k_cache_scale.stride(-1) != 1:
+        raise ValueError("indexer key-cache rows must be dense")
+    bs = k_cache.stride(0) // d_I
+    if k_cache.stride(0) != bs * d_I or (k_cache.shape[0] > 1 and k_cache_scale.stride(0) != bs):
+        raise ValueError("the key cache and its scales must share one sequence stride (in rows)")
+    if k_cache.shape[0] == 1:
+        bs = max(bs, k_cache.shape[1])
+    return k_cache.data_ptr(), bs
 
 
 def _stream() -> int:
@@ -165,7 +222,10 @@ def sparse_mla(q, kv, idx, sm_scale: float, d_v: int, v=None):
     out = torch.empty((B, n_q, H, d_v), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
     ws = _workspace(workspace_size(DSA_OP_SPARSE_MLA, B, n_q, n_k, H, d_v, k, dt), q.device)
-    _check(lib().dsa_sparse_mla(_ptr(q), _ptr(kv), _ptr(v), _ptr(idx), B, n_q, n_k, H, d_qk, d_v, k,
+    q_p, ld_q = _rows(q, 3)
+    kv_p, ld_kv = _rows(kv, 2)
+    v_p, ld_v = _rows(v, 2)
+    _check(lib().dsa_sparse_mla(q_p, ld_q, kv_p, ld_kv, v_p, ld_v, _ptr(idx), B, n_q, n_k, H, d_qk, d_v, k,
                                 float(sm_scale), dt, _ptr(out), _ptr(lse), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream()))
     return (out[0], lse[0]) if squeeze else (out, lse)
@@ -195,8 +255,11 @@ def forward_prefill(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int, sm_scale: 
     lse = torch.empty((L, H), dtype=torch.float32, device=dev) if lse is None else lse
     if ws is None:
         ws = _workspace(workspace_size(DSA_OP_PREFILL, 1, L, L, H, d_v, k, at), dev)
+    q_p, ld_q = _rows(q, 2)
+    kv_p, ld_kv = _rows(kv, 1)
+    v_p, ld_v = _rows(v, 1)
     _check(lib().dsa_forward_prefill(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w),
-                                     _ptr(q), _ptr(kv), _ptr(v), L, H_I, d_I, H, d_qk, d_v, k,
+                                     q_p, ld_q, kv_p, ld_kv, v_p, ld_v, L, H_I, d_I, H, d_qk, d_v, k,
                                      float(sm_scale), it, at, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
@@ -215,9 +278,13 @@ def forward_decode(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cac
     lse = torch.empty((B, H), dtype=torch.float32, device=dev) if lse is None else lse
     if ws is None:
         ws = _workspace(workspace_size(DSA_OP_DECODE, B, 1, n_k_max, H, d_v, k, at), dev)
+    kc_p, kc_bs = _key_cache(k_cache, k_cache_scale)
+    q_p, ld_q = _rows(q, 2)
+    kv_p, ld_kv, bs_kv = _cache(kv_cache)
+    v_p, ld_v, bs_v = _cache(v_cache)
     _check(lib().dsa_forward_decode(B, _ptr(ctx_len), n_k_max, _ptr(q_idx), _ptr(q_scale), _ptr(w),
-                                    _ptr(k_cache), _ptr(k_cache_scale), _ptr(q), _ptr(kv_cache),
-                                    _ptr(v_cache), H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
+                                    kc_p, k_cache_scale.data_ptr(), kc_bs, q_p, ld_q, kv_p, ld_kv, bs_kv,
+                                    v_p, ld_v, bs_v, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
                                     _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
@@ -238,9 +305,13 @@ def forward_chunk(q_pos, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cache,
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if lse is None else lse
     if ws is None:
         ws = _workspace(workspace_size(DSA_OP_CHUNK, B, n_q, n_k_max, H, d_v, k, at), dev)
+    kc_p, kc_bs = _key_cache(k_cache, k_cache_scale)
+    q_p, ld_q = _rows(q, 3)
+    kv_p, ld_kv, bs_kv = _cache(kv_cache)
+    v_p, ld_v, bs_v = _cache(v_cache)
     _check(lib().dsa_forward_chunk(B, n_q, _ptr(q_pos), n_k_max, _ptr(q_idx), _ptr(q_scale), _ptr(w),
-                                   _ptr(k_cache), _ptr(k_cache_scale), _ptr(q), _ptr(kv_cache),
-                                   _ptr(v_cache), H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
+                                   kc_p, k_cache_scale.data_ptr(), kc_bs, q_p, ld_q, kv_p, ld_kv, bs_kv,
+                                   v_p, ld_v, bs_v, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
                                    _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
@@ -300,6 +371,34 @@ def indexer_kl(q, kv, idx, lse, idx_scores, sm_scale: float, p_out: bool = False
     return kl, p
 
 
+def indexer_kl_dense(q_idx, q_scale, k_idx, k_scale, w, q, kv, sm_scale: float, q_pos=None, want_lse=False,
+                     kl=None, ws=None):
+    """Dense warm-up KL loss: per query row, KL(head-averaged dense attention distribution
+    over every key up to its position || softmax of its index scores over the same keys).
+    Indexer operands as for ``indexer`` and attention operands q [n_q, H, d_qk] / kv
+    [n_k, d_qk] (or with a leading B) -> (kl [.., n_q], lse [.., n_q, H] or None)."""
+    squeeze = q_idx.dim() == 3
+    if squeeze:
+        q_idx, q_scale, w, k_idx, k_scale, q, kv = (x.unsqueeze(0) for x in (q_idx, q_scale, w, k_idx, k_scale,
+                                                                             q, kv))
+    B, n_q, H_I, d_I = q_idx.shape
+    n_k = k_idx.shape[1]
+    H, d_qk = q.shape[-2:]
+    at = _attn_dtype(q)
+    if kl is None:
+        kl = torch.empty((B, n_q), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device) if want_lse else None
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_KL_DENSE, B, n_q, n_k, H, 1, 1, at), q.device)
+    _check(lib().dsa_indexer_kl_dense(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), _ptr(q),
+                                      _ptr(kv), B, n_q, n_k, _ptr(q_pos), H_I, d_I, H, d_qk, float(sm_scale),
+                                      _idx_dtype(q_idx), at, _ptr(kl), _ptr(lse), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream()))
+    if squeeze:
+        return kl[0], (lse[0] if lse is not None else None)
+    return kl, lse
+
+
 def _x_dtype(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return DSA_BF16
@@ -326,8 +425,10 @@ def fp8_quantize_rows(x, repeat: int = 1, codes=None, scale=None):
 
 def kcache_append(k_new, pos, k_cache, k_cache_scale):
     """Quantise k_new [B, n_new, d_I] into k_cache [B, n_k_max, d_I] / k_cache_scale
-    [B, n_k_max] at rows pos[b] .. pos[b] + n_new - 1 (in place)."""
-    assert k_new.is_cuda and k_new.is_contiguous() and k_cache.is_contiguous() and k_cache_scale.is_contiguous()
+    [B, n_k_max] at rows pos[b] .. pos[b] + n_new - 1 (in place; the caches may be
+    [:, :n_k_max] views of longer per-sequence buffers)."""
+    assert k_new.is_cuda and k_new.is_contiguous()
     B, n_new, d_I = k_new.shape
+    kc_p, kc_bs = _key_cache(k_cache, k_cache_scale)
     _check(lib().dsa_kcache_append(_ptr(k_new), _x_dtype(k_new), B, n_new, d_I, _ptr(pos), k_cache.shape[1],
-                                   _ptr(k_cache), _ptr(k_cache_scale), _stream()))
+                                   kc_bs, kc_p, k_cache_scale.data_ptr(), _stream()))

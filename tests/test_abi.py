@@ -27,14 +27,14 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 16
+    assert len(syms) == 17
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(dsa._SIGNATURES)
 
 
 def test_version_and_status_strings(L):
-    assert L.dsa_abi_version() == 1
+    assert L.dsa_abi_version() == 2
     for st in (0, -1, -2, -3, -4):
         assert L.dsa_status_string(st)
     assert b"unknown" in L.dsa_status_string(7)
@@ -70,11 +70,21 @@ def test_topk_validation(L):
 
 
 def test_sparse_mla_validation(L):
-    args = dict(q=FAKE, kv=FAKE, v=None, idx=FAKE, B=1, nq=4, nk=64, H=128, dqk=576, dv=512, k=2048,
-                sm=0.04, dt=dsa.DSA_BF16, out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    args = dict(q=FAKE, ldq=576, kv=FAKE, ldkv=576, v=None, ldv=0, idx=FAKE, B=1, nq=4, nk=64, H=128, dqk=576,
+                dv=512, k=2048, sm=0.04, dt=dsa.DSA_BF16, out=FAKE, lse=None, ws=None, wsb=0, st=None)
     order = list(args)
     call = lambda **kw: L.dsa_sparse_mla(*[kw.get(n, args[n]) for n in order])
     assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
+    # element strides: at least the row width, and whole 16-byte units for bf16
+    assert call(ldq=575) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldq=580) == dsa.DSA_ERR_INVALID_ARG
+    assert b"ld_q" in L.dsa_last_error()
+    assert call(ldkv=512) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldkv=588) == dsa.DSA_ERR_INVALID_ARG
+    assert b"ld_kv" in L.dsa_last_error()
+    assert call(ldq=640, ldkv=640) == dsa.DSA_ERR_WORKSPACE     # padded rows pass validation
+    assert call(dt=dsa.DSA_F32, H=4, dqk=64, dv=64, k=64, v=FAKE, ldq=64, ldkv=64, ldv=63) == dsa.DSA_ERR_INVALID_ARG
+    assert b"ld_v" in L.dsa_last_error()
     assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
     assert call(v=FAKE) == dsa.DSA_ERR_UNSUPPORTED            # bf16 path reads V from kv
     assert call(k=100) == dsa.DSA_ERR_UNSUPPORTED             # k must be a multiple of 32
@@ -88,43 +98,64 @@ def test_sparse_mla_validation(L):
 
 
 def test_forward_validation(L):
-    pre = dict(qi=FAKE, qs=FAKE, ki=FAKE, ks=FAKE, w=FAKE, q=FAKE, kv=FAKE, v=None, L=1024, H_I=64, d_I=128,
-               H=128, dqk=576, dv=512, k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, idx=FAKE,
-               out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    pre = dict(qi=FAKE, qs=FAKE, ki=FAKE, ks=FAKE, w=FAKE, q=FAKE, ldq=576, kv=FAKE, ldkv=576, v=None, ldv=0,
+               L=1024, H_I=64, d_I=128, H=128, dqk=576, dv=512, k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3,
+               at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None, ws=None, wsb=0, st=None)
     order = list(pre)
     call = lambda **kw: L.dsa_forward_prefill(*[kw.get(n, pre[n]) for n in order])
     assert call(idx=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldq=100) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldkv=577) == dsa.DSA_ERR_INVALID_ARG
     assert call(L=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(it=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED     # fp32 indexer with bf16 attention
     assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED
-    f32 = dict(it=dsa.DSA_F32, at=dsa.DSA_F32, H_I=2, d_I=32, H=4, dqk=64, dv=64, v=FAKE, k=64, L=512)
+    f32 = dict(it=dsa.DSA_F32, at=dsa.DSA_F32, H_I=2, d_I=32, H=4, dqk=64, dv=64, v=FAKE, k=64, L=512,
+               ldq=64, ldkv=64, ldv=64)
     need = L.dsa_workspace_size(dsa.DSA_OP_PREFILL, 1, 512, 512, 4, 64, 64, dsa.DSA_F32)
     assert need >= 512 * 512 * 4
     assert call(**f32) == dsa.DSA_ERR_WORKSPACE
-    dec = dict(B=64, ctx=FAKE, nkm=131072, qi=FAKE, qs=FAKE, w=FAKE, kc=FAKE, kcs=FAKE, q=FAKE, kv=FAKE,
-               v=None, H_I=64, d_I=128, H=128, dqk=576, dv=512, k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3,
-               at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    assert call(**dict(f32, ldv=60)) == dsa.DSA_ERR_INVALID_ARG
+    assert call(**dict(f32, ldq=67, ldkv=65, ldv=70)) == dsa.DSA_ERR_WORKSPACE   # fp32 strides need no alignment
+    n = 131072
+    dec = dict(B=64, ctx=FAKE, nkm=n, qi=FAKE, qs=FAKE, w=FAKE, kc=FAKE, kcs=FAKE, kcbs=n, q=FAKE, ldq=576,
+               kv=FAKE, ldkv=576, kvbs=n * 576, v=None, ldv=0, vbs=0, H_I=64, d_I=128, H=128, dqk=576, dv=512,
+               k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None, ws=None,
+               wsb=0, st=None)
     order = list(dec)
     call = lambda **kw: L.dsa_forward_decode(*[kw.get(n, dec[n]) for n in order])
     assert call(ctx=None) == dsa.DSA_ERR_INVALID_ARG
+    # cache strides: sequences may not overlap; bf16 strides in whole 16-byte units
+    assert call(kcbs=n - 1) == dsa.DSA_ERR_INVALID_ARG
+    assert b"kc_seq_stride" in L.dsa_last_error()
+    assert call(kvbs=n * 576 - 8) == dsa.DSA_ERR_INVALID_ARG
+    assert b"kv_seq_stride" in L.dsa_last_error()
+    assert call(ldkv=640, kvbs=n * 576) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldkv=640, kvbs=n * 640 + 4) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldq=572) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldkv=640, kvbs=n * 640 + 64, kcbs=n + 5, ldq=1024) == dsa.DSA_ERR_WORKSPACE   # padded caches pass
     assert call() == dsa.DSA_ERR_WORKSPACE
     need = L.dsa_workspace_size(dsa.DSA_OP_DECODE, 64, 1, 131072, 128, 512, 2048, dsa.DSA_BF16)
     assert need >= 64 * 131072 * 4
     assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG   # misaligned workspace
-    assert call(nkm=1 << 19, ws=FAKE, wsb=1 << 40) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(nkm=1 << 19, kcbs=1 << 19, kvbs=576 << 19, ws=FAKE, wsb=1 << 40) == dsa.DSA_ERR_UNSUPPORTED
 
 
 def test_chunk_validation(L):
-    ch = dict(B=4, nq=512, qpos=FAKE, nkm=131072, qi=FAKE, qs=FAKE, w=FAKE, kc=FAKE, kcs=FAKE, q=FAKE,
-              kv=FAKE, v=None, H_I=64, d_I=128, H=128, dqk=576, dv=512, k=2048, sm=0.04,
-              it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None, ws=None, wsb=0, st=None)
+    n = 131072
+    ch = dict(B=4, nq=512, qpos=FAKE, nkm=n, qi=FAKE, qs=FAKE, w=FAKE, kc=FAKE, kcs=FAKE, kcbs=n, q=FAKE,
+              ldq=576, kv=FAKE, ldkv=576, kvbs=n * 576, v=None, ldv=0, vbs=0, H_I=64, d_I=128, H=128, dqk=576,
+              dv=512, k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None,
+              ws=None, wsb=0, st=None)
     order = list(ch)
     call = lambda **kw: L.dsa_forward_chunk(*[kw.get(n, ch[n]) for n in order])
     assert call(qpos=None) == dsa.DSA_ERR_INVALID_ARG           # positions are required
+    assert call(kcbs=1000) == dsa.DSA_ERR_INVALID_ARG
+    assert call(kvbs=1000) == dsa.DSA_ERR_INVALID_ARG
+    assert call(ldq=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(nq=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(B=65536) == dsa.DSA_ERR_INVALID_ARG
     assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED               # FP8 selection keeps <= 2048
-    assert call(nkm=1 << 25) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(nkm=1 << 25, kcbs=1 << 25, kvbs=576 << 25) == dsa.DSA_ERR_UNSUPPORTED
     assert call(it=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED       # fp32 indexer with bf16 attention
     assert call(kc=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG          # misaligned FP8 cache
     # the FP8 selection keeps per-row key-sample scores and candidate lists, never score rows:
@@ -136,7 +167,9 @@ def test_chunk_validation(L):
     need = L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 1, 131072, 128, 512, 2048, dsa.DSA_BF16)
     assert need > 0 and call(nq=1) == dsa.DSA_ERR_WORKSPACE
     f32 = dict(it=dsa.DSA_F32, at=dsa.DSA_F32, H_I=2, d_I=32, H=4, dqk=64, dv=64, v=FAKE, k=64, nkm=4096,
-               nq=16)
+               nq=16, kcbs=4096, ldq=64, ldkv=64, kvbs=4096 * 64, ldv=64, vbs=4096 * 64)
+    assert call(**dict(f32, ldv=64, vbs=4096 * 64 - 1)) == dsa.DSA_ERR_INVALID_ARG
+    assert b"v_seq_stride" in L.dsa_last_error()
     need = L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 4, 16, 4096, 4, 64, 64, dsa.DSA_F32)
     assert need >= 4 * 16 * 4096 * 4
     assert call(**f32) == dsa.DSA_ERR_WORKSPACE
@@ -185,6 +218,28 @@ def test_training_stage_validation(L):
     assert L.dsa_workspace_size(dsa.DSA_OP_MLA_BWD, 1, 131072, 131072, 128, 512, 2048, dsa.DSA_BF16) == need
 
 
+def test_dense_kl_validation(L):
+    n = 8192
+    kd = dict(qi=FAKE, qs=FAKE, ki=FAKE, ks=FAKE, w=FAKE, q=FAKE, kv=FAKE, B=1, nq=n, nk=n, qpos=None, H_I=64,
+              d_I=128, H=128, dqk=576, sm=0.04, it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, kl=FAKE, lse=None, ws=None,
+              wsb=0, st=None)
+    order = list(kd)
+    call = lambda **kw: L.dsa_indexer_kl_dense(*[kw.get(n_, kd[n_]) for n_ in order])
+    assert call(kl=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(H=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(it=dsa.DSA_BF16) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(kv=FAKE + 2) == dsa.DSA_ERR_INVALID_ARG
+    # the workspace holds score rows of one pass, at most 2^28 floats (and one row at least)
+    need = L.dsa_workspace_size(dsa.DSA_OP_KL_DENSE, 1, n, n, 128, 1, 1, dsa.DSA_BF16)
+    assert need == n * n * 4
+    assert L.dsa_workspace_size(dsa.DSA_OP_KL_DENSE, 1, 131072, 131072, 128, 1, 1, dsa.DSA_BF16) == 2048 * 131072 * 4
+    assert call() == dsa.DSA_ERR_WORKSPACE
+    assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG
+    f32 = dict(it=dsa.DSA_F32, at=dsa.DSA_F32, H_I=2, d_I=32, H=4, dqk=64)
+    assert call(**dict(f32, nk=5000, nq=5000)) == dsa.DSA_ERR_UNSUPPORTED      # fp32 path: n_k <= 4096
+    assert call(**dict(f32, nk=512, nq=512)) == dsa.DSA_ERR_WORKSPACE
+
+
 def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
@@ -203,9 +258,10 @@ def test_quantiser_validation(L):
     assert call(rep=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(rep=4, ss=2) == dsa.DSA_ERR_INVALID_ARG
     order = [("k", FAKE), ("dt", dsa.DSA_BF16), ("B", 2), ("n", 3), ("d", 128), ("pos", FAKE),
-             ("nmax", 64), ("c", FAKE), ("s", FAKE), ("st", None)]
+             ("nmax", 64), ("bs", 64), ("c", FAKE), ("s", FAKE), ("st", None)]
     call = lambda **kw: L.dsa_kcache_append(*[kw.get(n, d) for n, d in order])
     assert call(pos=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(bs=63) == dsa.DSA_ERR_INVALID_ARG
     assert call(B=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(B=70000) == dsa.DSA_ERR_INVALID_ARG
     assert call(nmax=0) == dsa.DSA_ERR_INVALID_ARG

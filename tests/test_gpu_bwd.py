@@ -2,10 +2,12 @@
 oracle's chain rule, on the forward's own lse and output.
 
 bf16 bar: the kernels round P and dZ to bf16 for the matrix cores (relative 2^-9 each) and
-take D_h = dO_h . O_h from the bf16 forward output, so every gradient element carries an
-error of a few 2^-9 of the magnitudes summed into it.  The tests bound the Frobenius error
-relative to the reference by 1e-2 and the element error by 2e-2 of the tensor's largest
-reference value.
+take D_h = dO_h . O_h from the bf16 forward output (itself formed from bf16 P), so every
+gradient element carries an error of a few 2^-9 of the magnitudes summed into it.  Each
+element is held to its own bound: 2^-7 times the sum of the absolute values of the terms
+that make it (|dZ| |kv| for dq; |dZ| |q| and P |dO| for dkv), plus the effect of an error of
+2^-8 sum_d |dO_hd| (P |V|)_hd in D_h, plus 1e-6 of the tensor's largest value for the fp32
+accumulation.  The Frobenius error relative to the reference is also held to 1e-2.
 """
 import sys
 
@@ -39,21 +41,58 @@ def _idx(rng, n_q, n_k, k, causal_offset=None):
     return idx
 
 
-def _compare(name, got, ref):
+def _compare(name, got, ref, bound=None):
     err = got - ref
     frob = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
     elem = float(np.abs(err).max() / max(np.abs(ref).max(), 1e-30))
-    _say(f"  {name}: relative Frobenius error {frob:.2e}, max element error / max {elem:.2e}")
-    assert frob <= FROB_REL and elem <= ELEM_REL, (name, frob, elem)
+    msg = f"  {name}: relative Frobenius error {frob:.2e}, max element error / max {elem:.2e}"
+    ok = frob <= FROB_REL and elem <= ELEM_REL
+    if bound is not None:
+        tol = bound + 1e-6 * np.abs(ref).max()
+        ratio = float((np.abs(err) / tol).max())
+        msg += f", worst element error / own bound {ratio:.2e}"
+        ok = ok and ratio <= 1.0
+    _say(msg)
+    assert ok, (name, frob, elem)
 
 
-def _bf16_case(B, n_q, n_k, k, seed):
+U = 2.0 ** -8   # a bf16 rounding (2^-9) with a factor 2 of slack
+
+
+def _element_bounds(q, kv, v, idx, do, sm_scale):
+    """Per-element error bounds of the bf16 kernels' dq and dkv (see the module docstring),
+    from the float64 operands: 2U times the magnitudes of the summed terms, plus the
+    propagated D_h error."""
+    n_q, n_k = q.shape[0], kv.shape[0]
+    Bq = np.zeros(q.shape)
+    Bkv = np.zeros(kv.shape)
+    akv, av = np.abs(kv), np.abs(v)
+    for t in range(n_q):
+        sel = idx[t][(idx[t] >= 0) & (idx[t] < n_k)]
+        if len(sel) == 0:
+            continue
+        z = sm_scale * (q[t] @ kv[sel].T)
+        P = np.exp(z - z.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dP = do[t] @ v[sel].T
+        dZ = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+        dD = U * np.sum(np.abs(do[t]) * (P @ av[sel]), axis=1)        # bound on the D_h error
+        PdD = P * dD[:, None]
+        Bq[t] = 2 * U * sm_scale * (np.abs(dZ) @ akv[sel]) + sm_scale * (PdD @ akv[sel])
+        contrib = 2 * U * sm_scale * (np.abs(dZ).T @ np.abs(q[t])) + sm_scale * (PdD.T @ np.abs(q[t]))
+        contrib[:, : v.shape[1]] += 2 * U * (P.T @ np.abs(do[t]))
+        Bkv[sel] += contrib
+    return Bq, Bkv
+
+
+def _bf16_case(B, n_q, n_k, k, seed, idx=None):
     cfg = S.CONFIGS["prefill_8k"].with_(L=n_k, seed=seed)
     inps = [S.make_prefill(cfg.with_(seed=seed + b)) for b in range(B)]
     rng = np.random.default_rng(seed)
     q_bits = np.stack([inp.q[:n_q] for inp in inps])
     kv_bits = np.stack([inp.kv for inp in inps])
-    idx = np.stack([_idx(rng, n_q, n_k, k) for _ in range(B)])
+    if idx is None:
+        idx = np.stack([_idx(rng, n_q, n_k, k) for _ in range(B)])
     do_bits = S.bf16_bits(rng.standard_normal((B, n_q, 128, 512)).astype(np.float32))
     q, kv, do = dev_bf16(q_bits), dev_bf16(kv_bits), dev_bf16(do_bits)
     idx_d = torch.from_numpy(idx).cuda()
@@ -65,8 +104,9 @@ def _bf16_case(B, n_q, n_k, k, seed):
     for b in range(B):
         q64, kv64, do64 = O.bf16_to_f64(q_bits[b]), O.bf16_to_f64(kv_bits[b]), O.bf16_to_f64(do_bits[b])
         r_dq, r_dkv, _ = O.sparse_mqa_backward(q64, kv64, kv64[:, :512], idx[b], do64, cfg.sm_scale, True)
-        _compare(f"dq[{b}]", g_dq[b], r_dq)
-        _compare(f"dkv[{b}]", g_dkv[b], r_dkv)
+        b_dq, b_dkv = _element_bounds(q64, kv64, kv64[:, :512], idx[b], do64, cfg.sm_scale)
+        _compare(f"dq[{b}]", g_dq[b], r_dq, b_dq)
+        _compare(f"dkv[{b}]", g_dkv[b], r_dkv, b_dkv)
         # keys no query selected get exactly zero
         unused = np.setdiff1d(np.arange(n_k), idx[b][idx[b] >= 0])
         assert np.all(g_dkv[b][unused] == 0)
@@ -84,6 +124,26 @@ def test_backward_bf16_two_passes_and_batch():
     _bf16_case(1, 4200, 4400, 64, seed=62)
     _say("[sparse MLA backward, bf16] B=2, n_q=96, k=128")
     _bf16_case(2, 96, 1500, 128, seed=63)
+
+
+def test_backward_bf16_k2048_across_a_pass_boundary():
+    """k = 2048 (the workload's k: 64 chunks per row, every iteration of the row scan, the
+    full P / dZ workspace) over 4100 queries, so the second pass of at most 4096 queries
+    runs too.  Every 41st row keeps 2048 distinct ids with -1 holes inside later chunks;
+    the other rows keep 32 to 96 ids, also with holes (the oracle's cost stays small)."""
+    n_q, n_k, k = 4100, 8192, 2048
+    _say(f"[sparse MLA backward, bf16] n_q={n_q}, n_k={n_k}, k={k} (two passes)")
+    rng = np.random.default_rng(66)
+    idx = np.full((n_q, k), -1, dtype=np.int32)
+    for t in range(n_q):
+        full = t % 41 == 0 or t in (4095, 4096, 4099)
+        m = k if full else int(rng.integers(32, 97))
+        ids = np.sort(rng.choice(n_k, m, replace=False)).astype(np.int32)
+        slots = np.arange(m) if full else np.sort(rng.choice(k, m, replace=False))
+        idx[t, slots] = ids
+        if full:   # holes in later chunks (ids are ignored wherever a -1 sits)
+            idx[t, rng.choice(np.arange(k // 2, k), 40, replace=False)] = -1
+    _bf16_case(1, n_q, n_k, k, seed=67, idx=idx[None])
 
 
 def test_backward_bf16_rows_without_keys():
@@ -106,8 +166,11 @@ def test_backward_bf16_rows_without_keys():
                                            O.bf16_to_f64(inp.kv)[:, :512], idx, O.bf16_to_f64(
                                                do.view(torch.int16).cpu().numpy().view(np.uint16)),
                                            cfg.sm_scale, True)
-    _compare("dq", out_to_f64(dq), r_dq)
-    _compare("dkv", dkv.double().cpu().numpy(), r_dkv)
+    q64, kv64 = O.bf16_to_f64(inp.q[:64]), O.bf16_to_f64(inp.kv)
+    do64 = O.bf16_to_f64(do.view(torch.int16).cpu().numpy().view(np.uint16))
+    b_dq, b_dkv = _element_bounds(q64, kv64, kv64[:, :512], idx, do64, cfg.sm_scale)
+    _compare("dq", out_to_f64(dq), r_dq, b_dq)
+    _compare("dkv", dkv.double().cpu().numpy(), r_dkv, b_dkv)
 
 
 def test_backward_fp32_vs_oracle():

@@ -129,6 +129,43 @@ def test_chunk_batch_offsets_vs_oracle():
     _say(f"  attention max-abs on the GPU's selection {worst:.3e}")
 
 
+def test_chunk_two_selection_passes_and_sampled_thresholds():
+    """B = 4 sequences of n_q = 4200 rows: the selection runs in two passes of 4096 rows per
+    sequence, and rows that see more than 6144 of the 12288 cached keys take a sampled
+    threshold.  Offsets include a negative one (rows before the first key) and rows past the
+    end of the cache.  Every row's selection must equal the top-k of the library's scores;
+    sampled rows overlap the oracle's selection, and their attention matches the oracle."""
+    n_q, n_k = 4200, 12288
+    q_pos = [-100, 3000, 8000, 10000]
+    _say(f"[chunk two passes] B=4, n_q={n_q}, n_k_max={n_k}, q_pos={q_pos}")
+    cfg = S.CONFIGS["prefill_8k"].with_(L=n_k)
+    inps = [S.make_prefill(cfg.with_(seed=51 + b)) for b in range(len(q_pos))]
+    rows, qi, qs, w, q, kc, kcs, kv = _chunk_inputs(inps, q_pos, n_q)
+    pos_d = torch.tensor(q_pos, dtype=torch.int32, device="cuda")
+    qi_d, qs_d, w_d = dev_u8(qi), dev_f32(qs), dev_f32(w)
+    kc_d, kcs_d = dev_u8(kc), dev_f32(kcs)
+    idx, out, lse = dsa.forward_chunk(pos_d, qi_d, qs_d, w_d, kc_d, kcs_d, dev_bf16(q), dev_bf16(kv), cfg.k,
+                                      cfg.sm_scale, cfg.d_v)
+    scores = dsa.indexer(qi_d, qs_d, kc_d, kcs_d, w_d, q_pos=pos_d)
+    ref_idx = dsa.topk(scores, cfg.k, q_pos=pos_d)
+    torch.cuda.synchronize()
+    diff = (idx != ref_idx).any(dim=2).nonzero().tolist()
+    assert not diff, f"{len(diff)} rows differ from top-k of the scores, first {diff[:5]}"
+    del scores, ref_idx
+    g_idx, g_out = idx.cpu().numpy(), out_to_f64(out)
+    assert np.all(g_idx[0, :100] == -1) and np.all(g_out[0, :100] == 0)
+    rng = np.random.default_rng(52)
+    for b, p0 in enumerate(q_pos):
+        pick = sorted(set([4095, 4096, n_q - 1] + rng.integers(0, n_q, 5).tolist()))
+        pos = np.array([p0 + i for i in pick])
+        W = O.widen_inputs(inps[b], rows[b][pick])
+        ref = O.dsa_rows(W["qhat"], W["w"], W["khat"], W["q"], W["kv"], W["v"], pos, cfg.k, cfg.sm_scale)
+        ov, _ = overlap(g_idx[b, pick], ref["idx"])
+        assert ov >= OVERLAP_MIN, (b, ov)
+        o_ref, _ = O.sparse_mqa(W["q"], W["kv"], W["v"], g_idx[b, pick], cfg.sm_scale)
+        assert np.abs(g_out[b, pick] - o_ref).max() <= ATOL_BF16, b
+
+
 def test_chunk_small_k_and_ragged_rows():
     """k = 96 (many buffer cuts per row) and n_q = 7 (a ragged last group of rows)."""
     n_k = 3000

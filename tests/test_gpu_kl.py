@@ -179,3 +179,102 @@ def test_kl_dense_warmup_when_k_covers_the_context():
         A = O.indexer_magnitude_row(W["qhat"][j], W["w"][j], W["khat"], int(t))
         kl_ref, _ = O.indexer_kl_row(W["q"][j], W["kv"], np.arange(t + 1), I, cfg.sm_scale)
         assert abs(float(g_kl[t]) - kl_ref) <= 2e-2 * float(A.max()) + 1e-4, (t, float(g_kl[t]), kl_ref)
+
+
+def _check_dense_rows(rows, pos, q_f64, kv_f64, g_sc, g_kl, g_lse, sm_scale, v_f64=None):
+    """Dense warm-up rows: KL against the oracle over keys 0 .. pos on the GPU's own scores,
+    and the dense attention lse against the oracle's."""
+    worst = 0.0
+    n_k = kv_f64.shape[0]
+    for j, t in enumerate(rows):
+        p_ = int(pos[j])
+        n = max(0, min(p_ + 1, n_k))
+        if n == 0:
+            assert float(g_kl[j]) == 0.0 and np.all(np.isneginf(g_lse[j])), t
+            continue
+        ids = np.arange(n, dtype=np.int32)
+        sc = g_sc[j][:n].astype(np.float64)
+        kl_ref, p_ref = O.indexer_kl_row(q_f64[j], kv_f64, ids, sc, sm_scale)
+        log_q = sc - (sc.max() + np.log(np.sum(np.exp(sc - sc.max()))))
+        gap = np.where(p_ref > 0, np.log(np.where(p_ref > 0, p_ref, 1.0)) - log_q, 0.0)
+        tol = _kl_tol(p_ref, gap)
+        err = abs(float(g_kl[j]) - kl_ref)
+        worst = max(worst, err / tol)
+        assert err <= tol, (t, float(g_kl[j]), kl_ref, tol)
+        _, l_ref = O.sparse_mqa_row(q_f64[j], kv_f64, kv_f64 if v_f64 is None else v_f64, ids, sm_scale)
+        assert np.allclose(g_lse[j], l_ref, atol=1e-4, rtol=1e-5), t
+    return worst
+
+
+def test_kl_dense_warmup_every_key_bf16():
+    """The dense warm-up over every key s <= t at L = 8192 (far more keys than k = 2048):
+    KL per row and the dense attention lse against the float64 oracle, on the index scores
+    the library itself produces (dsa_indexer's, bit-identical to the ones the loss uses)."""
+    cfg = S.CONFIGS["prefill_8k"]
+    L = cfg.L
+    _say(f"[indexer KL, dense warm-up] L={L}, every key up to each row")
+    inp = S.make_prefill(cfg)
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    q, kv = dev_bf16(inp.q), dev_bf16(inp.kv)
+    kl, lse = dsa.indexer_kl_dense(qi, qs, ki, ks, w, q, kv, cfg.sm_scale, want_lse=True)
+    kl2, _ = dsa.indexer_kl_dense(qi, qs, ki, ks, w, q, kv, cfg.sm_scale)
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    torch.cuda.synchronize()
+    assert torch.equal(kl, kl2), "not deterministic"
+    rng = np.random.default_rng(17)
+    rows = np.array(sorted({0, 1, 31, 32, 2047, 2048, 4095, 6143, L - 1} | set(rng.integers(0, L, 24).tolist())))
+    g_sc = scores[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del scores
+    g_kl, g_lse = kl.cpu().numpy()[rows], lse.cpu().numpy()[rows]
+    assert np.all(np.isfinite(kl.cpu().numpy())) and float(kl.min()) >= -1e-4
+    W = O.widen_inputs(inp, rows)
+    worst = _check_dense_rows(rows, rows, W["q"], W["kv"], g_sc, g_kl, g_lse, cfg.sm_scale)
+    _say(f"  worst KL error / bound {worst:.3e} over {len(rows)} rows; mean KL {float(kl.mean()):.4f}")
+
+
+def test_kl_dense_warmup_offsets_and_batch():
+    """B = 2 sequences of 300 query rows at offsets -10 (rows before the first key: KL 0,
+    lse -inf) and 2900 against 3000 keys (rows past the last key see every key)."""
+    n_q, n_k = 300, 3000
+    q_pos = [-10, 2900]
+    _say(f"[indexer KL, dense warm-up] B=2, n_q={n_q}, n_k={n_k}, q_pos={q_pos}")
+    cfg = S.CONFIGS["prefill_8k"].with_(L=n_k)
+    inps = [S.make_prefill(cfg.with_(seed=90 + b)) for b in range(2)]
+    rows = [np.clip(np.arange(p, p + n_q), 0, n_k - 1) for p in q_pos]
+    qi = dev_u8(np.stack([inp.qi[r] for inp, r in zip(inps, rows)]))
+    qs = dev_f32(np.stack([inp.q_scale[r] for inp, r in zip(inps, rows)]))
+    w = dev_f32(np.stack([inp.w[r] for inp, r in zip(inps, rows)]))
+    q = dev_bf16(np.stack([inp.q[r] for inp, r in zip(inps, rows)]))
+    ki = dev_u8(np.stack([inp.ki for inp in inps]))
+    ks = dev_f32(np.stack([inp.k_scale for inp in inps]))
+    kv = dev_bf16(np.stack([inp.kv for inp in inps]))
+    pos_d = torch.tensor(q_pos, dtype=torch.int32, device="cuda")
+    kl, lse = dsa.indexer_kl_dense(qi, qs, ki, ks, w, q, kv, cfg.sm_scale, q_pos=pos_d, want_lse=True)
+    scores = dsa.indexer(qi, qs, ki, ks, w, q_pos=pos_d)
+    torch.cuda.synchronize()
+    g_kl, g_lse, g_sc = kl.cpu().numpy(), lse.cpu().numpy(), scores.cpu().numpy()
+    for b in range(2):
+        pick = np.array([0, 5, 9, 10, 11, 99, 100, 101, 150, 299])
+        W = O.widen_inputs(inps[b], rows[b][pick])
+        _check_dense_rows(pick, q_pos[b] + pick, W["q"], W["kv"], g_sc[b][pick], g_kl[b][pick], g_lse[b][pick],
+                          cfg.sm_scale)
+
+
+def test_kl_dense_warmup_fp32_every_row():
+    cfg = S.CONFIGS["tiny_fp32_512"]
+    _say("[indexer KL, dense warm-up, fp32] L=512, every row")
+    inp = S.make_prefill(cfg)
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    q, kv = dev_f32(inp.q), dev_f32(inp.kv)
+    kl, lse = dsa.indexer_kl_dense(qi, qs, ki, ks, w, q, kv, cfg.sm_scale, want_lse=True)
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    torch.cuda.synchronize()
+    W = O.widen_inputs(inp)
+    rows = np.arange(cfg.L)
+    g_kl, g_lse, g_sc = kl.cpu().numpy(), lse.cpu().numpy(), scores.cpu().numpy()
+    for t in rows:
+        ids = np.arange(t + 1, dtype=np.int32)
+        kl_ref, _ = O.indexer_kl_row(W["q"][t], W["kv"], ids, g_sc[t][: t + 1].astype(np.float64), cfg.sm_scale)
+        assert abs(float(g_kl[t]) - kl_ref) <= 1e-5 * (1 + abs(kl_ref)), (t, float(g_kl[t]), kl_ref)
+        _, l_ref = O.sparse_mqa_row(W["q"][t], W["kv"], W["kv"], ids, cfg.sm_scale)
+        assert np.allclose(g_lse[t], l_ref, atol=1e-5, rtol=1e-6), t

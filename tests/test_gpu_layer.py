@@ -142,6 +142,57 @@ def test_prefill_end_to_end_vs_oracle(c2):
     _say(f"  indexer worst error / bound {worst_rel:.3e}")
 
 
+def test_prefill_every_row_vs_oracle(c2):
+    """Every one of the 8192 rows against the float64 oracle: the library's score row within
+    the indexer tolerance; the selection equal to the oracle's full-sort top-k of those
+    scores (bit for bit) and overlapping the oracle's own selection; the attention output
+    and lse against the oracle on the GPU's selection."""
+    cfg, inp = c2
+    L, k = cfg.L, cfg.k
+    _say(f"[prefill every row vs oracle] L={L}")
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    q, kv = dev_bf16(inp.q), dev_bf16(inp.kv)
+    idx, out, lse = dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, k, cfg.sm_scale, cfg.d_v)
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    torch.cuda.synchronize()
+    g_idx, g_lse, g_sc = idx.cpu().numpy(), lse.cpu().numpy(), scores.cpu().numpy()
+    del scores
+    worst_rel = worst_err = 0.0
+    inter = total = 0
+    for r0 in range(0, L, 512):
+        rows = np.arange(r0, min(L, r0 + 512))
+        W = O.widen_inputs(inp, rows)
+        g_out = out_to_f64(out[r0:r0 + len(rows)])
+        absk = np.abs(W["khat"])
+        for j, t in enumerate(rows):
+            t = int(t)
+            g = g_sc[t].astype(np.float64)
+            ref = O.indexer_row(W["qhat"][j], W["w"][j], W["khat"], t)
+            A = O.indexer_magnitude_row(W["qhat"][j], W["w"][j], W["khat"], t)
+            M = np.abs(W["w"][j]) @ (np.abs(W["qhat"][j]) @ absk[: t + 1].T)
+            err = np.abs(g[: t + 1] - ref)
+            bound = 1e-2 * A + 2.0 * cfg.d_I * 2.0 ** -24 * M
+            rel = float((err / (bound + 1e-300)).max())
+            worst_rel = max(worst_rel, rel)
+            assert rel <= 1.0, (t, rel)
+            assert np.array_equal(O.topk_row(g, t, k), g_idx[t]), f"selection differs at row {t}"
+            own = O.topk_row(ref, t, k)
+            sa, sb = set(g_idx[t][g_idx[t] >= 0].tolist()), set(own[own >= 0].tolist())
+            inter += len(sa & sb)
+            total += len(sb)
+            o_ref, l_ref = O.sparse_mqa_row(W["q"][j], W["kv"], W["v"], g_idx[t], cfg.sm_scale)
+            e = float(np.abs(g_out[j] - o_ref).max())
+            worst_err = max(worst_err, e)
+            assert e <= ATOL_BF16, (t, e)
+            assert np.allclose(g_lse[t], l_ref, atol=1e-3, rtol=1e-4), t
+        if r0 % 2048 == 0:
+            _say(f"  rows < {r0 + len(rows)} checked")
+    ov = inter / total
+    _say(f"  indexer worst error / bound {worst_rel:.3e}; selection == oracle top-k of the GPU scores on "
+         f"every row; overlap with the oracle's own selection {ov:.5f}; attention max-abs {worst_err:.3e}")
+    assert ov >= OVERLAP_MIN
+
+
 def test_decode_small_batch():
     """Decode over caches of different lengths: selection == top-k of the library's scores,
     overlap with the oracle, attention on the GPU's selection."""

@@ -108,15 +108,25 @@ def _check_topk_exact(scores_dev, idx_dev, k, pos_of_row):
         assert np.array_equal(got[i], want), (i, got[i][:8], want[:8])
 
 
-@pytest.mark.parametrize("k", [64, 256, 2048])
-def test_topk_exact_on_gpu_scores(c2_small, k):
-    cfg, inp = c2_small
-    _say(f"[topk exact] k={k}")
+@pytest.fixture(scope="module")
+def c2_5k():
+    cfg = S.CONFIGS["prefill_8k"].with_(L=5000)
+    return cfg, S.make_prefill(cfg)
+
+
+@pytest.mark.parametrize("k,which", [(64, "c2_small"), (256, "c2_small"), (2048, "c2_5k")])
+def test_topk_exact_on_gpu_scores(k, which, request):
+    """Rows longer than k run the radix select; at k = 2048 rows 2048 .. 4999 of L = 5000 do."""
+    cfg, inp = request.getfixturevalue(which)
+    assert cfg.L >= 2 * k or k < 2048
+    _say(f"[topk exact] k={k}, L={cfg.L}")
     qi, qs, ki, ks, w = indexer_inputs_dev(inp)
     scores = dsa.indexer(qi, qs, ki, ks, w)
     idx = dsa.topk(scores, k)
     torch.cuda.synchronize()
     _check_topk_exact(scores, idx, k, lambda i: i)
+    g = idx.cpu().numpy()
+    assert np.all(g[cfg.L - 1] >= 0) and cfg.L > k     # a full row: k keys kept out of L
 
 
 def test_topk_ties_zeros_and_positions():
