@@ -378,6 +378,31 @@ int dsa_indexer_kl_dense(const void* q_idx, const float* q_scale, const void* k_
                          dsa_stream_t stream);
 
 /*
+ * dsa_forward_decode_noalloc -- dsa_forward_decode without a workspace argument, for
+ * callers that cannot allocate device memory: code under stream capture, tight serving
+ * loops, harnesses that forbid allocation.  The arguments and results are those of
+ * dsa_forward_decode (minus ws / ws_bytes), computed by the same kernels.
+ *
+ * Its scratch is a fixed 128 MiB array of the library in device memory, held on every GPU
+ * the library runs on until the process ends (the 64 x 131072-token decode workload needs
+ * about 101 MB).  A shape whose dsa_workspace_size(DSA_OP_DECODE, ...) exceeds 128 MiB
+ * returns DSA_ERR_UNSUPPORTED before anything is enqueued.  Nothing is allocated, by the
+ * library or by any routine it calls.  All calls on one GPU share that GPU's array: calls
+ * that overlap on one GPU (concurrent streams, several threads) race and must be ordered
+ * by the caller.  The array keeps the previous call's contents; the call needs nothing
+ * zeroed.
+ */
+int dsa_forward_decode_noalloc(int64_t B, const int32_t* ctx_len, int64_t n_k_max,
+                               const void* q_idx, const float* q_scale, const float* w,
+                               const void* k_cache, const float* k_cache_scale,
+                               int64_t kc_seq_stride, const void* q, int64_t ld_q,
+                               const void* kv_cache, int64_t ld_kv, int64_t kv_seq_stride,
+                               const void* v_cache, int64_t ld_v, int64_t v_seq_stride,
+                               int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v,
+                               int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype,
+                               int32_t* idx, void* out, float* lse, dsa_stream_t stream);
+
+/*
  * dsa_fp8_quantize_rows -- FP8 E4M3FN quantisation of the indexer operands, the step
  * before the lightning indexer (the indexer runs in FP8: 53ai.com V3.2-Exp summary,
  * section 创新架构; juhe.plus explainer, section 第一步：Lightning Indexer).  Per row of

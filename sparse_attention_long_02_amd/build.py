@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "prefill_topk.hip", "sparse_mla.hip", "quant.hip",
-           "attn_kl.hip", "sparse_mla_bwd.hip", "indexer_dense.hip"]
+           "attn_kl.hip", "sparse_mla_bwd.hip", "indexer_dense.hip", "noalloc.hip"]
 # sources whose kernels keep MFMA accumulators in the accumulation registers (the backward's
 # dq accumulators do not fit next to its operands in the vector registers)
 AGPR_ACC = {"sparse_mla_bwd.hip"}

@@ -41,6 +41,9 @@ _SIGNATURES = {
     "dsa_forward_decode": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
                                           _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dsa_forward_decode_noalloc": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
+                                                  _vp, _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
                                          _vp, _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -287,6 +290,30 @@ def forward_decode(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cac
                                     v_p, ld_v, bs_v, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
                                     _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream()))
+    return idx, out, lse
+
+
+def forward_decode_noalloc(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cache, k: int,
+                           sm_scale: float, d_v: int, v_cache=None, idx=None, out=None, lse=None):
+    """forward_decode with the library's fixed scratch instead of a workspace (the entry
+    point for callers that cannot allocate; the outputs must be passed in to allocate
+    nothing here either)."""
+    B, H_I, d_I = q_idx.shape
+    n_k_max = k_cache.shape[1]
+    _, H, d_qk = q.shape
+    it, at = _idx_dtype(q_idx), _attn_dtype(q)
+    dev = q.device
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev) if idx is None else idx
+    out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if lse is None else lse
+    kc_p, kc_bs = _key_cache(k_cache, k_cache_scale)
+    q_p, ld_q = _rows(q, 2)
+    kv_p, ld_kv, bs_kv = _cache(kv_cache)
+    v_p, ld_v, bs_v = _cache(v_cache)
+    _check(lib().dsa_forward_decode_noalloc(B, _ptr(ctx_len), n_k_max, _ptr(q_idx), _ptr(q_scale), _ptr(w), kc_p,
+                                            k_cache_scale.data_ptr(), kc_bs, q_p, ld_q, kv_p, ld_kv, bs_kv, v_p,
+                                            ld_v, bs_v, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
+                                            _ptr(idx), _ptr(out), _ptr(lse), _stream()))
     return idx, out, lse
 
 

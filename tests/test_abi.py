@@ -27,7 +27,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 17
+    assert len(syms) == 18
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(dsa._SIGNATURES)
