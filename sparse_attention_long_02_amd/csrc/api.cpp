@@ -88,6 +88,42 @@ size_t decode_scores_bytes(int64_t B, int64_t n_k) { return (size_t)B * n_k * si
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Decode selection workspace.  Long caches (FP8 indexer, n_k_max >= DEC_FILTER_MIN) take the
+// threshold-filtered path: per sequence a 1-in-SEL_SAMPLE_STRIDE key sample's scores, a
+// threshold, the candidate segments of the filtering indexer's waves with their counts, and a
+// redo byte; the full score rows are written only for sequences the candidates do not decide.
+constexpr int64_t DEC_FILTER_MIN = 16384;
+struct DecWs {
+  float* scores;
+  float* samp;
+  float* thr;
+  uint32_t* cnt;
+  uint8_t* redo;
+  uint2* cand;
+};
+bool dec_filtered(int64_t n_k_max, int32_t idx_dtype) {
+  return idx_dtype == DSA_FP8_E4M3 && n_k_max >= DEC_FILTER_MIN;
+}
+size_t dec_sel_bytes(int64_t B, int64_t n_k_max, int32_t idx_dtype, DecWs* out = nullptr, void* base = nullptr) {
+  const size_t o_samp = align256(decode_scores_bytes(B, n_k_max));
+  if (!dec_filtered(n_k_max, idx_dtype)) {
+    if (out) *out = DecWs{(float*)base, nullptr, nullptr, nullptr, nullptr, nullptr};
+    return o_samp;
+  }
+  const size_t o_thr = o_samp + align256((size_t)B * dsa::sel_sample_ld(n_k_max) * sizeof(float));
+  const size_t o_cnt = o_thr + align256((size_t)B * sizeof(float));
+  const size_t o_redo = o_cnt + align256((size_t)B * dsa::dec_split_segments(n_k_max) * sizeof(uint32_t));
+  const int64_t segs = dsa::dec_split_segments(n_k_max);
+  const size_t o_cand = o_redo + align256((size_t)B);
+  const size_t total = o_cand + align256((size_t)B * segs * dsa::DEC_SEG * sizeof(uint2));
+  if (out) {
+    char* p = (char*)base;
+    *out = DecWs{(float*)p, (float*)(p + o_samp), (float*)(p + o_thr), (uint32_t*)(p + o_cnt), (uint8_t*)(p + o_redo),
+                 (uint2*)(p + o_cand)};
+  }
+  return total;
+}
+
 
 // largest key count of the fused selection (32-bit byte offsets within a sequence's keys)
 constexpr int64_t FUSED_MAX_KEYS = ((int64_t)1 << 25) - 1;
@@ -227,7 +263,9 @@ size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32
     case DSA_OP_SELECT:
       return dtype == DSA_F32 ? align256((size_t)n_q * n_k * sizeof(float)) : sel_bytes(1, n_q, n_k);
     case DSA_OP_DECODE:
-      return align256(decode_scores_bytes(B, n_k)) + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
+      // the attention dtype selects the pair: bf16 attention goes with the FP8 indexer
+      return dec_sel_bytes(B, n_k, dtype == DSA_BF16 ? DSA_FP8_E4M3 : DSA_F32) +
+             dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
     case DSA_OP_MLA_BWD:
       return dsa::sparse_mla_bwd_ws_bytes(B, n_q, k, dtype);
     case DSA_OP_CHUNK:
@@ -396,21 +434,55 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
   SUPPORT(n_k_max <= dsa::TOPK_MAX_N, "decode supports n_k_max <= %lld", (long long)dsa::TOPK_MAX_N);
   if (idx_dtype == DSA_FP8_E4M3) REQUIRE(aligned16(q_idx) && aligned16(k_cache), "FP8 operands must be 16-byte aligned");
   if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv_cache) && aligned16(out), "bf16 operands must be 16-byte aligned");
-  const size_t s_bytes = align256(decode_scores_bytes(B, n_k_max));
+  SUPPORT(idx_dtype == attn_dtype || (idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16),
+          "decode pairs an FP8 indexer with bf16 attention, or fp32 with fp32");
+  DecWs dw;
+  const size_t s_bytes = dec_sel_bytes(B, n_k_max, idx_dtype, &dw, ws);
   const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, attn_dtype);
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "dsa_forward_decode needs %zu workspace bytes (got %zu)", need, ws_bytes);
   REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  float* scores = (float*)ws;
   // the query of sequence b is its row 0, at position ctx_len[b] - 1
-  dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, H_I, d_I,
-                      idx_dtype, 0, 1, scores, n_k_max, kc_seq_stride};
-  st = hip_status(dsa::launch_indexer(ia, s), "decode indexer launch");
-  if (st) return st;
-  dsa::TopkArgs ta{scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx};
-  st = hip_status(dsa::launch_topk(ta, s), "decode top-k launch");
-  if (st) return st;
+  if (dec_filtered(n_k_max, idx_dtype)) {
+    const uint8_t* q8 = (const uint8_t*)q_idx;
+    const uint8_t* k8 = (const uint8_t*)k_cache;
+    const int64_t ld_s = dsa::sel_sample_ld(n_k_max);
+    // 1. scores of every SEL_SAMPLE_STRIDE-th key; 2. each sequence's threshold (and its
+    // candidate count zeroed); 3. the filtering indexer appends the keys above it; 4. the
+    // top-k of each candidate list; 5. sequences whose list did not decide them: full score
+    // rows and the exact row selection (both launches skip every other sequence)
+    dsa::SplitIdxArgs sa{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, dw.samp, ld_s,
+                         dsa::SEL_SAMPLE_STRIDE, nullptr, nullptr, nullptr, nullptr, kc_seq_stride};
+    st = hip_status(dsa::launch_idx_split(sa, s), "decode key-sample indexer launch");
+    if (st) return st;
+    dsa::SelThresholdArgs ta{dw.samp, ld_s, 1, B, 1, n_k_max, ctx_len, -1, k, dw.thr};
+    st = hip_status(dsa::launch_sel_threshold(ta, s), "decode threshold launch");
+    if (st) return st;
+    dsa::SplitIdxArgs fa{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, nullptr, 0, 1,
+                         dw.thr, dw.cand, dw.cnt, nullptr, kc_seq_stride};
+    st = hip_status(dsa::launch_idx_split(fa, s), "decode filtering indexer launch");
+    if (st) return st;
+    dsa::DecCandArgs ca{dw.cand, dw.cnt, dsa::dec_split_segments(n_k_max), B, 1, n_k_max, ctx_len, -1, k, idx,
+                        dw.redo};
+    st = hip_status(dsa::launch_dec_cand_topk(ca, s), "decode candidate top-k launch");
+    if (st) return st;
+    dsa::SplitIdxArgs ra{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, dw.scores, n_k_max,
+                         1, nullptr, nullptr, nullptr, dw.redo, kc_seq_stride};
+    st = hip_status(dsa::launch_idx_split(ra, s), "decode indexer launch (undecided sequences)");
+    if (st) return st;
+    dsa::TopkArgs tk{dw.scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx, 0, 0, 0, dw.redo};
+    st = hip_status(dsa::launch_topk(tk, s), "decode top-k launch (undecided sequences)");
+    if (st) return st;
+  } else {
+    dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, H_I, d_I,
+                        idx_dtype, 0, 1, dw.scores, n_k_max, kc_seq_stride};
+    st = hip_status(dsa::launch_indexer(ia, s), "decode indexer launch");
+    if (st) return st;
+    dsa::TopkArgs ta{dw.scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx};
+    st = hip_status(dsa::launch_topk(ta, s), "decode top-k launch");
+    if (st) return st;
+  }
   dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, 1, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
                  out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v_cache ? ld_v : 0,
                  kv_seq_stride, v_cache ? v_seq_stride : 0};

@@ -28,6 +28,42 @@ struct IndexerArgs {
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
 
+// FP8 index scores of a few rows with their keys split over blocks (decode), SPLIT_TILES
+// 64-key tiles per block of 4 waves.  Row i of sequence b sits at position q_pos[b] +
+// pos_offset + row_begin + i.  Store mode (cand null): the scores of keys 0, S, 2S, ..
+// (S = key_stride) to columns 0, 1, 2, .. of row b * n_rows + i of `scores` (ld floats
+// apart), -inf past the row's position.  Filter mode: no store; each wave of each block
+// writes the keys it scores above thr[b * n_rows + i] to its own segment of DEC_SEG slots
+// (see dec_split_segments), as (fp32 score bits, key) pairs in ascending key order, and
+// their number (which may exceed DEC_SEG) to the segment's count.  redo non-null: only rows
+// whose redo byte is set run.
+constexpr int SPLIT_TILES = 32;  // 2048 keys per block, 8 tiles per wave
+constexpr int DEC_SEG = 64;      // candidate slots per wave segment
+// candidate segments of a row in filter mode (4 per block): row r's list is at
+// cand + r * segs * DEC_SEG, its counts at cnt + r * segs
+inline int64_t dec_split_segments(int64_t n_k) {
+  return 4 * ((n_k + SPLIT_TILES * 64 - 1) / (SPLIT_TILES * 64));
+}
+struct SplitIdxArgs {
+  const uint8_t* q8;
+  const float* qs;
+  const uint8_t* k8;
+  const float* ks;
+  const float* w;
+  int64_t B, n_q, n_k;
+  const int32_t* q_pos;
+  int64_t pos_offset, row_begin, n_rows;
+  float* scores;
+  int64_t ld;
+  int32_t key_stride;
+  const float* thr;
+  uint2* cand;
+  uint32_t* cnt;
+  const uint8_t* redo;
+  int64_t k_bstride;
+};
+hipError_t launch_idx_split(const SplitIdxArgs& a, hipStream_t st);
+
 struct TopkArgs {
   const float* scores;
   int64_t ld_scores, B, n_rows, n_k;
@@ -39,6 +75,7 @@ struct TopkArgs {
   int64_t score_rows = 0;  // score rows per sequence (0: n_rows)
   int64_t out_rows = 0;    // idx rows per sequence (0: n_rows); row i goes to idx row out_row0 + i
   int64_t out_row0 = 0;
+  const uint8_t* redo = nullptr;  // non-null: only rows b * n_rows + i whose byte is set (long rows)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 constexpr int64_t TOPK_MAX_N = 262144;
@@ -143,6 +180,24 @@ struct SelThresholdArgs {
   float* thr;
 };
 hipError_t launch_sel_threshold(const SelThresholdArgs& a, hipStream_t st);
+
+// Decode: per row i of sequence b (position q_pos[b] + pos_offset + i, n = the keys it sees),
+// the top-k of its candidate segments (the filtering split indexer's, n_segs per row) when
+// no segment overflowed and k <= their total <= SEL_CAND_CAP: ascending with ties to the
+// lower key, -1 padded, to idx row b * n_rows + i (redo byte 0); every key when n <= k
+// (redo 0); else nothing (redo 1).
+struct DecCandArgs {
+  const uint2* cand;
+  const uint32_t* cnt;
+  int64_t n_segs;
+  int64_t B, n_rows, n_k;
+  const int32_t* q_pos;
+  int64_t pos_offset;
+  int32_t k;
+  int32_t* idx;
+  uint8_t* redo;
+};
+hipError_t launch_dec_cand_topk(const DecCandArgs& a, hipStream_t st);
 
 // Per row: the top-k of its candidate list when k <= cnt <= SEL_CAND_CAP (written to idx
 // row out_row0 + i of sequence b's out_rows rows, ascending, -1 padded; redo byte 0), every

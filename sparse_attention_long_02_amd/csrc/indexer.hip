@@ -67,49 +67,74 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
     for (int64_t key = (int64_t)ntiles * KEY_TILE + lane; key < n_k; key += KEY_TILE) srow[key] = -INFINITY;
 }
 
-// grid: x = key splits of SPLIT_TILES tiles, y = row, z = sequence
-constexpr int SPLIT_TILES = 32;  // 2048 keys per block, 8 tiles per wave
+// grid: x = key splits of SPLIT_TILES tiles, y = row, z = sequence.
+// Store mode: the row's scores of keys 0, S, 2S, ... (S = key_stride) go to columns 0, 1,
+// 2, ... of its score row, -inf for keys past its position.  Filter mode (FILTER): nothing
+// is stored; every wave keeps its own segment of DEC_SEG slots of the row's candidate list:
+// the keys it scores above thr[b * n_rows + i], as (fp32 score bits, key index) pairs in
+// ascending key order at cand + ((b * n_rows + i) * n_segs + seg) * DEC_SEG, seg =
+// 4 blockIdx.x + wave (slots past DEC_SEG are counted, not stored), and their number at
+// cnt[(b * n_rows + i) * n_segs + seg].  No atomics: a wave's slots come from a ballot and
+// its running count.  With redo non-null only rows whose redo byte is set run.
 
+template <bool FILTER>
 __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int64_t n_rows,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, int key_stride, const float* __restrict__ thr,
+    uint2* __restrict__ cand, uint32_t* __restrict__ cnt, const uint8_t* __restrict__ redo) {
   const int b = blockIdx.z;
   const int64_t i = blockIdx.y;
+  const int64_t rid = (int64_t)b * n_rows + i;
+  if (redo && !redo[rid]) return;  // uniform over the block
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + row_begin + i;
   const int64_t row = row_begin + i;
   const int64_t qrow = (int64_t)b * n_q + row;
   const uint8_t* kb8 = k8 + (int64_t)b * kbs * IDX_DIM;
   const float* ksb = ks + (int64_t)b * kbs;
-  float* srow = scores + ((int64_t)b * n_rows + i) * ld;
+  float* srow = scores + rid * ld;
   const int64_t t0 = (int64_t)blockIdx.x * SPLIT_TILES;
-  int64_t n_vis = pos + 1 < n_k ? pos + 1 : n_k;
-  n_vis = n_vis > 0 ? n_vis : 0;
+  // launch keys: key j is cache row j * key_stride; the row sees those at or below pos
+  const int64_t n_keys = (n_k + key_stride - 1) / key_stride;
+  int64_t lim = pos < n_k - 1 ? pos : n_k - 1;
+  const int64_t n_vis = lim >= 0 ? lim / key_stride + 1 : 0;
   const int64_t vis_tiles = (n_vis + KEY_TILE - 1) / KEY_TILE;
 
-  const int64_t all_tiles = (n_k + KEY_TILE - 1) / KEY_TILE;
+  const int64_t all_tiles = (n_keys + KEY_TILE - 1) / KEY_TILE;
   const int64_t t_end = t0 + SPLIT_TILES < all_tiles ? t0 + SPLIT_TILES : all_tiles;
   const int64_t t_vis = t_end < vis_tiles ? t_end : vis_tiles;
-  // tiles wholly beyond the query's position
-  for (int64_t t = (t0 > t_vis ? t0 : t_vis) + wv; t < t_end; t += 4) {
-    const int64_t key = t * KEY_TILE + lane;
-    if (key < n_k) srow[key] = -INFINITY;
+  if (!FILTER) {  // tiles wholly beyond the query's position
+    for (int64_t t = (t0 > t_vis ? t0 : t_vis) + wv; t < t_end; t += 4) {
+      const int64_t key = t * KEY_TILE + lane;
+      if (key < n_keys) srow[key] = -INFINITY;
+    }
   }
   // visible tiles of this wave: t0 + wv, t0 + wv + 4, ...; each tile's key fragments are
   // loaded one tile ahead, while the previous tile is scored
   int64_t t = t0 + wv;
-  if (t >= t_vis) return;
+  const int64_t seg = rid * (4 * (int64_t)gridDim.x) + 4 * blockIdx.x + wv;
+  if (t >= t_vis) {
+    if (FILTER && lane == 0) cnt[seg] = 0u;
+    return;
+  }
   IdxRow Q;
   load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
+  float T = 0.f;
+  uint2* crow = nullptr;
+  uint32_t ccount = 0;  // wave-uniform
+  if (FILTER) {
+    T = thr[rid];
+    crow = cand + seg * DEC_SEG;
+  }
   v8i bf[4];
   float ksc;
   {
     const int64_t key0 = t * KEY_TILE, key = key0 + lane;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bf[f] = global_key_fragment(kb8, key0, f, n_k);
-    ksc = ksb[key < n_k ? key : n_k - 1];
+    for (int f = 0; f < 4; ++f) bf[f] = global_key_fragment(kb8, key0, f, n_keys, key_stride);
+    ksc = ksb[(key < n_keys ? key : n_keys - 1) * key_stride];
   }
   for (; t < t_vis; t += 4) {
     const int64_t tn = t + 4;
@@ -118,16 +143,41 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     if (tn < t_vis) {
       const int64_t key0 = tn * KEY_TILE, key = key0 + lane;
 #pragma unroll
-      for (int f = 0; f < 4; ++f) bn[f] = global_key_fragment(kb8, key0, f, n_k);
-      kn = ksb[key < n_k ? key : n_k - 1];
+      for (int f = 0; f < 4; ++f) bn[f] = global_key_fragment(kb8, key0, f, n_keys, key_stride);
+      kn = ksb[(key < n_keys ? key : n_keys - 1) * key_stride];
     }
     const int64_t key = t * KEY_TILE + lane;
     const float sc = score_tile64(Q, bf, ksc);
-    if (key < n_k) srow[key] = key <= pos ? sc : -INFINITY;
+    if (FILTER) {
+      const bool pass = key < n_vis && sc > T;
+      const uint64_t m = ballot(pass);
+      const uint32_t slot = ccount + lanes_below(m);
+      if (pass && slot < (uint32_t)DEC_SEG) crow[slot] = make_uint2(__float_as_uint(sc), (uint32_t)key);
+      ccount += (uint32_t)__popcll((unsigned long long)m);
+    } else if (key < n_keys) {
+      srow[key] = key < n_vis ? sc : -INFINITY;
+    }
 #pragma unroll
     for (int f = 0; f < 4; ++f) bf[f] = bn[f];
     ksc = kn;
   }
+  if (FILTER && lane == 0) cnt[seg] = ccount;
+}
+
+hipError_t launch_idx_split(const SplitIdxArgs& a, hipStream_t st) {
+  const int64_t n_keys = (a.n_k + a.key_stride - 1) / a.key_stride;
+  dim3 grid((unsigned)((n_keys + SPLIT_TILES * KEY_TILE - 1) / (SPLIT_TILES * KEY_TILE)), (unsigned)a.n_rows,
+            (unsigned)a.B);
+  const int64_t kbs = a.k_bstride ? a.k_bstride : a.n_k;
+  if (a.cand)
+    hipLaunchKernelGGL(idx_scores_fp8_split<true>, grid, dim3(256), 0, st, a.q8, a.qs, a.k8, a.ks, a.w, a.n_q, a.n_k,
+                       kbs, a.q_pos, a.pos_offset, a.row_begin, a.n_rows, nullptr, (int64_t)0, 1, a.thr, a.cand,
+                       a.cnt, a.redo);
+  else
+    hipLaunchKernelGGL(idx_scores_fp8_split<false>, grid, dim3(256), 0, st, a.q8, a.qs, a.k8, a.ks, a.w, a.n_q,
+                       a.n_k, kbs, a.q_pos, a.pos_offset, a.row_begin, a.n_rows, a.scores, a.ld, a.key_stride,
+                       nullptr, nullptr, nullptr, a.redo);
+  return hipGetLastError();
 }
 
 // fp32 indexer: one thread per (row, key).
@@ -167,11 +217,10 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
                        (const float*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, kbs, a.q_pos, a.pos_offset, a.H_I, a.d_I,
                        a.row_begin, a.n_rows, a.scores, a.ld_scores);
   } else if (a.n_rows * a.B <= 512) {
-    dim3 grid((unsigned)((a.n_k + SPLIT_TILES * KEY_TILE - 1) / (SPLIT_TILES * KEY_TILE)),
-              (unsigned)a.n_rows, (unsigned)a.B);
-    hipLaunchKernelGGL(idx_scores_fp8_split, grid, dim3(256), 0, st, (const uint8_t*)a.q_idx, a.q_scale,
-                       (const uint8_t*)a.k_idx, a.k_scale, a.w, a.n_q, a.n_k, kbs, a.q_pos, a.pos_offset, a.row_begin,
-                       a.n_rows, a.scores, a.ld_scores);
+    SplitIdxArgs sa{(const uint8_t*)a.q_idx, a.q_scale, (const uint8_t*)a.k_idx, a.k_scale, a.w, a.B, a.n_q, a.n_k,
+                    a.q_pos, a.pos_offset, a.row_begin, a.n_rows, a.scores, a.ld_scores, 1, nullptr, nullptr,
+                    nullptr, nullptr, a.k_bstride};
+    return launch_idx_split(sa, st);
   } else {
     dim3 grid((unsigned)((a.n_rows + 3) / 4), (unsigned)a.B);
     hipLaunchKernelGGL(idx_scores_fp8_rows, grid, dim3(256), 0, st, (const uint8_t*)a.q_idx, a.q_scale,

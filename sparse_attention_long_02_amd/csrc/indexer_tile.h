@@ -143,12 +143,12 @@ __device__ __forceinline__ v8i lds_key_fragment(const uint8_t* tile, int f) {
 }
 
 // B operand of fragment f straight from global memory (keys key0 + 16f + lane%16,
-// clamped to n_k - 1 so the read stays in bounds).
+// clamped to n_k - 1 so the read stays in bounds; key j is row j * stride).
 __device__ __forceinline__ v8i global_key_fragment(const uint8_t* __restrict__ k8, int64_t key0,
-                                                   int f, int64_t n_k) {
+                                                   int f, int64_t n_k, int stride = 1) {
   const int l = lane_id();
   int64_t key = key0 + 16 * f + (l & 15);
-  key = key < n_k ? key : n_k - 1;
+  key = (key < n_k ? key : n_k - 1) * stride;
   // plain loads: the two halves of a lane's 32 bytes come from two instructions that each
   // touch half of every row, and the second must find the row in L2 (with streaming loads
   // it was fetched from HBM twice)

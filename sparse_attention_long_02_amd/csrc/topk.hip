@@ -274,7 +274,7 @@ constexpr int TL_MIN_N = 16384;  // rows at least this long (and k <= TL_CAP / 4
 __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t n_rows, int64_t n_k,
     const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int k,
-    int32_t* __restrict__ idx) {
+    int32_t* __restrict__ idx, const uint8_t* __restrict__ redo) {
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t sel[TK_WORDS];
   __shared__ uint32_t tie[TK_WORDS];
@@ -285,6 +285,7 @@ __global__ __launch_bounds__(TL_THREADS) void topk_long_kernel(
   int64_t n;
   const float* srow;
   int32_t* out;
+  if (redo && !redo[(int64_t)blockIdx.y * n_rows + blockIdx.x]) return;  // uniform over the block
   row_geometry(n_rows, n_k, q_pos, pos_offset, row_begin, k, ld, scores, idx, n, srow, out);
   const int tid = threadIdx.x;
   if (n <= k) {
@@ -476,6 +477,91 @@ __global__ __launch_bounds__(TO_THREADS) void sel_candidates_kernel(
   if (tid == 0) redo[orow] = 0;
 }
 
+// Decode: the top-k of each row's candidate segments (the filtering split indexer's).  When
+// no segment overflowed and k <= total <= SEL_CAND_CAP, the segments hold every key above the
+// threshold, and at least k of them, so v* (the k-th largest score) and every key equal to
+// it are among them: the segments are packed into LDS, an exact select gives v*, and LDS
+// bitmaps over the row's positions put the kept keys (and the lowest-positioned ties) in
+// ascending order.  Otherwise the row is marked for the exact full-row selection.
+constexpr int DC_THREADS = 1024;
+constexpr int DC_MAX_SEGS = (int)(4 * (TOPK_MAX_N / (SPLIT_TILES * 64)));
+__global__ __launch_bounds__(DC_THREADS) void dec_cand_topk_kernel(
+    const uint2* __restrict__ cand, const uint32_t* __restrict__ cnt, int64_t n_segs, int64_t n_rows, int64_t n_k,
+    const int32_t* __restrict__ q_pos, int64_t pos_offset, int k, int32_t* __restrict__ idx,
+    uint8_t* __restrict__ redo) {
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t sel[TK_WORDS];
+  __shared__ uint32_t tie[TK_WORDS];
+  __shared__ uint32_t ckey[SEL_CAND_CAP];
+  __shared__ int32_t cpos[SEL_CAND_CAP];
+  __shared__ uint32_t soff[DC_MAX_SEGS + 1];
+  __shared__ uint32_t wtot[DC_THREADS / WAVE];
+  __shared__ uint32_t s_digit, s_above, s_bad;
+  const int64_t i = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t rid = (int64_t)b * n_rows + i;
+  const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + i;
+  int64_t n = pos + 1 < n_k ? pos + 1 : n_k;
+  n = n > 0 ? n : 0;
+  int32_t* out = idx + rid * k;
+  const int tid = threadIdx.x;
+  if (n <= k) {  // every visible key is kept
+    for (int j = tid; j < k; j += DC_THREADS) out[j] = j < n ? j : -1;
+    if (tid == 0) redo[rid] = 0;
+    return;
+  }
+  // segment offsets (one thread per segment), an overflowed segment or too many candidates
+  // leave the row undecided
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  const uint32_t c_own = tid < n_segs ? cnt[rid * n_segs + tid] : 0u;
+  if (c_own > (uint32_t)DEC_SEG) s_bad = 1;
+  uint32_t total;
+  const uint32_t off = block_excl_scan<DC_THREADS>(c_own, wtot, total);
+  if (tid < n_segs) soff[tid] = off;
+  if (tid == 0) soff[n_segs] = total;
+  __syncthreads();
+  if (s_bad || total < (uint32_t)k || total > (uint32_t)SEL_CAND_CAP) {
+    if (tid == 0) redo[rid] = 1;
+    return;
+  }
+  const uint2* cr = cand + rid * n_segs * DEC_SEG;
+  for (int64_t sgi = tid / DEC_SEG; sgi < n_segs; sgi += DC_THREADS / DEC_SEG) {
+    const uint32_t j = (uint32_t)(tid % DEC_SEG);
+    const uint32_t o = soff[sgi];
+    if (j < soff[sgi + 1] - o) {
+      const uint2 e = cr[sgi * DEC_SEG + j];
+      ckey[o + j] = score_key(__uint_as_float(e.x));
+      cpos[o + j] = (int32_t)e.y;
+    }
+  }
+  const int64_t nw = (n + 31) / 32;
+  for (int64_t j = tid; j < nw; j += DC_THREADS) {
+    sel[j] = 0;
+    tie[j] = 0;
+  }
+  __syncthreads();
+  uint32_t rem;
+  const uint32_t vstar = select_lds<DC_THREADS>(ckey, (int)total, (uint32_t)k, hist, wtot, &s_digit, &s_above, rem);
+  for (uint32_t j = tid; j < total; j += DC_THREADS) {
+    const uint32_t u = ckey[j];
+    const int32_t sp = cpos[j];
+    if (u > vstar) atomicOr(&sel[sp >> 5], 1u << (sp & 31));
+    else if (u == vstar) atomicOr(&tie[sp >> 5], 1u << (sp & 31));
+  }
+  __syncthreads();
+  write_kept<DC_THREADS>(sel, tie, n, rem, k, out, wtot);
+  if (tid == 0) redo[rid] = 0;
+}
+
+hipError_t launch_dec_cand_topk(const DecCandArgs& a, hipStream_t st) {
+  if (a.n_rows <= 0 || a.B <= 0) return hipSuccess;
+  if (a.n_k > TOPK_MAX_N || a.n_segs > DC_MAX_SEGS || a.n_segs > DC_THREADS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dec_cand_topk_kernel, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(DC_THREADS), 0, st, a.cand,
+                     a.cnt, a.n_segs, a.n_rows, a.n_k, a.q_pos, a.pos_offset, a.k, a.idx, a.redo);
+  return hipGetLastError();
+}
+
 hipError_t launch_sel_threshold(const SelThresholdArgs& a, hipStream_t st) {
   if (a.n_rows <= 0 || a.B <= 0) return hipSuccess;
   if ((a.n_k + SEL_SAMPLE_STRIDE - 1) / SEL_SAMPLE_STRIDE > TH_MAX || a.ld_s < sel_sample_ld(a.n_k))
@@ -499,7 +585,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   dim3 grid((unsigned)a.n_rows, (unsigned)a.B);
   if (a.n_k >= TL_MIN_N && a.k <= TL_CAP / 4)
     hipLaunchKernelGGL(topk_long_kernel, grid, dim3(TL_THREADS), 0, st, a.scores, a.ld_scores, a.n_rows, a.n_k,
-                       a.q_pos, a.pos_offset, a.row_begin, a.k, a.idx);
+                       a.q_pos, a.pos_offset, a.row_begin, a.k, a.idx, a.redo);
+  else if (a.redo)
+    return hipErrorInvalidValue;  // the row-skipping variant exists for long rows only
   else
     hipLaunchKernelGGL(topk_rows_kernel, grid, dim3(TK_THREADS), 0, st, a.scores, a.ld_scores, a.n_rows, a.n_k,
                        a.q_pos, a.pos_offset, a.row_begin, a.k, a.idx);
