@@ -204,6 +204,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=8192, help="tokens of the chunked-prefill stage")
+    ap.add_argument("--dense-kl", type=int, default=32768, help="rows of the dense warm-up KL stage (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the DSA layer on a single MI355X "
@@ -340,6 +341,31 @@ def main():
     log(f"[bench] indexer KL: scores at selected keys {t_sa * 1e3:.3f} ms, KL {t_kl * 1e3:.3f} ms "
         f"({g_bytes / t_kl / 1e9:.0f} GB/s gathered), mean KL {float(klv.mean()):.4f}")
     del isc, klv
+
+    # indexer KL loss of the dense warm-up stage over the sequence's first rows: dense index
+    # scores (FP8 indexer) and two sweeps of dense attention over every key up to the row
+    Ld = min(args.dense_kl, L)
+    if Ld > 0:
+        kld = torch.empty((Ld,), dtype=torch.float32, device="cuda")
+        ws_kd = torch.empty(dsa.workspace_size(dsa.DSA_OP_KL_DENSE, 1, Ld, Ld, cfg.H, 1, 1, dsa.DSA_BF16),
+                            dtype=torch.uint8, device="cuda")
+
+        def kl_dense():
+            dsa.indexer_kl_dense(qi[:Ld], qs[:Ld], ki[:Ld], ks[:Ld], w[:Ld], q[:Ld], kv[:Ld], cfg.sm_scale,
+                                 kl=kld, ws=ws_kd)
+        kl_dense()
+        t_kd = time_calls(torch, kl_dense, args.stage_reps)
+        keys = kept_keys(Ld, Ld)
+        f_kd = 2 * 2 * cfg.H * cfg.d_qk * keys
+        stages["indexer_kl_dense"] = {
+            "ms": t_kd * 1e3, "rows": Ld, "keys": keys, "bf16_flop": f_kd, "mfma_frac": f_kd / t_kd / PEAK_BF16,
+            "indexer_fp8_flop": indexer_flops(Ld, cfg.H_I, cfg.d_I),
+            "gather_bytes": 2 * keys * cfg.d_qk * 2, "mean_kl": float(kld.mean()),
+            "note": "dense warm-up indexer loss: dense FP8 index scores, then two sweeps of dense attention "
+                    "(head lse, then the KL terms) over every key up to the row"}
+        log(f"[bench] dense warm-up KL over {Ld} rows: {t_kd * 1e3:.3f} ms "
+            f"({f_kd / t_kd / 1e12:.0f} TFLOP/s bf16), mean KL {float(kld.mean()):.4f}")
+        del kld, ws_kd
 
     # backward of the sparse attention over the step's selection (the sparse training
     # stage): seeded bf16 output gradients of the workload's shape

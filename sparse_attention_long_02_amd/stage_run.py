@@ -1,7 +1,7 @@
 """Runs each prefill stage once, at a benchmark workload, for hardware-counter profiling.
 
     python -m sparse_attention_long_02_amd.stage_run [--workload prefill_128k] [--copy-mib 4096]
-                                                     [--training]
+                                                     [--training] [--dense-kl L] [--decode]
 
 Order of the dispatches: one device-to-device copy of --copy-mib MiB (its FETCH_SIZE and
 WRITE_SIZE readings calibrate the counters against a known byte count), then
@@ -9,7 +9,9 @@ dsa_select_prefill (per chunk of rows: key-sample indexer, thresholds, filtering
 candidate top-k; then the streaming selection of any undecided rows), then dsa_sparse_mla on
 that selection.  With --training, then the sparse-stage indexer loss (dsa_indexer_scores_at,
 dsa_indexer_kl) and dsa_sparse_mla_backward for seeded output gradients, as the benchmark
-runs them.  Inputs are the seeded synthetic tensors the benchmark uses.
+runs them.  With --dense-kl L, the dense warm-up loss (dsa_indexer_kl_dense) over the first L
+rows and keys of the same sequence.  With --decode, one dsa_forward_decode of the 64 x 131072
+decode workload.  Inputs are the seeded synthetic tensors the benchmark uses.
 """
 from __future__ import annotations
 
@@ -27,6 +29,9 @@ def main():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--copy-mib", type=int, default=4096)
     ap.add_argument("--training", action="store_true")
+    ap.add_argument("--dense-kl", type=int, default=0)
+    ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
 
     import torch
@@ -45,7 +50,27 @@ def main():
     print(f"[stage_run] copy of {n} bytes done", flush=True)
     del src, dst
 
+    if not args.no_prefill:
+        prefill(args, cfg, torch, bench, dsa)
+    if args.decode:
+        decode(torch, bench, dsa, S)
+
+
+def decode(torch, bench, dsa, S):
+    dcfg = S.CONFIGS["decode_64x128k"]
+    ctx, qi, qs, w, kc, kcs, q, kvc = bench.decode_inputs_on_gpu(dcfg, torch)
+    dsa.forward_decode(ctx, qi, qs, w, kc, kcs, q, kvc, dcfg.k, dcfg.sm_scale, dcfg.d_v)
+    torch.cuda.synchronize()
+    print("[stage_run] forward_decode done", flush=True)
+
+
+def prefill(args, cfg, torch, bench, dsa):
     qi, qs, ki, ks, w, q, kv = bench.prefill_inputs_on_gpu(cfg, torch)
+    if args.dense_kl:
+        n = min(args.dense_kl, cfg.L)
+        dsa.indexer_kl_dense(qi[:n], qs[:n], ki[:n], ks[:n], w[:n], q[:n], kv[:n], cfg.sm_scale)
+        torch.cuda.synchronize()
+        print(f"[stage_run] indexer_kl_dense over {n} rows done", flush=True)
     idx = torch.empty((cfg.L, cfg.k), dtype=torch.int32, device="cuda")
     dsa.select_prefill(qi, qs, ki, ks, w, cfg.k, idx=idx)
     torch.cuda.synchronize()
