@@ -34,7 +34,7 @@ namespace dsa {
 
 constexpr int NBUF = 4;       // chunk buffers (4 x 38912 B)
 constexpr int MLA_WAVES = 4;
-constexpr int KRING = 10;     // K fragments read ahead of the logit MFMAs
+constexpr int KRING = 4;      // K fragments read ahead of the logit MFMAs
 constexpr int O_TILES = MDV / 32;   // 16 O^T tiles per wave
 constexpr float RESCALE_SLACK = 8.f;  // log2 units the running max may lag
 
