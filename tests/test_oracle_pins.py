@@ -534,3 +534,29 @@ def test_attention_backward_single_key_closed_form():
     want[4] = g[0].sum(axis=0)
     want[1] = g[1].sum(axis=0)
     assert np.allclose(dv, want, rtol=1e-14)
+
+
+def test_widen_inputs_matches_torch_decoders():
+    """widen_inputs against torch's own decoders, independently of the oracle's tables: the
+    bf16 operands through torch.bfloat16, the FP8 codes through torch.float8_e4m3fn times
+    the per-row scales, and the fp32 path as a plain cast; a row subset keeps those rows."""
+    cfg = S.CONFIGS["prefill_8k"].with_(L=64, seed=5)
+    inp = S.make_prefill(cfg)
+    rows = np.array([3, 0, 63, 17])
+    for sel in (None, rows):
+        W = O.widen_inputs(inp, sel)
+        r = slice(None) if sel is None else sel
+        bf = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+        f8 = lambda codes: torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+        assert np.array_equal(W["q"], bf(inp.q[r]))
+        assert np.array_equal(W["kv"], bf(inp.kv))
+        assert np.array_equal(W["v"], bf(inp.kv)[:, : cfg.d_v])
+        assert np.array_equal(W["qhat"], f8(inp.qi[r]) * inp.q_scale[r].astype(np.float64)[..., None])
+        assert np.array_equal(W["khat"], f8(inp.ki) * inp.k_scale.astype(np.float64)[:, None])
+        assert np.array_equal(W["w"], inp.w[r].astype(np.float64))
+    t = S.CONFIGS["tiny_fp32_512"].with_(L=48)
+    tin = S.make_prefill(t)
+    W = O.widen_inputs(tin, rows[rows < 48])
+    assert np.array_equal(W["qhat"], tin.qi[rows[rows < 48]].astype(np.float64)
+                          * tin.q_scale[rows[rows < 48]].astype(np.float64)[..., None])
+    assert np.array_equal(W["v"], tin.v.astype(np.float64))
