@@ -4,11 +4,15 @@ sequences of 131072 cached tokens.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_128k]
                     [--decode-workload decode_64x128k | none] [--no-cpu-baseline]
+                    [--other-workloads prefill_8k,prefill_32k | none]
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors from the generator shared with
 the tests, already resident in HBM when timing starts.  A step is one call of
-dsa_forward_prefill over the whole sequence.  The roofline object describes the slower of
-the two prefill stages, timed separately with HIP events on the stream they run on.
+dsa_forward_prefill over the whole sequence; `value` is the sequence length over the mean
+step time of the K timed steps (their median and minimum are reported beside it).  The
+roofline object describes the slower of the two prefill stages, timed separately with HIP
+events on the stream they run on.  The 8K and 32K prefill rates and the decode step time
+are reported as fields of the same line.
 """
 from __future__ import annotations
 
@@ -146,6 +150,39 @@ def time_calls(torch, fn, reps):
     return start.elapsed_time(end) / 1e3 / reps
 
 
+def time_each(torch, fn, reps):
+    """Seconds of each of `reps` back-to-back calls (an event pair around every call, all on
+    the current stream): (mean over the whole run, median, min)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    each = sorted(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(reps))
+    return ev[0].elapsed_time(ev[reps]) / 1e3 / reps, float(np.median(each)), each[0]
+
+
+def prefill_rate(cfg, torch, dsa, warmup, reps):
+    """Whole-layer prefill rate of one more workload (its own inputs, same entry point)."""
+    qi, qs, ki, ks, w, q, kv = prefill_inputs_on_gpu(cfg, torch)
+    L, k = cfg.L, cfg.k
+    idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((L, cfg.H, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((L, cfg.H), dtype=torch.float32, device="cuda")
+    ws_n = dsa.workspace_size(dsa.DSA_OP_PREFILL, 1, L, L, cfg.H, cfg.d_v, k, dsa.DSA_BF16)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
+
+    def step():
+        dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, k, cfg.sm_scale, cfg.d_v, idx=idx, out=out, lse=lse, ws=ws)
+    for _ in range(warmup):
+        step()
+    mean, med, mn = time_each(torch, step, reps)
+    return {"workload": cfg.name, "seq_len": L, "tokens_per_s": L / mean, "ms_per_step": mean * 1e3,
+            "ms_median": med * 1e3, "ms_min": mn * 1e3, "steps": reps, "warmup": warmup}
+
+
 def cpu_baseline(cfg, budget_s=15.0):
     """The float64 oracle, as it stands, on a bounded sample of query rows of the same
     workload: rows drawn uniformly from the sequence, whole layer per row, until about
@@ -197,14 +234,16 @@ def cpu_model() -> str:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--decode-workload", default="decode_64x128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=8192, help="tokens of the chunked-prefill stage")
     ap.add_argument("--dense-kl", type=int, default=32768, help="rows of the dense warm-up KL stage (0: skip)")
+    ap.add_argument("--other-workloads", default="prefill_8k,prefill_32k",
+                    help="comma-separated prefill workloads also timed (whole layer), or none")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the DSA layer on a single MI355X "
@@ -236,15 +275,11 @@ def main():
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
+    mean_s, med_s, min_s = time_each(torch, step, args.steps)
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / args.steps
-    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step (wall {wall:.2f}s)")
+    ms_step = mean_s * 1e3
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step, median {med_s * 1e3:.3f}, "
+        f"min {min_s * 1e3:.3f} (wall {wall:.2f}s)")
 
     # the two stages alone (same stream, HIP events)
     t_sel = time_calls(torch, lambda: dsa.select_prefill(qi, qs, ki, ks, w, k, idx=idx), args.stage_reps)
@@ -403,11 +438,22 @@ def main():
                                out=dout, lse=dlse, ws=ws_d)
         for _ in range(args.warmup):
             dstep()
-        t_dec = time_calls(torch, dstep, max(args.steps, 10))
+        t_dec, t_dec_med, t_dec_min = time_each(torch, dstep, max(args.steps, 10))
         icache = dcfg.batch * dcfg.L * (dcfg.d_I + 4)
-        log(f"[bench] decode {t_dec * 1e6:.1f} us/step")
-        decode = {"workload": dcfg.name, "us_per_step": t_dec * 1e6, "batch": dcfg.batch, "ctx": dcfg.L,
+        log(f"[bench] decode {t_dec * 1e6:.1f} us/step (median {t_dec_med * 1e6:.1f}, min {t_dec_min * 1e6:.1f})")
+        decode = {"workload": dcfg.name, "us_per_step": t_dec * 1e6, "us_median": t_dec_med * 1e6,
+                  "us_min": t_dec_min * 1e6, "steps": max(args.steps, 10), "batch": dcfg.batch, "ctx": dcfg.L,
                   "index_cache_bytes": icache, "index_cache_hbm_frac": icache / t_dec / PEAK_HBM}
+        del ctx, dqi, dqs, dw, kc, kcs, dq, kvc, ws_d, didx, dout, dlse
+        torch.cuda.empty_cache()
+
+    others = []
+    if args.other_workloads != "none":
+        for name in args.other_workloads.split(","):
+            r = prefill_rate(S.CONFIGS[name], torch, dsa, args.warmup, args.steps)
+            log(f"[bench] {name}: {r['tokens_per_s']:.0f} tokens/s ({r['ms_per_step']:.3f} ms/step)")
+            others.append(r)
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -422,7 +468,9 @@ def main():
         "config": {"workload": cfg.name, "seq_len": L, "batch": 1, "topk": k, "heads": cfg.H,
                    "d_qk": cfg.d_qk, "d_v": cfg.d_v, "indexer_heads": cfg.H_I, "indexer_dim": cfg.d_I,
                    "parallelism": "single GPU"},
-        "roofline": roof, "stages": stages, "decode": decode, "cpu_baseline": cpu,
+        "ms_per_step_median": med_s * 1e3, "ms_per_step_min": min_s * 1e3,
+        "roofline": roof, "stages": stages, "decode": decode, "other_prefill_workloads": others,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
