@@ -405,14 +405,15 @@ constexpr int TH_MAX = (int)(TOPK_MAX_N / SEL_SAMPLE_STRIDE);
 
 // The row's sample keys live in dynamic LDS of ceil(n_k / SEL_SAMPLE_STRIDE) words (16 KB at
 // 131072 keys), so that many blocks share a CU.
-__global__ __launch_bounds__(TH_THREADS) void sel_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
+template <int NT>
+__global__ __launch_bounds__(NT) void sel_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
                                                                    int64_t rows_pad, int64_t n_rows, int64_t n_k,
                                                                    const int32_t* __restrict__ q_pos,
                                                                    int64_t row_begin, int k,
                                                                    float* __restrict__ thr) {
   extern __shared__ uint32_t keys[];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t wtot[TH_THREADS / WAVE];
+  __shared__ uint32_t wtot[NT / WAVE];
   __shared__ uint32_t s_digit, s_above;
   const int64_t i = n_rows - 1 - (int64_t)blockIdx.x;
   const int b = blockIdx.y;
@@ -430,10 +431,10 @@ __global__ __launch_bounds__(TH_THREADS) void sel_threshold_kernel(const float* 
   int r = (int)ceilf(m + 5.f * sqrtf(m) + 5.f);
   r = r < ns ? r : ns;
   const float* srow = samp + ((int64_t)b * rows_pad + i) * ld_s;
-  for (int j = tid; j < ns; j += TH_THREADS) keys[j] = score_key(srow[j]);
+  for (int j = tid; j < ns; j += NT) keys[j] = score_key(srow[j]);
   __syncthreads();
   uint32_t rem;
-  const uint32_t T = select_lds<TH_THREADS>(keys, ns, (uint32_t)r, hist, wtot, &s_digit, &s_above, rem);
+  const uint32_t T = select_lds<NT>(keys, ns, (uint32_t)r, hist, wtot, &s_digit, &s_above, rem);
   // the filter keeps the keys scoring strictly above this sample (the key is mapped back to
   // its fp32 value; a -0 sample was read as +0, and the two compare equal anyway)
   if (tid == 0) *out = __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
@@ -567,8 +568,13 @@ hipError_t launch_sel_threshold(const SelThresholdArgs& a, hipStream_t st) {
   if ((a.n_k + SEL_SAMPLE_STRIDE - 1) / SEL_SAMPLE_STRIDE > TH_MAX || a.ld_s < sel_sample_ld(a.n_k))
     return hipErrorInvalidValue;
   const size_t lds = (size_t)((a.n_k + SEL_SAMPLE_STRIDE - 1) / SEL_SAMPLE_STRIDE) * sizeof(uint32_t);
-  hipLaunchKernelGGL(sel_threshold_kernel, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(TH_THREADS), lds, st, a.samp,
-                     a.ld_s, a.rows_pad, a.n_rows, a.n_k, a.q_pos, a.row_begin, a.k, a.thr);
+  // few rows (decode): one 1024-thread block per row, so the select's passes run 4x wider
+  if (a.n_rows * a.B < 512)
+    hipLaunchKernelGGL(sel_threshold_kernel<1024>, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(1024), lds, st,
+                       a.samp, a.ld_s, a.rows_pad, a.n_rows, a.n_k, a.q_pos, a.row_begin, a.k, a.thr);
+  else
+    hipLaunchKernelGGL(sel_threshold_kernel<TH_THREADS>, dim3((unsigned)a.n_rows, (unsigned)a.B), dim3(TH_THREADS), lds,
+                       st, a.samp, a.ld_s, a.rows_pad, a.n_rows, a.n_k, a.q_pos, a.row_begin, a.k, a.thr);
   return hipGetLastError();
 }
 
