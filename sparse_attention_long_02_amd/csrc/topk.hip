@@ -444,9 +444,10 @@ __global__ __launch_bounds__(TO_THREADS) void sel_candidates_kernel(
     const uint2* __restrict__ cand, const uint32_t* __restrict__ cnt, int64_t rows_pad, int64_t n_rows, int64_t n_k,
     const int32_t* __restrict__ q_pos, int64_t row_begin, int k, int32_t* __restrict__ idx, int64_t out_rows,
     int64_t out_row0, uint8_t* __restrict__ redo) {
-  // the candidates' score keys in LDS (24 KB, so several blocks share a CU); their key
-  // indices are read back from the list when the kept ones are written
+  // the candidates' score keys and key indices in LDS (48 KB, so three blocks share a CU):
+  // the list is read from memory once
   __shared__ uint32_t ckey[SEL_CAND_CAP];
+  __shared__ int32_t cidx[SEL_CAND_CAP];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wtot[TO_THREADS / WAVE];
   __shared__ uint32_t s_digit, s_above;
@@ -470,11 +471,15 @@ __global__ __launch_bounds__(TO_THREADS) void sel_candidates_kernel(
     return;
   }
   const uint2* cr = cand + r * SEL_CAND_PITCH;
-  for (uint32_t j = tid; j < c; j += TO_THREADS) ckey[j] = score_key(__uint_as_float(cr[j].x));
+  for (uint32_t j = tid; j < c; j += TO_THREADS) {
+    const uint2 e = cr[j];
+    ckey[j] = score_key(__uint_as_float(e.x));
+    cidx[j] = (int32_t)e.y;
+  }
   __syncthreads();
   uint32_t rem;
   const uint32_t vstar = select_lds<TO_THREADS>(ckey, (int)c, (uint32_t)k, hist, wtot, &s_digit, &s_above, rem);
-  write_from_candidates(ckey, [cr](uint32_t j) { return (int32_t)cr[j].y; }, c, vstar, rem, k, out, wtot);
+  write_from_candidates(ckey, [](uint32_t j) { return cidx[j]; }, c, vstar, rem, k, out, wtot);
   if (tid == 0) redo[orow] = 0;
 }
 
