@@ -195,11 +195,12 @@ def test_prefill_every_row_vs_oracle(c2):
 
 def test_decode_small_batch():
     """Decode over caches of different lengths: selection == top-k of the library's scores,
-    overlap with the oracle, attention on the GPU's selection."""
-    cfg = S.CONFIGS["decode_64x128k"].with_(L=6000, batch=4)
-    _say("[decode] B=4, n_k_max=6000")
+    overlap with the oracle, attention on the GPU's selection.  The last sequence has an
+    empty cache (ctx_len 0): nothing is kept, the output is zero and lse is -inf."""
+    cfg = S.CONFIGS["decode_64x128k"].with_(L=6000, batch=5)
+    _say("[decode] B=5, n_k_max=6000")
     inp = S.make_decode(cfg)
-    ctx_l = [1, 2048, 2049, 6000]
+    ctx_l = [1, 2048, 2049, 6000, 0]
     ctx = torch.tensor(ctx_l, dtype=torch.int32, device="cuda")
     qi, qs, w = dev_u8(inp.qi), dev_f32(inp.q_scale), dev_f32(inp.w)
     kc, kcs = dev_u8(inp.ki), dev_f32(inp.k_scale)
@@ -221,6 +222,11 @@ def test_decode_small_batch():
         qf = O.bf16_to_f64(inp.q[b])[None]
         r = O.dsa_rows(qhat, inp.w[b][None].astype(np.float64), khat, qf, kvf, kvf[:, :512], np.array([pos]),
                        cfg.k, cfg.sm_scale)
+        if pos < 0:  # no preceding token: the oracle keeps nothing, outputs zero, lse -inf
+            assert np.array_equal(g_idx[b], r["idx"][0]) and np.all(r["idx"] == -1), b
+            assert np.array_equal(got[b], r["out"][0]) and np.all(got[b] == 0), b
+            assert np.all(np.isneginf(r["lse"][0])) and torch.all(torch.isneginf(lse[b])), b
+            continue
         ov, _ = overlap(g_idx[b][None], r["idx"])
         assert ov >= OVERLAP_MIN, (b, ov)
         o, l = O.sparse_mqa(qf, kvf, kvf[:, :512], g_idx[b][None], cfg.sm_scale)
@@ -255,3 +261,28 @@ def test_decode_long_rows_selection():
     assert np.array_equal(g[7], np.arange(cfg.k))      # all ties: the lowest indices
     assert np.array_equal(g[6][:1], [0]) and np.all(g[6][1:] == -1)
     assert np.array_equal(g[5], np.arange(2048))
+
+
+@pytest.mark.parametrize("L", [1, 17, 65, 130])
+def test_prefill_short_sequences_vs_oracle(L):
+    """Sequences shorter than one 64-key tile, one 16-row group, or k: every query keeps all
+    of its preceding keys (0..t, -1 padded), so the layer is dense causal attention; every
+    row's output and lse against the float64 oracle (ragged tiles and groups on both sides)."""
+    cfg = S.CONFIGS["prefill_8k"].with_(L=L, seed=70 + L)
+    _say(f"[prefill, short] L={L}")
+    inp = S.make_prefill(cfg)
+    qi, qs, ki, ks, w = indexer_inputs_dev(inp)
+    q, kv = dev_bf16(inp.q), dev_bf16(inp.kv)
+    idx, out, lse = dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, cfg.k, cfg.sm_scale, cfg.d_v)
+    torch.cuda.synchronize()
+    g_idx = idx.cpu().numpy()
+    for t in range(L):
+        assert np.array_equal(g_idx[t, : t + 1], np.arange(t + 1)) and np.all(g_idx[t, t + 1:] == -1), t
+    W = O.widen_inputs(inp)
+    rows = np.arange(L)
+    ref = O.dsa_rows(W["qhat"], W["w"], W["khat"], W["q"], W["kv"], W["v"], rows, cfg.k, cfg.sm_scale)
+    assert np.array_equal(ref["idx"], g_idx)
+    err = float(np.abs(out_to_f64(out) - ref["out"]).max())
+    _say(f"  attention max-abs {err:.3e}")
+    assert err <= ATOL_BF16
+    assert np.allclose(lse.cpu().numpy(), ref["lse"], atol=1e-3, rtol=1e-4)
