@@ -13,16 +13,17 @@
 //     rows), the keys are N (B = 16 keys x 128 bytes).  The MFMA's block scales multiply
 //     every product by 2^-25, exactly (powers of two), so each head dot x lies in
 //     (-0.77, 0.77) whatever the FP8 codes (|x| <= 448^2 * 128 * 2^-25);
-//   * ReLU: pairs of head dots are packed to f16 (round toward zero) and clamped at 0 with
-//     one packed max (one VALU op per head value);
+//   * ReLU: pairs of head dots are packed to f16 (round to nearest even) by one conversion
+//     whose output clamp to [0, 1] is the ReLU, as every head dot lies below 1 in magnitude
+//     (one VALU op per pair of head values);
 //   * the weighted head sum runs on the matrix core: per "head half" (32 heads) a
 //     16x16x32 f16 MFMA whose A operand holds the half's normalised weights
 //     c' = c / max|c| (f16) in every row and whose B operand is the ReLU'd values, so every
 //     lane receives the half's sum for its key (l % 16) in fp32;
 //   * the two head halves are added; the result is scaled by max|c| * 2^25 and by k_scale.
-// Relative error of a term: <= 2^-10 (f16 truncation) + 2^-11 (f16 weight); f16
-// subnormals below 2^-14 (head dots below 2^11 in code units) carry an absolute error of
-// at most 2 code units.
+// Relative error of a term: <= 2^-11 (f16 rounding of the head dot) + 2^-11 (f16 weight);
+// f16 subnormals below 2^-14 (head dots below 2^11 in code units) carry an absolute error
+// of at most 1 code unit.
 #pragma once
 
 #include "dsa_device.h"
@@ -93,14 +94,22 @@ __device__ __forceinline__ void load_idx_half(IdxHalf& Q, const uint8_t* __restr
 }
 
 // ReLU'd f16 B operand of the head-sum MFMA from the two FP8 MFMA results of a head half
-// (slot e = head block e/4, MFMA row 4g + e%4).
+// (slot e = head block e/4, MFMA row 4g + e%4).  min(max(., 0), 1) of the converted pair
+// compiles to v_cvt_pk_f16_f32 with its clamp bit, which on this part gives exactly the
+// ReLU of values below 1 in magnitude, the sign of zero included (v_cvt_pkrtz_f16_f32's
+// clamp does not: negative inputs keep their sign there).
 __device__ __forceinline__ v8h relu_pack(v4f x0, v4f x1) {
   typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  typedef float f2v __attribute__((ext_vector_type(2)));
   const h2v zero = h2v{(_Float16)0.f, (_Float16)0.f};
-  const h2v r0 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0[0], x0[1])), zero);
-  const h2v r1 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0[2], x0[3])), zero);
-  const h2v r2 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x1[0], x1[1])), zero);
-  const h2v r3 = __builtin_elementwise_max(__builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x1[2], x1[3])), zero);
+  const h2v one = h2v{(_Float16)1.f, (_Float16)1.f};
+  auto relu = [&](float a, float b) {
+    return __builtin_elementwise_min(__builtin_elementwise_max(__builtin_convertvector(f2v{a, b}, h2v), zero), one);
+  };
+  const h2v r0 = relu(x0[0], x0[1]);
+  const h2v r1 = relu(x0[2], x0[3]);
+  const h2v r2 = relu(x1[0], x1[1]);
+  const h2v r3 = relu(x1[2], x1[3]);
   return v8h{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
