@@ -113,12 +113,22 @@ def mla_flops(L, k, H, d_qk, d_v):
 
 # ------------------------------------------------------------------------------ counters
 
+def sources_sha256(paths):
+    """sha256 over the named files (repository-relative, comma-separated) read in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths.split(","):
+        with open(os.path.join(ROOT, rel), "rb") as g:
+            h.update(g.read())
+    return h.hexdigest()
+
+
 def recorded_traffic(kernel, workload):
     """HBM bytes per launch recorded from the FETCH_SIZE / WRITE_SIZE counter passes under
     profiles/ (calibrated on a copy of known size), or None when none is recorded or the
-    kernel's source has changed since (its sha256 no longer matches)."""
+    kernel's sources (its .hip file and the headers it includes) have changed since: their
+    sha256 no longer matches."""
     import glob
-    import hashlib
     import re
     pat = re.compile(r"^traffic (\S+) (\S+) bytes=(\d+) source=(\S+) sha256=([0-9a-f]+)\s*$")
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -127,12 +137,10 @@ def recorded_traffic(kernel, workload):
                 m = pat.match(line)
                 if not m or m.group(1) != kernel or m.group(2) != workload:
                     continue
-                src = os.path.join(ROOT, m.group(4))
-                if not os.path.exists(src):
+                if not all(os.path.exists(os.path.join(ROOT, r)) for r in m.group(4).split(",")):
                     return None
-                with open(src, "rb") as g:
-                    if hashlib.sha256(g.read()).hexdigest() != m.group(5):
-                        return None
+                if sources_sha256(m.group(4)) != m.group(5):
+                    return None
                 return int(m.group(3))
     return None
 

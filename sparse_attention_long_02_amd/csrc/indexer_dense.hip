@@ -205,9 +205,12 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   auto tile_step = [&](int t) {
     const uint8_t* tile = ring + (t % DN_SLOTS) * DN_SLOT_BYTES;
     float v[4];
+    // each fragment's B operand is read from LDS one fragment ahead
+    v8i bnext = dense_fragment(tile, 0, lane);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const v8i bf = dense_fragment(tile, f, lane);
+      const v8i bf = bnext;
+      if (f < 3) bnext = dense_fragment(tile, f + 1, lane);
       v4f d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
