@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 
 #include "dsa_kernels.h"
 
@@ -170,9 +171,13 @@ static size_t sel_bytes(int64_t B, int64_t n_q, int64_t n_k) {
 
 // rows 0 .. n_q - 1 of each of B sequences (row r at position (q_pos ? q_pos[b] : 0) + r)
 // (kbs: key rows between the sequences of k8 / ks; 0 means n_k)
+// chunk_done (optional): called after each chunk with its rows [r0, r0 + n), once they are
+// final on stream s; the chunk's undecided rows are then selected before the call instead of
+// in one pass after the last chunk.
+using ChunkHook = std::function<int(int64_t r0, int64_t n)>;
 static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks, const float* w,
                       int64_t B, int64_t n_q, int64_t n_k, const int32_t* q_pos, int32_t k, int32_t* idx, void* ws,
-                      size_t ws_bytes, hipStream_t s, int64_t kbs = 0) {
+                      size_t ws_bytes, hipStream_t s, int64_t kbs = 0, const ChunkHook* chunk_done = nullptr) {
   SUPPORT(n_k <= FUSED_MAX_KEYS, "FP8 selection supports up to %lld keys", (long long)FUSED_MAX_KEYS);
   dsa::PrefillTopkArgs pa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, k, idx, nullptr, kbs};
   if (!sel_filtered(n_k)) return hip_status(dsa::launch_prefill_topk(pa, s), "indexer/top-k launch");
@@ -199,7 +204,18 @@ static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, con
     dsa::SelCandArgs ca{sw.cand, sw.cnt, rp, B, n, n_k, q_pos, r0, k, idx, n_q, r0, sw.redo};
     st = hip_status(dsa::launch_sel_candidates(ca, s), "candidate top-k launch");
     if (st) return st;
+    if (chunk_done) {
+      dsa::PrefillTopkArgs pc = pa;
+      pc.redo = sw.redo;
+      pc.row_begin = r0;
+      pc.row_end = r0 + n;
+      st = hip_status(dsa::launch_prefill_topk(pc, s), "exact selection of the chunk's remaining rows");
+      if (st) return st;
+      st = (*chunk_done)(r0, n);
+      if (st) return st;
+    }
   }
+  if (chunk_done) return DSA_OK;
   pa.redo = sw.redo;
   return hip_status(dsa::launch_prefill_topk(pa, s), "exact selection of the remaining rows");
 }
@@ -333,6 +349,34 @@ int dsa_sparse_mla(const void* q, int64_t ld_q, const void* kv, int64_t ld_kv, c
   return hip_status(dsa::launch_sparse_mla(a, (hipStream_t)stream), "dsa_sparse_mla launch");
 }
 
+// A second stream (default priority) per host thread and device.  The prefill runs the
+// attention of each finished selection chunk on it, beside the selection of the next chunk,
+// and the caller's stream waits for it before the call's work ends.  Created on first use and
+// kept for the life of the thread.
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev = nullptr;
+};
+static AuxStream* aux_stream() {
+  constexpr int MAX_DEVICES = 64;
+  thread_local AuxStream aux[MAX_DEVICES];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  AuxStream& a = aux[dev];
+  if (!a.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t ev = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    a.s = st;
+    a.ev = ev;
+  }
+  return &a;
+}
+
 static int select_prefill(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
                           const float* w, int64_t L, int32_t H_I, int32_t d_I, int32_t k, int32_t idx_dtype,
                           int32_t* idx, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -393,6 +437,36 @@ int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_i
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "dsa_forward_prefill needs %zu workspace bytes (got %zu)", need, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
+  // FP8 selection in several chunks: each chunk's attention runs on a second stream while the
+  // next chunk is selected (the two kernels share the GPU; run back to back they take a few
+  // per cent longer).  Chunk launches never split their keys, so they need no workspace.
+  AuxStream* aux = nullptr;
+  if (!f32 && attn_dtype == DSA_BF16 && sel_filtered(L) && sel_chunk_rows(1, L) < L) aux = aux_stream();
+  if (aux) {
+    bool forked = false;
+    const ChunkHook mla_chunk = [&](int64_t r0, int64_t n) -> int {
+      int e = hip_status(hipEventRecord(aux->ev, s), "prefill: event record");
+      if (e) return e;
+      e = hip_status(hipStreamWaitEvent(aux->s, aux->ev, 0), "prefill: stream wait");
+      if (e) return e;
+      forked = true;
+      dsa::MlaArgs a{(const uint16_t*)q + r0 * H * ld_q, kv, v, idx + r0 * k, 1, n, L, H, d_qk, d_v, k, sm_scale,
+                     attn_dtype, (uint16_t*)out + r0 * H * d_v, lse ? lse + r0 * H : nullptr, nullptr, 0, ld_q,
+                     ld_kv, v ? ld_v : 0, L * ld_kv, v ? L * ld_v : 0};
+      a.max_split = 1;
+      return hip_status(dsa::launch_sparse_mla(a, aux->s), "prefill sparse attention launch (chunk)");
+    };
+    st = select_fp8((const uint8_t*)q_idx, q_scale, (const uint8_t*)k_idx, k_scale, w, 1, L, L, nullptr, k, idx, ws,
+                    s_bytes, s, 0, &mla_chunk);
+    if (forked) {
+      // join, whatever happened: the caller's stream waits for every attention launch
+      int e = hip_status(hipEventRecord(aux->ev, aux->s), "prefill: event record");
+      if (!e) e = hip_status(hipStreamWaitEvent(s, aux->ev, 0), "prefill: stream wait");
+      if (e) (void)hipStreamSynchronize(aux->s);
+      if (!st) st = e;
+    }
+    return st;
+  }
   st = select_prefill(q_idx, q_scale, k_idx, k_scale, w, L, H_I, d_I, k, idx_dtype, idx, ws, s_bytes, s);
   if (st) return st;
   dsa::MlaArgs a{q, kv, v, idx, 1, L, L, H, d_qk, d_v, k, sm_scale, attn_dtype, out, lse,

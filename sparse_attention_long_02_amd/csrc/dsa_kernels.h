@@ -96,6 +96,9 @@ struct MlaArgs {
   // element strides (0: dense): between the head rows of q, the rows of kv and v, and the
   // sequences of kv and v
   int64_t ld_q = 0, ld_kv = 0, ld_v = 0, bs_kv = 0, bs_v = 0;
+  // at most this many key splits per query (0: as sparse_mla_splits chooses; 1: never split,
+  // so no workspace is used)
+  int32_t max_split = 0;
 };
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 // workspace of the bf16 kernel when it splits each query's keys over several blocks
@@ -119,6 +122,9 @@ struct PrefillTopkArgs {
   // 4 rows runs if any of its rows is marked) and the rows below k are left alone.
   const uint8_t* redo = nullptr;
   int64_t k_bstride = 0;    // key rows between sequences of k8 / ks (0: n_k)
+  // only rows [row_begin, row_end) of each sequence are selected and written (row_end < 0:
+  // up to n_q)
+  int64_t row_begin = 0, row_end = -1;
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 

@@ -397,16 +397,16 @@ __device__ __forceinline__ GroupGeom group_geom(int G, int B, int n_q, int n_k, 
   return g;
 }
 
-// With a redo list, a group runs only if one of its rows (from row_lo up) is marked.
+// With a redo list, a group runs only if one of its rows in [row_lo, row_end) is marked.
 __device__ __forceinline__ bool group_skipped(const uint8_t* __restrict__ redo, const GroupGeom& g, int n_q,
-                                              int row_lo) {
+                                              int row_lo, int row_end) {
   if (!redo) return false;
   const uint8_t* r = redo + (size_t)g.b * n_q;
   bool any = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = g.row_hi - 4 + j;
-    if (row >= row_lo && row >= 0) any |= r[row] != 0;
+    if (row >= row_lo && row < row_end && row >= 0) any |= r[row] != 0;
   }
   return !any;
 }
@@ -414,8 +414,8 @@ __device__ __forceinline__ bool group_skipped(const uint8_t* __restrict__ redo, 
 __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int B,
-    int n_q, int n_k, int64_t kbs, int row_lo, int k, int n_groups, int32_t* __restrict__ idx,
-    const uint8_t* __restrict__ redo) {
+    int n_q, int n_k, int64_t kbs, int row_lo, int row_end, int k, int g_begin, int g_end,
+    int32_t* __restrict__ idx, const uint8_t* __restrict__ redo) {
   // ring of three tile pairs (pair p = tiles 2p, 2p+1) and their key scales
   __shared__ __align__(16) uint8_t tk0[TILE_BYTES];
   __shared__ __align__(16) uint8_t tk1[TILE_BYTES];
@@ -438,9 +438,9 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     // ---------------- scoring waves ----------------
     const int f = wv >> 1, hh = wv & 1;
     const TileDma dl = tile_dma_lane(wv, lane);
-    for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
+    for (int G = g_begin + blockIdx.x; G < g_end; G += gridDim.x) {
       const GroupGeom g = group_geom(G, B, n_q, n_k, q_pos);
-      if (group_skipped(redo, g, n_q, row_lo)) continue;
+      if (group_skipped(redo, g, n_q, row_lo, row_end)) continue;
       if (g.n_keys <= k) continue;  // every row keeps all it sees: the owners write it
       const int row0 = g.row_hi - 4;
       const size_t rbase = (size_t)g.b * n_q;
@@ -449,8 +449,8 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
       IdxHalf Qh[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // rows below row_lo are not this kernel's: score a valid row
-        const size_t r = rbase + max(row0 + j, row_lo);
+        // rows outside [row_lo, row_end) are not this launch's: score a valid row
+        const size_t r = rbase + min(max(row0 + j, row_lo), row_end - 1);
         const float cmax = row_cmax(qs + r * IDX_HEADS, w + r * IDX_HEADS);
         load_idx_half(Qh[j], q8 + r * IDX_HEADS * IDX_DIM, qs + r * IDX_HEADS, w + r * IDX_HEADS, hh, cmax);
       }
@@ -503,11 +503,11 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
   } else {
     // ---------------- owner waves ----------------
     const int r = wv - PF_SCORE_WAVES;
-    for (int G = blockIdx.x; G < n_groups; G += gridDim.x) {
+    for (int G = g_begin + blockIdx.x; G < g_end; G += gridDim.x) {
       const GroupGeom g = group_geom(G, B, n_q, n_k, q_pos);
-      if (group_skipped(redo, g, n_q, row_lo)) continue;
+      if (group_skipped(redo, g, n_q, row_lo, row_end)) continue;
       const int my_row = g.row_hi - 4 + r;
-      const bool valid = my_row >= row_lo;
+      const bool valid = my_row >= row_lo && my_row < row_end;
       // last key this row sees (-1: none)
       const int64_t lim64 = min((int64_t)g.pos0 + my_row, (int64_t)n_k - 1);
       const int lim = (int)(lim64 < -1 ? -1 : lim64);
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
           for (int j = lane; j < k; j += WAVE) out[j] = j <= lim ? j : -1;
         continue;
       }
-      const size_t rq = (size_t)g.b * n_q + max(my_row, row_lo);
+      const size_t rq = (size_t)g.b * n_q + min(max(my_row, row_lo), row_end - 1);
       OwnerState S{0, 0u, 0u, 0u, row_cmax(qs + rq * IDX_HEADS, w + rq * IDX_HEADS)};
       if (lane == 0) lds_store(&s_cnt[r], __int_as_float(0));
       const int nsteps = (g.n_keys + STEP_KEYS - 1) / STEP_KEYS;
@@ -560,11 +560,11 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
   }
 }
 
-// rows [0, n) of each sequence (row t at position t) keep every key they see:
+// rows [t0, n) of each sequence (row t at position t) keep every key they see:
 // idx[b][t] = 0 .. min(t, n_k - 1), -1 padded
-__global__ __launch_bounds__(256) void prefill_fill_kernel(int64_t n, int64_t n_q, int64_t n_k, int k,
+__global__ __launch_bounds__(256) void prefill_fill_kernel(int64_t t0, int64_t n, int64_t n_q, int64_t n_k, int k,
                                                            int32_t* __restrict__ idx) {
-  const int64_t t = blockIdx.x;
+  const int64_t t = t0 + blockIdx.x;
   if (t >= n) return;
   const int64_t lim = t < n_k - 1 ? t : n_k - 1;
   int32_t* out = idx + ((int64_t)blockIdx.y * n_q + t) * k;
@@ -572,18 +572,20 @@ __global__ __launch_bounds__(256) void prefill_fill_kernel(int64_t n, int64_t n_
 }
 
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
-  // Without q_pos, row t sits at position t: rows below k keep every key they see and are
-  // written by the fill kernel.  With q_pos the positions live on the device, and groups
-  // whose rows see at most k keys are written by the fused kernel's owners.
-  int64_t row_lo = 0;
+  // Rows [row_begin, row_end) of every sequence (row_end < 0: to n_q).  Without q_pos, row t
+  // sits at position t: rows below k keep every key they see and are written by the fill
+  // kernel.  With q_pos the positions live on the device, and groups whose rows see at most
+  // k keys are written by the fused kernel's owners.
+  const int64_t row_end = a.row_end < 0 || a.row_end > a.n_q ? a.n_q : a.row_end;
+  int64_t row_lo = a.row_begin > 0 ? a.row_begin : 0;
   if (!a.q_pos) {
-    row_lo = a.k < a.n_q ? a.k : a.n_q;
-    if (row_lo > 0 && !a.redo)
-      hipLaunchKernelGGL(prefill_fill_kernel, dim3((unsigned)row_lo, (unsigned)a.B), dim3(256), 0, st, row_lo,
-                         a.n_q, a.n_k, a.k, a.idx);
+    const int64_t below = a.k < row_end ? a.k : row_end;  // rows [row_lo, below) keep all keys
+    if (below > row_lo && !a.redo)
+      hipLaunchKernelGGL(prefill_fill_kernel, dim3((unsigned)(below - row_lo), (unsigned)a.B), dim3(256), 0, st,
+                         row_lo, below, a.n_q, a.n_k, a.k, a.idx);
+    row_lo = below > row_lo ? below : row_lo;
   }
-  const int64_t n_rows = a.n_q - row_lo;
-  if (n_rows > 0) {
+  if (row_end > row_lo) {
     static int n_cu = 0;
     if (n_cu == 0) {
       int dev = 0;
@@ -591,12 +593,16 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
           hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
         n_cu = 256;
     }
-    const int64_t n_groups = a.B * ((n_rows + 3) / 4);
+    // group G holds rows n_q - 4 (G / B) - 4 .. n_q - 4 (G / B) - 1 of sequence G % B: the
+    // groups that meet rows [row_lo, row_end)
+    const int64_t g_begin = a.B * ((a.n_q - row_end) / 4);
+    const int64_t g_end = a.B * ((a.n_q - 1 - row_lo) / 4 + 1);
+    const int64_t n_groups = g_end - g_begin;
     const int64_t blocks = n_groups < n_cu ? n_groups : n_cu;
     hipLaunchKernelGGL(prefill_idx_topk_kernel, dim3((unsigned)blocks), dim3(PF_WAVES * 64), 0, st, a.q8, a.qs,
                        a.k8, a.ks, a.w, a.q_pos, (int)a.B, (int)a.n_q, (int)a.n_k,
-                       a.k_bstride ? a.k_bstride : a.n_k, (int)row_lo, a.k,
-                       (int)n_groups, a.idx, a.redo);
+                       a.k_bstride ? a.k_bstride : a.n_k, (int)row_lo, (int)row_end, a.k, (int)g_begin,
+                       (int)g_end, a.idx, a.redo);
   }
   return hipGetLastError();
 }

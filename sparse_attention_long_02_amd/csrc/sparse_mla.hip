@@ -557,7 +557,8 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
                        bs_v, a.sm_scale, (float*)a.out, a.lse);
     return hipGetLastError();
   }
-  const int s = sparse_mla_splits(a.B, a.n_q, a.k, a.dtype);
+  int s = sparse_mla_splits(a.B, a.n_q, a.k, a.dtype);
+  if (a.max_split > 0 && s > a.max_split) s = a.max_split;
   float* part_o = nullptr;
   float* part_lse = nullptr;
   if (s > 1) {

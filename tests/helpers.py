@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 import oracle as O
+from sparse_attention_long_02_amd import synth as S
 
 
 def dev_u8(a):
@@ -51,3 +52,24 @@ def overlap(idx_a, idx_b):
         if sb:
             worst = min(worst, i / len(sb))
     return inter / max(tot, 1), worst
+
+
+def prefill_on_gpu(cfg):
+    """Stream the generator's row blocks into device tensors (the benchmark's recipe).
+    Returns the device operands (qi, qs, ki, ks, w, q, kv) and the host key arrays."""
+    L = cfg.L
+    qi = torch.empty((L, cfg.H_I, cfg.d_I), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((L, cfg.H_I), dtype=torch.float32, device="cuda")
+    w = torch.empty((L, cfg.H_I), dtype=torch.float32, device="cuda")
+    q = torch.empty((L, cfg.H, cfg.d_qk), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, L, 8192):
+        rows = np.arange(r0, min(L, r0 + 8192))
+        a, b, c, d = S.query_rows(cfg, rows)
+        sl = slice(r0, r0 + len(rows))
+        qi[sl].copy_(torch.from_numpy(a))
+        qs[sl].copy_(torch.from_numpy(b))
+        w[sl].copy_(torch.from_numpy(c))
+        q[sl].copy_(torch.from_numpy(d.view(np.int16)).view(torch.bfloat16))
+    ki, ks, kv, _ = S.key_rows(cfg)
+    return (qi, qs, torch.from_numpy(ki).cuda(), torch.from_numpy(ks).cuda(), w, q,
+            torch.from_numpy(kv.view(np.int16)).cuda().view(torch.bfloat16)), (ki, ks, kv)

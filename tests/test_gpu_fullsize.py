@@ -14,7 +14,7 @@ import torch
 import oracle as O
 from sparse_attention_long_02_amd import dsa
 from sparse_attention_long_02_amd import synth as S
-from tests.helpers import out_to_f64, overlap
+from tests.helpers import out_to_f64, overlap, prefill_on_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -25,26 +25,6 @@ OVERLAP_MIN = 0.995
 def _say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def _prefill_on_gpu(cfg):
-    """Stream the generator's row blocks into device tensors (the benchmark's recipe)."""
-    L = cfg.L
-    qi = torch.empty((L, cfg.H_I, cfg.d_I), dtype=torch.uint8, device="cuda")
-    qs = torch.empty((L, cfg.H_I), dtype=torch.float32, device="cuda")
-    w = torch.empty((L, cfg.H_I), dtype=torch.float32, device="cuda")
-    q = torch.empty((L, cfg.H, cfg.d_qk), dtype=torch.bfloat16, device="cuda")
-    for r0 in range(0, L, 8192):
-        rows = np.arange(r0, min(L, r0 + 8192))
-        a, b, c, d = S.query_rows(cfg, rows)
-        sl = slice(r0, r0 + len(rows))
-        qi[sl].copy_(torch.from_numpy(a))
-        qs[sl].copy_(torch.from_numpy(b))
-        w[sl].copy_(torch.from_numpy(c))
-        q[sl].copy_(torch.from_numpy(d.view(np.int16)).view(torch.bfloat16))
-    ki, ks, kv, _ = S.key_rows(cfg)
-    return (qi, qs, torch.from_numpy(ki).cuda(), torch.from_numpy(ks).cuda(), w, q,
-            torch.from_numpy(kv.view(np.int16)).cuda().view(torch.bfloat16)), (ki, ks, kv)
 
 
 def _indexer_ok(g, qhat, w, khat, t, d_I):
@@ -64,7 +44,7 @@ def test_prefill_full_size_sampled_rows(name):
     cfg = S.CONFIGS[name]
     L, k = cfg.L, cfg.k
     _say(f"[full-size prefill] {name} L={L}: generating inputs")
-    (qi, qs, ki_d, ks_d, w, q, kv_d), (ki, ks, kv) = _prefill_on_gpu(cfg)
+    (qi, qs, ki_d, ks_d, w, q, kv_d), (ki, ks, kv) = prefill_on_gpu(cfg)
     _say("  forward_prefill")
     idx, out, lse = dsa.forward_prefill(qi, qs, ki_d, ks_d, w, q, kv_d, k, cfg.sm_scale, cfg.d_v)
     torch.cuda.synchronize()

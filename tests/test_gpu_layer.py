@@ -9,7 +9,7 @@ import torch
 import oracle as O
 from sparse_attention_long_02_amd import dsa
 from sparse_attention_long_02_amd import synth as S
-from tests.helpers import dev_bf16, dev_f32, dev_u8, indexer_inputs_dev, out_to_f64, overlap
+from tests.helpers import dev_bf16, dev_f32, dev_u8, indexer_inputs_dev, out_to_f64, overlap, prefill_on_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -286,3 +286,49 @@ def test_prefill_short_sequences_vs_oracle(L):
     _say(f"  attention max-abs {err:.3e}")
     assert err <= ATOL_BF16
     assert np.allclose(lse.cpu().numpy(), ref["lse"], atol=1e-3, rtol=1e-4)
+
+
+@pytest.fixture(scope="module")
+def three_chunks():
+    """L = 33002: the prefill selection runs in chunks of 16384, 16384 and 234 rows, and the
+    chunk boundaries fall inside 4-row groups of the exact re-selection (counted from the
+    last row)."""
+    cfg = S.CONFIGS["prefill_32k"].with_(L=33002)
+    ops, _ = prefill_on_gpu(cfg)
+    return cfg, ops
+
+
+@pytest.mark.parametrize("case", ["plain", "sample_low"])
+def test_prefill_chunk_pipeline_matches_one_pass(three_chunks, case):
+    """dsa_forward_prefill over more than one selection chunk runs each chunk's attention on
+    a second stream beside the next chunk's selection, and selects each chunk's undecided
+    rows before that chunk's attention starts.  Its indices, output and lse must equal, bit
+    for bit, those of dsa_select_prefill (one re-selection pass after the last chunk)
+    followed by one dsa_sparse_mla launch, and the selection must be the top-k of
+    dsa_indexer's scores on every row.  "sample_low" zeroes every 32nd key, the sampled
+    ones, so that the thresholds fall below more keys than a candidate list holds and every
+    row past 6144 keys goes to the exact re-selection, in all three chunks."""
+    cfg, (qi, qs, ki, ks, w, q, kv) = three_chunks
+    _say(f"[prefill chunk pipeline] L={cfg.L} {case}")
+    if case == "sample_low":
+        ki = ki.clone()
+        ki[::32] = 0
+    k = cfg.k
+    idx, out, lse = dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, k, cfg.sm_scale, cfg.d_v)
+    idx1, out1, lse1 = dsa.forward_prefill(qi, qs, ki, ks, w, q, kv, k, cfg.sm_scale, cfg.d_v)
+    sel = dsa.select_prefill(qi, qs, ki, ks, w, k)
+    out2, lse2 = dsa.sparse_mla(q, kv, sel, cfg.sm_scale, cfg.d_v)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, sel), f"rows differ: {(idx != sel).any(dim=1).nonzero().flatten()[:5].tolist()}"
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    # a second call (the same streams and events again) gives the same bits
+    assert torch.equal(idx1, idx) and torch.equal(out1.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse1, lse)
+    del out1, lse1, out2, lse2
+    scores = dsa.indexer(qi, qs, ki, ks, w)
+    ref = dsa.topk(scores, k)
+    torch.cuda.synchronize()
+    diff = (idx != ref).any(dim=1).nonzero().flatten().tolist()
+    assert not diff, f"{len(diff)} rows differ from topk(indexer), first {diff[:5]}"
+    del scores, ref
