@@ -227,6 +227,12 @@ int dsa_select_prefill(const void* q_idx, const float* q_scale, const void* k_id
  *   idx [L, k] int32 (output: the selection), out [L, H, d_v], lse [L, H] or NULL
  * idx_dtype: DSA_FP8_E4M3 or DSA_F32; attn_dtype: DSA_BF16 or DSA_F32.
  * Workspace: dsa_workspace_size(DSA_OP_PREFILL, 1, L, L, H, d_v, k, attn_dtype).
+ * Streams: with the FP8 selection in more than one chunk of rows (L > 16384), the attention
+ * of each finished chunk runs on a second stream of the library (default priority, one per
+ * host thread and device, created on the first such call and kept until the thread ends),
+ * fenced by events; `stream` waits for it before the call's work ends, so every output is
+ * complete when the work enqueued on `stream` is.  Results are bit-identical to selecting
+ * first and attending after.
  */
 int dsa_forward_prefill(const void* q_idx, const float* q_scale, const void* k_idx,
                         const float* k_scale, const float* w, const void* q, int64_t ld_q,
