@@ -62,7 +62,11 @@ def test_noalloc_decode_matches_workspace_decode():
 
 def test_noalloc_decode_refuses_oversized_scratch():
     L = dsa.lib()
-    B, n = 64, 262144
+    B, n = 128, 262144
+    # the pointers below are placeholders that must never reach a kernel: the call has to be
+    # refused on the host, so the shape's scratch must exceed the 128 MiB array
+    need = dsa.workspace_size(dsa.DSA_OP_DECODE, B, 1, n, 128, 512, 2048, dsa.DSA_BF16)
+    assert need > (128 << 20), f"shape needs only {need} bytes: pick a larger one"
     st = L.dsa_forward_decode_noalloc(B, 1 << 20, n, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, n, 1 << 20, 576,
                                       1 << 20, 576, n * 576, None, 0, 0, 64, 128, 128, 576, 512, 2048,
                                       ctypes.c_float(0.04), dsa.DSA_FP8_E4M3, dsa.DSA_BF16, 1 << 20, 1 << 20, None,
