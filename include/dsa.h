@@ -229,7 +229,7 @@ int dsa_select_prefill(const void* q_idx, const float* q_scale, const void* k_id
  * Workspace: dsa_workspace_size(DSA_OP_PREFILL, 1, L, L, H, d_v, k, attn_dtype).
  * Streams: with the FP8 selection in more than one chunk of rows (L > 16384), the attention
  * of each finished chunk runs on a second stream of the library (default priority, one per
- * host thread and device, created on the first such call and kept until the thread ends),
+ * host thread and device, created on the first such call and never released),
  * fenced by events; `stream` waits for it before the call's work ends, so every output is
  * complete when the work enqueued on `stream` is.  Results are bit-identical to selecting
  * first and attending after.

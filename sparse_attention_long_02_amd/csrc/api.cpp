@@ -352,7 +352,7 @@ int dsa_sparse_mla(const void* q, int64_t ld_q, const void* kv, int64_t ld_kv, c
 // A second stream (default priority) per host thread and device.  The prefill runs the
 // attention of each finished selection chunk on it, beside the selection of the next chunk,
 // and the caller's stream waits for it before the call's work ends.  Created on first use and
-// kept for the life of the thread.
+// never released (like the handles of a runtime, they go with the process).
 struct AuxStream {
   hipStream_t s = nullptr;
   hipEvent_t ev = nullptr;
