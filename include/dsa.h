@@ -391,7 +391,7 @@ int dsa_indexer_kl_dense(const void* q_idx, const float* q_scale, const void* k_
  *
  * Its scratch is a fixed 128 MiB array of the library in device memory, held on every GPU
  * the library runs on until the process ends (the 64 x 131072-token decode workload needs
- * about 101 MB).  A shape whose dsa_workspace_size(DSA_OP_DECODE, ...) exceeds 128 MiB
+ * about 110 MB).  A shape whose dsa_workspace_size(DSA_OP_DECODE, ...) exceeds 128 MiB
  * returns DSA_ERR_UNSUPPORTED before anything is enqueued.  Nothing is allocated, by the
  * library or by any routine it calls.  All calls on one GPU share that GPU's array: calls
  * that overlap on one GPU (concurrent streams, several threads) race and must be ordered
