@@ -69,6 +69,9 @@ typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
 
 #define DSA_ABI_VERSION 2
 
+/* Tokens per page of the paged caches (dsa_forward_decode_paged). */
+#define DSA_PAGE_ROWS 64
+
 enum dsa_status {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = -1, /* null pointer, bad dimension, misaligned pointer */
@@ -270,6 +273,37 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
                        int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k,
                        float sm_scale, int32_t idx_dtype, int32_t attn_dtype, int32_t* idx,
                        void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_forward_decode_paged -- dsa_forward_decode over paged caches: the same selection and
+ * attention (and bit-identical results) with the rows of every cache stored in fixed pages
+ * of a shared pool instead of one contiguous range per sequence, the layout of serving
+ * systems that grow sequences page by page (the serving form of the decode stage: yunpan.plus
+ * article, section 1.1 DSA).
+ * A page holds DSA_PAGE_ROWS consecutive tokens of one sequence.  Token s of sequence b lives
+ * in pool page p = block_table[b * bt_stride + s / DSA_PAGE_ROWS], row
+ * p * DSA_PAGE_ROWS + s % DSA_PAGE_ROWS of each pool:
+ *   k_pool         [n_pages * DSA_PAGE_ROWS, d_I] FP8 codes (16-byte aligned)
+ *   k_pool_scale   [n_pages * DSA_PAGE_ROWS] fp32
+ *   kv_pool        [n_pages * DSA_PAGE_ROWS] rows of d_qk bf16 values, ld_kv apart; V = the
+ *                  first d_v values of each row
+ *   block_table    device int32, bt_stride >= ceil(n_k_max / DSA_PAGE_ROWS) entries per
+ *                  sequence.  Entries of pages past a sequence's ctx_len[b] tokens may be read
+ *                  (by the tails of key tiles) but their rows are never used, and entries
+ *                  outside [0, n_pages) are clamped into the pool, so no table makes a kernel
+ *                  read outside the pools (a wrong one gives wrong results).
+ * q_idx, q_scale, w, q, ctx_len, idx, out, lse as dsa_forward_decode.  FP8 indexer and bf16
+ * attention only (DSA_ERR_UNSUPPORTED otherwise).
+ * Workspace: dsa_workspace_size(DSA_OP_DECODE, B, 1, n_k_max, H, d_v, k, attn_dtype).
+ */
+int dsa_forward_decode_paged(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx,
+                             const float* q_scale, const float* w, const void* k_pool,
+                             const float* k_pool_scale, const void* q, int64_t ld_q,
+                             const void* kv_pool, int64_t ld_kv, const int32_t* block_table,
+                             int64_t bt_stride, int64_t n_pages, int32_t H_I, int32_t d_I, int32_t H,
+                             int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype,
+                             int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                             size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * dsa_forward_chunk -- the whole layer for a chunk of n_q new tokens in each of B

@@ -490,6 +490,79 @@ static int check_cache_strides(int64_t n_k_max, int64_t kc_seq_stride, const voi
   return DSA_OK;
 }
 
+// The decode layer once its arguments are checked: selection (filtered for long FP8 caches),
+// then the split attention.  With a page table, k_cache / k_cache_scale / kv_cache are page
+// pools and the sequence strides are unused.
+static int decode_run(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx, const float* q_scale,
+                      const float* w, const void* k_cache, const float* k_cache_scale, int64_t kc_seq_stride,
+                      const void* q, int64_t ld_q, const void* kv_cache, int64_t ld_kv, int64_t kv_seq_stride,
+                      const void* v_cache, int64_t ld_v, int64_t v_seq_stride, int32_t H_I, int32_t d_I, int32_t H,
+                      int32_t d_qk, int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype, int32_t attn_dtype,
+                      int32_t* idx, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s,
+                      const dsa::PageTable& pt, const char* name) {
+  DecWs dw;
+  const size_t s_bytes = dec_sel_bytes(B, n_k_max, idx_dtype, &dw, ws);
+  const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, attn_dtype);
+  if (!ws || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "%s needs %zu workspace bytes (got %zu)", name, need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  int st = DSA_OK;
+  const uint8_t* q8 = (const uint8_t*)q_idx;
+  const uint8_t* k8 = (const uint8_t*)k_cache;
+  // the query of sequence b is its row 0, at position ctx_len[b] - 1
+  if (dec_filtered(n_k_max, idx_dtype)) {
+    const int64_t ld_s = dsa::sel_sample_ld(n_k_max);
+    // 1. scores of every SEL_SAMPLE_STRIDE-th key; 2. each sequence's threshold (and its
+    // candidate count zeroed); 3. the filtering indexer appends the keys above it; 4. the
+    // top-k of each candidate list; 5. sequences whose list did not decide them: full score
+    // rows and the exact row selection (both launches skip every other sequence)
+    dsa::SplitIdxArgs sa{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, dw.samp, ld_s,
+                         dsa::SEL_SAMPLE_STRIDE, nullptr, nullptr, nullptr, nullptr, kc_seq_stride};
+    sa.pages = pt;
+    st = hip_status(dsa::launch_idx_split(sa, s), "decode key-sample indexer launch");
+    if (st) return st;
+    dsa::SelThresholdArgs ta{dw.samp, ld_s, 1, B, 1, n_k_max, ctx_len, -1, k, dw.thr};
+    st = hip_status(dsa::launch_sel_threshold(ta, s), "decode threshold launch");
+    if (st) return st;
+    dsa::SplitIdxArgs fa{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, nullptr, 0, 1,
+                         dw.thr, dw.cand, dw.cnt, nullptr, kc_seq_stride};
+    fa.pages = pt;
+    st = hip_status(dsa::launch_idx_split(fa, s), "decode filtering indexer launch");
+    if (st) return st;
+    dsa::DecCandArgs ca{dw.cand, dw.cnt, dsa::dec_split_segments(n_k_max), B, 1, n_k_max, ctx_len, -1, k, idx,
+                        dw.redo};
+    st = hip_status(dsa::launch_dec_cand_topk(ca, s), "decode candidate top-k launch");
+    if (st) return st;
+    dsa::SplitIdxArgs ra{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, dw.scores, n_k_max,
+                         1, nullptr, nullptr, nullptr, dw.redo, kc_seq_stride};
+    ra.pages = pt;
+    st = hip_status(dsa::launch_idx_split(ra, s), "decode indexer launch (undecided sequences)");
+    if (st) return st;
+    dsa::TopkArgs tk{dw.scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx, 0, 0, 0, dw.redo};
+    st = hip_status(dsa::launch_topk(tk, s), "decode top-k launch (undecided sequences)");
+    if (st) return st;
+  } else {
+    if (pt.table) {  // paged caches are FP8: the split indexer reads them through the table
+      dsa::SplitIdxArgs ia{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, dw.scores,
+                           n_k_max, 1, nullptr, nullptr, nullptr, nullptr, 0};
+      ia.pages = pt;
+      st = hip_status(dsa::launch_idx_split(ia, s), "decode indexer launch");
+    } else {
+      dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, H_I, d_I,
+                          idx_dtype, 0, 1, dw.scores, n_k_max, kc_seq_stride};
+      st = hip_status(dsa::launch_indexer(ia, s), "decode indexer launch");
+    }
+    if (st) return st;
+    dsa::TopkArgs ta{dw.scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx};
+    st = hip_status(dsa::launch_topk(ta, s), "decode top-k launch");
+    if (st) return st;
+  }
+  dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, 1, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
+                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v_cache ? ld_v : 0,
+                 kv_seq_stride, v_cache ? v_seq_stride : 0};
+  a.pages = pt;
+  return hip_status(dsa::launch_sparse_mla(a, s), "decode sparse attention launch");
+}
+
 int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx, const float* q_scale,
                        const float* w, const void* k_cache, const float* k_cache_scale, int64_t kc_seq_stride,
                        const void* q, int64_t ld_q, const void* kv_cache, int64_t ld_kv, int64_t kv_seq_stride,
@@ -510,57 +583,45 @@ int dsa_forward_decode(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const
   if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv_cache) && aligned16(out), "bf16 operands must be 16-byte aligned");
   SUPPORT(idx_dtype == attn_dtype || (idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16),
           "decode pairs an FP8 indexer with bf16 attention, or fp32 with fp32");
-  DecWs dw;
-  const size_t s_bytes = dec_sel_bytes(B, n_k_max, idx_dtype, &dw, ws);
-  const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, attn_dtype);
-  if (!ws || ws_bytes < need)
-    return fail(DSA_ERR_WORKSPACE, "dsa_forward_decode needs %zu workspace bytes (got %zu)", need, ws_bytes);
-  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  // the query of sequence b is its row 0, at position ctx_len[b] - 1
-  if (dec_filtered(n_k_max, idx_dtype)) {
-    const uint8_t* q8 = (const uint8_t*)q_idx;
-    const uint8_t* k8 = (const uint8_t*)k_cache;
-    const int64_t ld_s = dsa::sel_sample_ld(n_k_max);
-    // 1. scores of every SEL_SAMPLE_STRIDE-th key; 2. each sequence's threshold (and its
-    // candidate count zeroed); 3. the filtering indexer appends the keys above it; 4. the
-    // top-k of each candidate list; 5. sequences whose list did not decide them: full score
-    // rows and the exact row selection (both launches skip every other sequence)
-    dsa::SplitIdxArgs sa{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, dw.samp, ld_s,
-                         dsa::SEL_SAMPLE_STRIDE, nullptr, nullptr, nullptr, nullptr, kc_seq_stride};
-    st = hip_status(dsa::launch_idx_split(sa, s), "decode key-sample indexer launch");
-    if (st) return st;
-    dsa::SelThresholdArgs ta{dw.samp, ld_s, 1, B, 1, n_k_max, ctx_len, -1, k, dw.thr};
-    st = hip_status(dsa::launch_sel_threshold(ta, s), "decode threshold launch");
-    if (st) return st;
-    dsa::SplitIdxArgs fa{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, nullptr, 0, 1,
-                         dw.thr, dw.cand, dw.cnt, nullptr, kc_seq_stride};
-    st = hip_status(dsa::launch_idx_split(fa, s), "decode filtering indexer launch");
-    if (st) return st;
-    dsa::DecCandArgs ca{dw.cand, dw.cnt, dsa::dec_split_segments(n_k_max), B, 1, n_k_max, ctx_len, -1, k, idx,
-                        dw.redo};
-    st = hip_status(dsa::launch_dec_cand_topk(ca, s), "decode candidate top-k launch");
-    if (st) return st;
-    dsa::SplitIdxArgs ra{q8, q_scale, k8, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, 0, 1, dw.scores, n_k_max,
-                         1, nullptr, nullptr, nullptr, dw.redo, kc_seq_stride};
-    st = hip_status(dsa::launch_idx_split(ra, s), "decode indexer launch (undecided sequences)");
-    if (st) return st;
-    dsa::TopkArgs tk{dw.scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx, 0, 0, 0, dw.redo};
-    st = hip_status(dsa::launch_topk(tk, s), "decode top-k launch (undecided sequences)");
-    if (st) return st;
-  } else {
-    dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, 1, n_k_max, ctx_len, -1, H_I, d_I,
-                        idx_dtype, 0, 1, dw.scores, n_k_max, kc_seq_stride};
-    st = hip_status(dsa::launch_indexer(ia, s), "decode indexer launch");
-    if (st) return st;
-    dsa::TopkArgs ta{dw.scores, n_k_max, B, 1, n_k_max, ctx_len, -1, 0, k, idx};
-    st = hip_status(dsa::launch_topk(ta, s), "decode top-k launch");
-    if (st) return st;
-  }
-  dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, 1, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
-                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v_cache ? ld_v : 0,
-                 kv_seq_stride, v_cache ? v_seq_stride : 0};
-  return hip_status(dsa::launch_sparse_mla(a, s), "decode sparse attention launch");
+  return decode_run(B, ctx_len, n_k_max, q_idx, q_scale, w, k_cache, k_cache_scale, kc_seq_stride, q, ld_q, kv_cache,
+                    ld_kv, kv_seq_stride, v_cache, ld_v, v_seq_stride, H_I, d_I, H, d_qk, d_v, k, sm_scale, idx_dtype,
+                    attn_dtype, idx, out, lse, ws, ws_bytes, (hipStream_t)stream, dsa::PageTable{},
+                    "dsa_forward_decode");
+}
+
+int dsa_forward_decode_paged(int64_t B, const int32_t* ctx_len, int64_t n_k_max, const void* q_idx,
+                             const float* q_scale, const float* w, const void* k_pool, const float* k_pool_scale,
+                             const void* q, int64_t ld_q, const void* kv_pool, int64_t ld_kv,
+                             const int32_t* block_table, int64_t bt_stride, int64_t n_pages, int32_t H_I,
+                             int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
+                             int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                             size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(ctx_len && q_idx && q_scale && w && k_pool && k_pool_scale && q && kv_pool && block_table && idx && out,
+          "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_k_max > 0, "B in [1, 65535] and n_k_max > 0 required");
+  SUPPORT(idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16,
+          "paged decode needs an FP8 indexer and bf16 attention");
+  int st = check_indexer_shape(H_I, d_I, idx_dtype);
+  if (st) return st;
+  st = check_attn_shape(H, d_qk, d_v, k, attn_dtype, false);
+  if (st) return st;
+  CHECK(check_ld("ld_q", ld_q, d_qk, attn_dtype));
+  CHECK(check_ld("ld_kv", ld_kv, d_qk, attn_dtype));
+  SUPPORT(n_k_max <= dsa::TOPK_MAX_N, "decode supports n_k_max <= %lld", (long long)dsa::TOPK_MAX_N);
+  const int64_t pages_per_seq = (n_k_max + dsa::PAGE_ROWS - 1) / dsa::PAGE_ROWS;
+  REQUIRE(bt_stride >= pages_per_seq, "bt_stride (%lld) must cover n_k_max (%lld pages of %d rows)",
+          (long long)bt_stride, (long long)pages_per_seq, dsa::PAGE_ROWS);
+  REQUIRE(n_pages > 0 && n_pages <= 2147483647LL / dsa::PAGE_ROWS, "n_pages must be in [1, 2^31 / %d)",
+          dsa::PAGE_ROWS);
+  REQUIRE(aligned16(q_idx) && aligned16(k_pool), "FP8 operands must be 16-byte aligned");
+  REQUIRE(aligned16(q) && aligned16(kv_pool) && aligned16(out), "bf16 operands must be 16-byte aligned");
+  dsa::PageTable pt;
+  pt.table = block_table;
+  pt.ld = bt_stride;
+  pt.n_pages = n_pages;
+  return decode_run(B, ctx_len, n_k_max, q_idx, q_scale, w, k_pool, k_pool_scale, 0, q, ld_q, kv_pool, ld_kv, 0,
+                    nullptr, 0, 0, H_I, d_I, H, d_qk, d_v, k, sm_scale, idx_dtype, attn_dtype, idx, out, lse, ws,
+                    ws_bytes, (hipStream_t)stream, pt, "dsa_forward_decode_paged");
 }
 
 int dsa_fp8_quantize_rows(const void* x, int32_t x_dtype, int64_t n_rows, int64_t width, int64_t ld_x,

@@ -44,6 +44,23 @@ constexpr int DEC_SEG = 64;      // candidate slots per wave segment
 inline int64_t dec_split_segments(int64_t n_k) {
   return 4 * ((n_k + SPLIT_TILES * 64 - 1) / (SPLIT_TILES * 64));
 }
+// Paged caches: the cached rows of sequence b, token j, live at pool row
+// table[b * ld + j / PAGE_ROWS] * PAGE_ROWS + j % PAGE_ROWS (page ids outside
+// [0, n_pages) are clamped into it, so a bad table cannot make a kernel read outside the
+// pool).  A null table means the contiguous per-sequence layout.
+constexpr int PAGE_ROWS = DSA_PAGE_ROWS;
+static_assert(PAGE_ROWS == 64, "paged_row() takes the page by a shift of 6");
+struct PageTable {
+  const int32_t* table = nullptr;
+  int64_t ld = 0;       // entries between the tables of consecutive sequences
+  int64_t n_pages = 0;  // pages in the pool
+};
+__device__ __forceinline__ int64_t paged_row(const PageTable& pt, int b, int64_t j) {
+  int64_t p = pt.table[(int64_t)b * pt.ld + (j >> 6)];
+  p = p < 0 ? 0 : p >= pt.n_pages ? pt.n_pages - 1 : p;
+  return p * PAGE_ROWS + (j & (PAGE_ROWS - 1));
+}
+
 struct SplitIdxArgs {
   const uint8_t* q8;
   const float* qs;
@@ -61,6 +78,7 @@ struct SplitIdxArgs {
   uint32_t* cnt;
   const uint8_t* redo;
   int64_t k_bstride;
+  PageTable pages = {};  // non-null table: k8 / ks are page pools (key_stride 1 or any)
 };
 hipError_t launch_idx_split(const SplitIdxArgs& a, hipStream_t st);
 
@@ -99,6 +117,8 @@ struct MlaArgs {
   // at most this many key splits per query (0: as sparse_mla_splits chooses; 1: never split,
   // so no workspace is used)
   int32_t max_split = 0;
+  // non-null table: kv is a page pool (bf16 path only; bs_kv unused)
+  PageTable pages = {};
 };
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 // workspace of the bf16 kernel when it splits each query's keys over several blocks

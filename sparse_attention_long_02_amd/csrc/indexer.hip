@@ -67,6 +67,32 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
     for (int64_t key = (int64_t)ntiles * KEY_TILE + lane; key < n_k; key += KEY_TILE) srow[key] = -INFINITY;
 }
 
+// Key fragment f of the tile at launch key key0 and the scale of launch key `key` (clamped to
+// n_keys - 1; launch key j is cache token j * stride of sequence b), from the contiguous
+// per-sequence cache (kbs rows apart) or, PAGED, through the page table.
+template <bool PAGED>
+__device__ __forceinline__ v8i split_key_fragment(const uint8_t* __restrict__ k8, const PageTable& pt, int b,
+                                                  int64_t kbs, int64_t key0, int f, int64_t n_keys, int stride) {
+  if constexpr (!PAGED) {
+    return global_key_fragment(k8 + (int64_t)b * kbs * IDX_DIM, key0, f, n_keys, stride);
+  } else {
+    const int l = lane_id();
+    int64_t key = key0 + 16 * f + (l & 15);
+    key = key < n_keys ? key : n_keys - 1;
+    const v4i* p = reinterpret_cast<const v4i*>(k8 + paged_row(pt, b, key * stride) * IDX_DIM + 32 * (l >> 4));
+    const v4i lo = p[0];
+    const v4i hi = p[1];
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+template <bool PAGED>
+__device__ __forceinline__ float split_key_scale(const float* __restrict__ ks, const PageTable& pt, int b,
+                                                 int64_t kbs, int64_t key, int64_t n_keys, int stride) {
+  key = key < n_keys ? key : n_keys - 1;
+  if constexpr (!PAGED) return ks[(int64_t)b * kbs + key * stride];
+  else return ks[paged_row(pt, b, key * stride)];
+}
+
 // grid: x = key splits of SPLIT_TILES tiles, y = row, z = sequence.
 // Store mode: the row's scores of keys 0, S, 2S, ... (S = key_stride) go to columns 0, 1,
 // 2, ... of its score row, -inf for keys past its position.  Filter mode (FILTER): nothing
@@ -77,13 +103,13 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
 // cnt[(b * n_rows + i) * n_segs + seg].  No atomics: a wave's slots come from a ballot and
 // its running count.  With redo non-null only rows whose redo byte is set run.
 
-template <bool FILTER>
+template <bool FILTER, bool PAGED>
 __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int64_t n_rows,
     float* __restrict__ scores, int64_t ld, int key_stride, const float* __restrict__ thr,
-    uint2* __restrict__ cand, uint32_t* __restrict__ cnt, const uint8_t* __restrict__ redo) {
+    uint2* __restrict__ cand, uint32_t* __restrict__ cnt, const uint8_t* __restrict__ redo, PageTable pt) {
   const int b = blockIdx.z;
   const int64_t i = blockIdx.y;
   const int64_t rid = (int64_t)b * n_rows + i;
@@ -92,8 +118,6 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
   const int64_t pos = (q_pos ? (int64_t)q_pos[b] : 0) + pos_offset + row_begin + i;
   const int64_t row = row_begin + i;
   const int64_t qrow = (int64_t)b * n_q + row;
-  const uint8_t* kb8 = k8 + (int64_t)b * kbs * IDX_DIM;
-  const float* ksb = ks + (int64_t)b * kbs;
   float* srow = scores + rid * ld;
   const int64_t t0 = (int64_t)blockIdx.x * SPLIT_TILES;
   // launch keys: key j is cache row j * key_stride; the row sees those at or below pos
@@ -133,8 +157,8 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
   {
     const int64_t key0 = t * KEY_TILE, key = key0 + lane;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bf[f] = global_key_fragment(kb8, key0, f, n_keys, key_stride);
-    ksc = ksb[(key < n_keys ? key : n_keys - 1) * key_stride];
+    for (int f = 0; f < 4; ++f) bf[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride);
+    ksc = split_key_scale<PAGED>(ks, pt, b, kbs, key, n_keys, key_stride);
   }
   for (; t < t_vis; t += 4) {
     const int64_t tn = t + 4;
@@ -143,8 +167,8 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     if (tn < t_vis) {
       const int64_t key0 = tn * KEY_TILE, key = key0 + lane;
 #pragma unroll
-      for (int f = 0; f < 4; ++f) bn[f] = global_key_fragment(kb8, key0, f, n_keys, key_stride);
-      kn = ksb[(key < n_keys ? key : n_keys - 1) * key_stride];
+      for (int f = 0; f < 4; ++f) bn[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride);
+      kn = split_key_scale<PAGED>(ks, pt, b, kbs, key, n_keys, key_stride);
     }
     const int64_t key = t * KEY_TILE + lane;
     const float sc = score_tile64(Q, bf, ksc);
@@ -169,14 +193,12 @@ hipError_t launch_idx_split(const SplitIdxArgs& a, hipStream_t st) {
   dim3 grid((unsigned)((n_keys + SPLIT_TILES * KEY_TILE - 1) / (SPLIT_TILES * KEY_TILE)), (unsigned)a.n_rows,
             (unsigned)a.B);
   const int64_t kbs = a.k_bstride ? a.k_bstride : a.n_k;
-  if (a.cand)
-    hipLaunchKernelGGL(idx_scores_fp8_split<true>, grid, dim3(256), 0, st, a.q8, a.qs, a.k8, a.ks, a.w, a.n_q, a.n_k,
-                       kbs, a.q_pos, a.pos_offset, a.row_begin, a.n_rows, nullptr, (int64_t)0, 1, a.thr, a.cand,
-                       a.cnt, a.redo);
-  else
-    hipLaunchKernelGGL(idx_scores_fp8_split<false>, grid, dim3(256), 0, st, a.q8, a.qs, a.k8, a.ks, a.w, a.n_q,
-                       a.n_k, kbs, a.q_pos, a.pos_offset, a.row_begin, a.n_rows, a.scores, a.ld, a.key_stride,
-                       nullptr, nullptr, nullptr, a.redo);
+  const bool paged = a.pages.table != nullptr;
+  auto kern = a.cand ? (paged ? idx_scores_fp8_split<true, true> : idx_scores_fp8_split<true, false>)
+                     : (paged ? idx_scores_fp8_split<false, true> : idx_scores_fp8_split<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.q8, a.qs, a.k8, a.ks, a.w, a.n_q, a.n_k, kbs, a.q_pos,
+                     a.pos_offset, a.row_begin, a.n_rows, a.cand ? nullptr : a.scores, a.cand ? (int64_t)0 : a.ld,
+                     a.cand ? 1 : (int)a.key_stride, a.thr, a.cand, a.cnt, a.redo, a.pages);
   return hipGetLastError();
 }
 

@@ -246,7 +246,8 @@ __device__ __forceinline__ v16f mla_logits(const v8bf* Qt, const uint8_t* buf) {
 __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int64_t n_q, int64_t n_k, int64_t ld_q, int64_t ld_kv, int64_t bs_kv, int k, float scale_log2, int n_split,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
+    PageTable pt) {
   __shared__ __align__(16) uint8_t buf0[CHUNK_BYTES];
   __shared__ __align__(16) uint8_t buf1[CHUNK_BYTES];
   __shared__ __align__(16) uint8_t buf2[CHUNK_BYTES];
@@ -260,7 +261,8 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   const int split = blockIdx.x % n_split;
   const int64_t qrow = (int64_t)b * n_q + qi;
   const int32_t* irow = idx + qrow * k;
-  const uint16_t* kvb = kv + (int64_t)b * bs_kv;
+  // paged caches: kv is the pool, and the ids become pool rows as they are staged below
+  const uint16_t* kvb = pt.table ? kv : kv + (int64_t)b * bs_kv;
 
   // B operands of S^T: head 32w + l%32, values 16ds + 8g .. +7
   v8bf Qt[D_STEPS];
@@ -273,10 +275,15 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     for (int ds = 0; ds < D_STEPS; ++ds) asm volatile("" : "+v"(Qt[ds]));
   }
 
-  // the row's selected ids -> LDS; every wave then finds the last valid one, and the
-  // chunks run up to the one holding it
-  const uint32_t nk = (uint32_t)min(n_k, (int64_t)INT32_MAX);
-  for (int j = tid; j < k; j += MLA_WAVES * 64) ids[j] = irow[j];
+  // the row's selected ids -> LDS (pool rows for paged caches, invalid ids kept invalid);
+  // every wave then finds the last valid one, and the chunks run up to the one holding it
+  const uint32_t nk_seq = (uint32_t)min(n_k, (int64_t)INT32_MAX);
+  const uint32_t nk = pt.table ? (uint32_t)min(pt.n_pages * PAGE_ROWS, (int64_t)INT32_MAX) : nk_seq;
+  for (int j = tid; j < k; j += MLA_WAVES * 64) {
+    int32_t id = irow[j];
+    if (pt.table) id = (uint32_t)id < nk_seq ? (int32_t)paged_row(pt, b, id) : -1;
+    ids[j] = id;
+  }
   __syncthreads();
   int last = -1;
   for (int j = l; j < k; j += 64)
@@ -568,7 +575,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(a.n_q * s), (unsigned)a.B);
   hipLaunchKernelGGL(sparse_mla_bf16_kernel, grid, dim3(MLA_WAVES * 64), 0, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.kv, a.idx, a.n_q, a.n_k, ld_q, ld_kv, bs_kv, a.k, a.sm_scale * LOG2E, s,
-                     (uint16_t*)a.out, a.lse, part_o, part_lse);
+                     (uint16_t*)a.out, a.lse, part_o, part_lse, a.pages);
   if (s > 1)
     hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(a.B * a.n_q * a.H)), dim3(128), 0, st, part_o,
                        part_lse, s, a.H, a.d_v, (uint16_t*)a.out, a.lse);

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_PAGE_ROWS = 64  # tokens per page of the paged caches
 (DSA_OP_INDEXER, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_PREFILL, DSA_OP_DECODE, DSA_OP_SELECT, DSA_OP_CHUNK,
  DSA_OP_MLA_BWD, DSA_OP_KL_DENSE) = range(9)
 
@@ -44,6 +45,9 @@ _SIGNATURES = {
     "dsa_forward_decode_noalloc": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
                                                   _vp, _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "dsa_forward_decode_paged": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
+                                                _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                                _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
                                          _vp, _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -290,6 +294,36 @@ def forward_decode(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cac
                                     v_p, ld_v, bs_v, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
                                     _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream()))
+    return idx, out, lse
+
+
+def forward_decode_paged(ctx_len, q_idx, q_scale, w, k_pool, k_pool_scale, q, kv_pool, block_table, n_k_max: int,
+                         k: int, sm_scale: float, d_v: int, idx=None, out=None, lse=None, ws=None):
+    """forward_decode over paged caches -> (idx [B, k], out, lse).  Pools of n_pages pages of
+    DSA_PAGE_ROWS tokens: k_pool [n_pages * DSA_PAGE_ROWS, d_I] FP8 codes, k_pool_scale
+    [n_pages * DSA_PAGE_ROWS], kv_pool [n_pages * DSA_PAGE_ROWS, d_qk] bf16 (rows may be a
+    padded view); block_table [B, >= ceil(n_k_max / DSA_PAGE_ROWS)] int32 page ids."""
+    B, H_I, d_I = q_idx.shape
+    _, H, d_qk = q.shape
+    it, at = _idx_dtype(q_idx), _attn_dtype(q)
+    dev = q.device
+    if k_pool.dim() != 2 or k_pool.stride(1) != 1 or k_pool.stride(0) != d_I or k_pool_scale.stride(-1) != 1:
+        raise ValueError("the indexer key pool is [rows, d_I] with dense rows")
+    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.dtype != torch.int32:
+        raise ValueError("block_table is [B, pages] int32 with contiguous rows")
+    n_pages = min(k_pool.shape[0], k_pool_scale.shape[0], kv_pool.shape[0]) // DSA_PAGE_ROWS
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev) if idx is None else idx
+    out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if lse is None else lse
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_DECODE, B, 1, n_k_max, H, d_v, k, at), dev)
+    q_p, ld_q = _rows(q, 2)
+    kv_p, ld_kv = _rows(kv_pool, 1)
+    _check(lib().dsa_forward_decode_paged(B, _ptr(ctx_len), n_k_max, _ptr(q_idx), _ptr(q_scale), _ptr(w),
+                                          k_pool.data_ptr(), k_pool_scale.data_ptr(), q_p, ld_q, kv_p, ld_kv,
+                                          block_table.data_ptr(), block_table.stride(0), n_pages, H_I, d_I, H,
+                                          d_qk, d_v, k, float(sm_scale), it, at, _ptr(idx), _ptr(out), _ptr(lse),
+                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
 
 
