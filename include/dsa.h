@@ -69,7 +69,7 @@ typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
 
 #define DSA_ABI_VERSION 2
 
-/* Tokens per page of the paged caches (dsa_forward_decode_paged). */
+/* Tokens per page of the paged caches (dsa_forward_decode_paged, dsa_forward_chunk_paged). */
 #define DSA_PAGE_ROWS 64
 
 enum dsa_status {
@@ -344,6 +344,26 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
                       int32_t d_v, int32_t k, float sm_scale, int32_t idx_dtype,
                       int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
                       size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_forward_chunk_paged -- dsa_forward_chunk over paged caches (chunked prefill into a
+ * paged cache): the same selection and attention, bit-identical results, with every cache
+ * row found through the block table as in dsa_forward_decode_paged (pools of n_pages pages
+ * of DSA_PAGE_ROWS tokens: k_pool codes, k_pool_scale, kv_pool rows ld_kv apart with V = the
+ * first d_v values; block_table with bt_stride >= ceil(n_k_max / DSA_PAGE_ROWS) entries per
+ * sequence, entries outside [0, n_pages) clamped into the pools).  The chunk's own rows must
+ * already be in the pools.  q_pos, q_idx, q_scale, w, q, idx, out, lse as dsa_forward_chunk.
+ * FP8 indexer and bf16 attention only.
+ * Workspace: dsa_workspace_size(DSA_OP_CHUNK, B, n_q, n_k_max, H, d_v, k, attn_dtype).
+ */
+int dsa_forward_chunk_paged(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max,
+                            const void* q_idx, const float* q_scale, const float* w,
+                            const void* k_pool, const float* k_pool_scale, const void* q,
+                            int64_t ld_q, const void* kv_pool, int64_t ld_kv,
+                            const int32_t* block_table, int64_t bt_stride, int64_t n_pages,
+                            int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k,
+                            float sm_scale, int32_t idx_dtype, int32_t attn_dtype, int32_t* idx,
+                            void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * dsa_indexer_scores_at -- lightning-indexer scores of the listed keys only (the scores the

@@ -177,9 +177,11 @@ static size_t sel_bytes(int64_t B, int64_t n_q, int64_t n_k) {
 using ChunkHook = std::function<int(int64_t r0, int64_t n)>;
 static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks, const float* w,
                       int64_t B, int64_t n_q, int64_t n_k, const int32_t* q_pos, int32_t k, int32_t* idx, void* ws,
-                      size_t ws_bytes, hipStream_t s, int64_t kbs = 0, const ChunkHook* chunk_done = nullptr) {
+                      size_t ws_bytes, hipStream_t s, int64_t kbs = 0, const ChunkHook* chunk_done = nullptr,
+                      const dsa::PageTable& pages = dsa::PageTable{}) {
   SUPPORT(n_k <= FUSED_MAX_KEYS, "FP8 selection supports up to %lld keys", (long long)FUSED_MAX_KEYS);
   dsa::PrefillTopkArgs pa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, k, idx, nullptr, kbs};
+  pa.pages = pages;
   if (!sel_filtered(n_k)) return hip_status(dsa::launch_prefill_topk(pa, s), "indexer/top-k launch");
   SelWs sw;
   const size_t need = sel_ws_bytes(B, n_q, n_k, &sw, ws);
@@ -193,12 +195,14 @@ static int select_fp8(const uint8_t* q8, const float* qs, const uint8_t* k8, con
     const int64_t rp = dsa::dense_rows_pad(n);
     dsa::DenseIdxArgs sa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, sw.samp, ld_s, dsa::SEL_SAMPLE_STRIDE,
                          nullptr, nullptr, nullptr, kbs};
+    sa.pages = pages;
     int st = hip_status(dsa::launch_idx_dense(sa, s), "key-sample indexer launch");
     if (st) return st;
     dsa::SelThresholdArgs ta{sw.samp, ld_s, rp, B, n, n_k, q_pos, r0, k, sw.thr};
     st = hip_status(dsa::launch_sel_threshold(ta, s), "threshold launch");
     if (st) return st;
     dsa::DenseIdxArgs fa{q8, qs, k8, ks, w, B, n_q, n_k, q_pos, r0, n, nullptr, 0, 1, sw.thr, sw.cand, sw.cnt, kbs};
+    fa.pages = pages;
     st = hip_status(dsa::launch_idx_dense(fa, s), "filtering indexer launch");
     if (st) return st;
     dsa::SelCandArgs ca{sw.cand, sw.cnt, rp, B, n, n_k, q_pos, r0, k, idx, n_q, r0, sw.redo};
@@ -650,6 +654,42 @@ int dsa_kcache_append(const void* k_new, int32_t dtype, int64_t B, int64_t n_new
   return hip_status(dsa::launch_fp8_quant_rows(a, (hipStream_t)stream), "key-cache append launch");
 }
 
+// The chunk layer once its arguments are checked.  With a page table (FP8 indexer, bf16
+// attention), k_cache / k_cache_scale / kv_cache are page pools and the sequence strides are
+// unused.
+static int chunk_run(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max, const void* q_idx,
+                     const float* q_scale, const float* w, const void* k_cache, const float* k_cache_scale,
+                     int64_t kc_seq_stride, const void* q, int64_t ld_q, const void* kv_cache, int64_t ld_kv,
+                     int64_t kv_seq_stride, const void* v_cache, int64_t ld_v, int64_t v_seq_stride, int32_t H_I,
+                     int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
+                     int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                     size_t ws_bytes, hipStream_t s, const dsa::PageTable& pt, const char* name) {
+  int st = DSA_OK;
+  const size_t s_bytes = chunk_scores_bytes(B, n_q, n_k_max, attn_dtype);
+  const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, attn_dtype);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "%s needs %zu workspace bytes (got %zu)", name, need, ws_bytes);
+  if (need) REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  if (idx_dtype == DSA_FP8_E4M3) {
+    st = select_fp8((const uint8_t*)q_idx, q_scale, (const uint8_t*)k_cache, k_cache_scale, w, B, n_q, n_k_max,
+                    q_pos, k, idx, ws, s_bytes, s, kc_seq_stride, nullptr, pt);
+  } else {
+    float* scores = (float*)ws;
+    dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, n_q, n_k_max, q_pos, 0, H_I, d_I,
+                        idx_dtype, 0, n_q, scores, n_k_max, kc_seq_stride};
+    st = hip_status(dsa::launch_indexer(ia, s), "chunk indexer launch");
+    if (st) return st;
+    dsa::TopkArgs ta{scores, n_k_max, B, n_q, n_k_max, q_pos, 0, 0, k, idx};
+    st = hip_status(dsa::launch_topk(ta, s), "chunk top-k launch");
+  }
+  if (st) return st;
+  dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, n_q, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
+                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v_cache ? ld_v : 0,
+                 kv_seq_stride, v_cache ? v_seq_stride : 0};
+  a.pages = pt;
+  return hip_status(dsa::launch_sparse_mla(a, s), "chunk sparse attention launch");
+}
+
 int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max, const void* q_idx,
                       const float* q_scale, const float* w, const void* k_cache, const float* k_cache_scale,
                       int64_t kc_seq_stride, const void* q, int64_t ld_q, const void* kv_cache, int64_t ld_kv,
@@ -679,29 +719,47 @@ int dsa_forward_chunk(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_
     SUPPORT(n_q <= 65535, "fp32 chunk supports n_q <= 65535");
   }
   if (attn_dtype == DSA_BF16) REQUIRE(aligned16(q) && aligned16(kv_cache) && aligned16(out), "bf16 operands must be 16-byte aligned");
-  const size_t s_bytes = chunk_scores_bytes(B, n_q, n_k_max, attn_dtype);
-  const size_t need = s_bytes + dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, attn_dtype);
-  if (need && (!ws || ws_bytes < need))
-    return fail(DSA_ERR_WORKSPACE, "dsa_forward_chunk needs %zu workspace bytes (got %zu)", need, ws_bytes);
-  if (need) REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  if (idx_dtype == DSA_FP8_E4M3) {
-    st = select_fp8((const uint8_t*)q_idx, q_scale, (const uint8_t*)k_cache, k_cache_scale, w, B, n_q, n_k_max,
-                    q_pos, k, idx, ws, s_bytes, s, kc_seq_stride);
-  } else {
-    float* scores = (float*)ws;
-    dsa::IndexerArgs ia{q_idx, q_scale, k_cache, k_cache_scale, w, B, n_q, n_k_max, q_pos, 0, H_I, d_I,
-                        idx_dtype, 0, n_q, scores, n_k_max, kc_seq_stride};
-    st = hip_status(dsa::launch_indexer(ia, s), "chunk indexer launch");
-    if (st) return st;
-    dsa::TopkArgs ta{scores, n_k_max, B, n_q, n_k_max, q_pos, 0, 0, k, idx};
-    st = hip_status(dsa::launch_topk(ta, s), "chunk top-k launch");
-  }
+  return chunk_run(B, n_q, q_pos, n_k_max, q_idx, q_scale, w, k_cache, k_cache_scale, kc_seq_stride, q, ld_q,
+                   kv_cache, ld_kv, kv_seq_stride, v_cache, ld_v, v_seq_stride, H_I, d_I, H, d_qk, d_v, k, sm_scale,
+                   idx_dtype, attn_dtype, idx, out, lse, ws, ws_bytes, (hipStream_t)stream, dsa::PageTable{},
+                   "dsa_forward_chunk");
+}
+
+int dsa_forward_chunk_paged(int64_t B, int64_t n_q, const int32_t* q_pos, int64_t n_k_max, const void* q_idx,
+                            const float* q_scale, const float* w, const void* k_pool, const float* k_pool_scale,
+                            const void* q, int64_t ld_q, const void* kv_pool, int64_t ld_kv,
+                            const int32_t* block_table, int64_t bt_stride, int64_t n_pages, int32_t H_I,
+                            int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t k, float sm_scale,
+                            int32_t idx_dtype, int32_t attn_dtype, int32_t* idx, void* out, float* lse, void* ws,
+                            size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(q_pos && q_idx && q_scale && w && k_pool && k_pool_scale && q && kv_pool && block_table && idx && out,
+          "null pointer argument");
+  REQUIRE(B > 0 && B <= 65535 && n_q > 0 && n_k_max > 0, "B in [1, 65535], n_q > 0 and n_k_max > 0 required");
+  REQUIRE(n_q <= 2147483647LL && n_q * H <= 2147483647LL, "n_q too large");
+  SUPPORT(idx_dtype == DSA_FP8_E4M3 && attn_dtype == DSA_BF16, "paged chunks need an FP8 indexer and bf16 attention");
+  int st = check_indexer_shape(H_I, d_I, idx_dtype);
   if (st) return st;
-  dsa::MlaArgs a{q, kv_cache, v_cache, idx, B, n_q, n_k_max, H, d_qk, d_v, k, sm_scale, attn_dtype,
-                 out, lse, (char*)ws + s_bytes, ws_bytes - s_bytes, ld_q, ld_kv, v_cache ? ld_v : 0,
-                 kv_seq_stride, v_cache ? v_seq_stride : 0};
-  return hip_status(dsa::launch_sparse_mla(a, s), "chunk sparse attention launch");
+  st = check_attn_shape(H, d_qk, d_v, k, attn_dtype, false);
+  if (st) return st;
+  CHECK(check_ld("ld_q", ld_q, d_qk, attn_dtype));
+  CHECK(check_ld("ld_kv", ld_kv, d_qk, attn_dtype));
+  SUPPORT(k <= 2048, "FP8 selection keeps at most 2048 keys (k = %d)", k);
+  SUPPORT(n_k_max <= FUSED_MAX_KEYS, "FP8 selection supports n_k_max <= %lld", (long long)FUSED_MAX_KEYS);
+  REQUIRE(B * ((n_q + 3) / 4) <= 2147483647LL, "B * n_q too large");
+  const int64_t pages_per_seq = (n_k_max + dsa::PAGE_ROWS - 1) / dsa::PAGE_ROWS;
+  REQUIRE(bt_stride >= pages_per_seq, "bt_stride (%lld) must cover n_k_max (%lld pages of %d rows)",
+          (long long)bt_stride, (long long)pages_per_seq, dsa::PAGE_ROWS);
+  REQUIRE(n_pages > 0 && n_pages <= 2147483647LL / dsa::PAGE_ROWS, "n_pages must be in [1, 2^31 / %d)",
+          dsa::PAGE_ROWS);
+  REQUIRE(aligned16(q_idx) && aligned16(k_pool), "FP8 operands must be 16-byte aligned");
+  REQUIRE(aligned16(q) && aligned16(kv_pool) && aligned16(out), "bf16 operands must be 16-byte aligned");
+  dsa::PageTable pt;
+  pt.table = block_table;
+  pt.ld = bt_stride;
+  pt.n_pages = n_pages;
+  return chunk_run(B, n_q, q_pos, n_k_max, q_idx, q_scale, w, k_pool, k_pool_scale, 0, q, ld_q, kv_pool, ld_kv, 0,
+                   nullptr, 0, 0, H_I, d_I, H, d_qk, d_v, k, sm_scale, idx_dtype, attn_dtype, idx, out, lse, ws,
+                   ws_bytes, (hipStream_t)stream, pt, "dsa_forward_chunk_paged");
 }
 
 int dsa_indexer_scores_at(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,

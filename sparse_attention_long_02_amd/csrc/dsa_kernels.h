@@ -145,6 +145,7 @@ struct PrefillTopkArgs {
   // only rows [row_begin, row_end) of each sequence are selected and written (row_end < 0:
   // up to n_q)
   int64_t row_begin = 0, row_end = -1;
+  PageTable pages = {};     // non-null table: k8 / ks are page pools
 };
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st);
 
@@ -179,6 +180,7 @@ struct DenseIdxArgs {
   uint2* cand = nullptr;
   uint32_t* cnt = nullptr;
   int64_t k_bstride = 0;    // key rows between sequences of k8 / ks (0: n_k)
+  PageTable pages = {};     // non-null table: k8 / ks are page pools
 };
 inline int64_t dense_rows_pad(int64_t n_rows) { return (n_rows + 15) / 16 * 16; }
 hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st);

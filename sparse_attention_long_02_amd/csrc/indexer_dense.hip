@@ -56,19 +56,24 @@ __device__ __forceinline__ DenseDma dense_dma_lane(int wv, int lane) {
   return d;
 }
 // Key j of the launch is cache row j * stride; keys past n_keys - 1 (the last one the
-// launch may read) read that key (their scores are masked).
+// launch may read) read that key (their scores are masked).  kb / ksb: the sequence's rows,
+// or (PAGED) the page pools, whose rows the table gives.
+template <bool PAGED>
 __device__ __forceinline__ void dense_tile_load(uint32_t slot, const uint8_t* __restrict__ kb,
                                                 const float* __restrict__ ksb, int64_t key0, int64_t n_keys,
-                                                int64_t stride, const DenseDma& d, int wv, int lane) {
+                                                int64_t stride, const DenseDma& d, int wv, int lane,
+                                                const PageTable& pt, int b) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int64_t key = key0 + (d.off[i] >> 7);
     const int64_t kc = (key < n_keys ? key : n_keys - 1) * stride;
-    dma16_all(kb + kc * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
+    const int64_t row = PAGED ? paged_row(pt, b, kc) : kc;
+    dma16_all(kb + row * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
   }
   if (wv == 3) {
     const int64_t key = key0 + lane;
-    dma4_vaddr(ksb + (key < n_keys ? key : n_keys - 1) * stride, slot + DN_TILE_BYTES);
+    const int64_t kc = (key < n_keys ? key : n_keys - 1) * stride;
+    dma4_vaddr(ksb + (PAGED ? paged_row(pt, b, kc) : kc), slot + DN_TILE_BYTES);
   }
 }
 
@@ -91,13 +96,13 @@ __device__ __forceinline__ v8i dense_fragment(const uint8_t* tile, int f, int la
 // Store mode: the row's scores go to row b * 16 n_grp + i of `scores` (ld floats apart, ld
 // a multiple of 64 covering the tiles the row needs); keys it does not see score -inf.
 // Filter mode: see DenseIdxArgs.
-template <bool FILTER>
+template <bool FILTER, bool PAGED>
 __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, int B, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t row_begin, int64_t n_rows, int64_t n_grp, int stride,
     float* __restrict__ scores, int64_t ld, const float* __restrict__ thr, uint2* __restrict__ cand,
-    uint32_t* __restrict__ cnt) {
+    uint32_t* __restrict__ cnt, PageTable pt) {
   __shared__ __align__(16) uint8_t ring[DN_SLOTS * DN_SLOT_BYTES];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int b = (int)(blockIdx.x % B);
@@ -111,14 +116,15 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   const int64_t n_vis = lim_last >= 0 ? lim_last / stride + 1 : 0;
   const int ntiles = (int)((n_vis + KEY_TILE - 1) / KEY_TILE);
 
-  const uint8_t* kb = k8 + (size_t)b * kbs * IDX_DIM;
-  const float* ksb = ks + (size_t)b * kbs;
+  const uint8_t* kb = PAGED ? k8 : k8 + (size_t)b * kbs * IDX_DIM;
+  const float* ksb = PAGED ? ks : ks + (size_t)b * kbs;
   const uint32_t ring0 = lds_addr(ring);
   const DenseDma dl = dense_dma_lane(wv, lane);
 #pragma unroll
   for (int t = 0; t < DN_SLOTS - 2; ++t)
     if (t < ntiles)
-      dense_tile_load(ring0 + t * DN_SLOT_BYTES, kb, ksb, (int64_t)t * KEY_TILE, n_keys, stride, dl, wv, lane);
+      dense_tile_load<PAGED>(ring0 + t * DN_SLOT_BYTES, kb, ksb, (int64_t)t * KEY_TILE, n_keys, stride, dl, wv,
+                             lane, pt, b);
 
   // this wave's rows i0 + 4wv + j; padding rows score the last real row
   const int g = lane >> 4, c = lane & 15, rq = c >> 2;
@@ -263,11 +269,11 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
     block_barrier();
     // into the slots of tiles t-2 and t-1, which every wave is done with
     if (t + 4 < ntiles)
-      dense_tile_load(ring0 + ((t + 4) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb, (int64_t)(t + 4) * KEY_TILE, n_keys,
-                      stride, dl, wv, lane);
+      dense_tile_load<PAGED>(ring0 + ((t + 4) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb, (int64_t)(t + 4) * KEY_TILE,
+                             n_keys, stride, dl, wv, lane, pt, b);
     if (t + 5 < ntiles)
-      dense_tile_load(ring0 + ((t + 5) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb, (int64_t)(t + 5) * KEY_TILE, n_keys,
-                      stride, dl, wv, lane);
+      dense_tile_load<PAGED>(ring0 + ((t + 5) % DN_SLOTS) * DN_SLOT_BYTES, kb, ksb, (int64_t)(t + 5) * KEY_TILE,
+                             n_keys, stride, dl, wv, lane, pt, b);
     const int t_end = t + 2 < ntiles ? t + 2 : ntiles;
 #pragma nounroll
     for (int u = t; u < t_end; ++u) tile_step(u);
@@ -284,14 +290,19 @@ hipError_t launch_idx_dense(const DenseIdxArgs& a, hipStream_t st) {
   const int64_t n_grp = (a.n_rows + 15) / 16;
   if (n_grp <= 0) return hipSuccess;
   if (a.key_stride < 1 || (a.cand && a.key_stride != 1)) return hipErrorInvalidValue;
-  if (a.cand)
-    hipLaunchKernelGGL(idx_dense_fp8_kernel<true>, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8,
-                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.k_bstride ? a.k_bstride : a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp, 1,
-                       nullptr, (int64_t)0, a.thr, a.cand, a.cnt);
-  else
-    hipLaunchKernelGGL(idx_dense_fp8_kernel<false>, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8,
-                       a.qs, a.k8, a.ks, a.w, (int)a.B, a.n_q, a.n_k, a.k_bstride ? a.k_bstride : a.n_k, a.q_pos, a.row_begin, a.n_rows, n_grp,
-                       a.key_stride, a.scores, a.ld, nullptr, nullptr, nullptr);
+  const bool paged = a.pages.table != nullptr;
+  const int64_t kbs = a.k_bstride ? a.k_bstride : a.n_k;
+  if (a.cand) {
+    auto kern = paged ? idx_dense_fp8_kernel<true, true> : idx_dense_fp8_kernel<true, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8, a.qs, a.k8, a.ks, a.w,
+                       (int)a.B, a.n_q, a.n_k, kbs, a.q_pos, a.row_begin, a.n_rows, n_grp, 1, nullptr, (int64_t)0,
+                       a.thr, a.cand, a.cnt, a.pages);
+  } else {
+    auto kern = paged ? idx_dense_fp8_kernel<false, true> : idx_dense_fp8_kernel<false, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.B * n_grp)), dim3(DN_WAVES * 64), 0, st, a.q8, a.qs, a.k8, a.ks, a.w,
+                       (int)a.B, a.n_q, a.n_k, kbs, a.q_pos, a.row_begin, a.n_rows, n_grp, a.key_stride, a.scores,
+                       a.ld, nullptr, nullptr, nullptr, a.pages);
+  }
   return hipGetLastError();
 }
 

@@ -274,13 +274,20 @@ __device__ __forceinline__ TileDma tile_dma_lane(int wv, int lane) {
   const int row = U >> 3, cp = U & 7;
   return TileDma{row, (uint32_t)(16 * (cp ^ (row & 7)))};
 }
+template <bool PAGED>
 __device__ __forceinline__ void dma_key_tile(uint8_t* tk, float* ts, const uint8_t* __restrict__ k8,
                                              const float* __restrict__ ks, int key0, int L, const TileDma& d,
-                                             int wv, int lane) {
-  // 32-bit offsets from the uniform bases (L * 128 < 2^32 for every supported L)
-  const uint32_t key = (uint32_t)min(key0 + d.krow, L - 1);
-  __builtin_amdgcn_global_load_lds(k8 + (key * IDX_DIM + d.koff), tk + 1024 * wv, 16, 0, 0);
-  if (wv == 0) __builtin_amdgcn_global_load_lds(ks + (uint32_t)min(key0 + lane, L - 1), ts, 4, 0, 0);
+                                             int wv, int lane, const PageTable& pt, int b) {
+  if constexpr (!PAGED) {
+    // 32-bit offsets from the uniform bases (L * 128 < 2^32 for every supported L)
+    const uint32_t key = (uint32_t)min(key0 + d.krow, L - 1);
+    __builtin_amdgcn_global_load_lds(k8 + (key * IDX_DIM + d.koff), tk + 1024 * wv, 16, 0, 0);
+    if (wv == 0) __builtin_amdgcn_global_load_lds(ks + (uint32_t)min(key0 + lane, L - 1), ts, 4, 0, 0);
+  } else {  // k8 / ks are the page pools
+    const int64_t row = paged_row(pt, b, min(key0 + d.krow, L - 1));
+    __builtin_amdgcn_global_load_lds(k8 + row * IDX_DIM + d.koff, tk + 1024 * wv, 16, 0, 0);
+    if (wv == 0) __builtin_amdgcn_global_load_lds(ks + paged_row(pt, b, min(key0 + lane, L - 1)), ts, 4, 0, 0);
+  }
 }
 
 // wait until step s's two tiles have landed (step s+1's may still be in flight); wave 0
@@ -411,11 +418,12 @@ __device__ __forceinline__ bool group_skipped(const uint8_t* __restrict__ redo, 
   return !any;
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, const int32_t* __restrict__ q_pos, int B,
     int n_q, int n_k, int64_t kbs, int row_lo, int row_end, int k, int g_begin, int g_end,
-    int32_t* __restrict__ idx, const uint8_t* __restrict__ redo) {
+    int32_t* __restrict__ idx, const uint8_t* __restrict__ redo, PageTable pt) {
   // ring of three tile pairs (pair p = tiles 2p, 2p+1) and their key scales
   __shared__ __align__(16) uint8_t tk0[TILE_BYTES];
   __shared__ __align__(16) uint8_t tk1[TILE_BYTES];
@@ -444,8 +452,8 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
       if (g.n_keys <= k) continue;  // every row keeps all it sees: the owners write it
       const int row0 = g.row_hi - 4;
       const size_t rbase = (size_t)g.b * n_q;
-      const uint8_t* kb = k8 + (size_t)g.b * kbs * IDX_DIM;
-      const float* ksb = ks + (size_t)g.b * kbs;
+      const uint8_t* kb = PAGED ? k8 : k8 + (size_t)g.b * kbs * IDX_DIM;
+      const float* ksb = PAGED ? ks : ks + (size_t)g.b * kbs;
       IdxHalf Qh[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -460,7 +468,7 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
       // owners never take a key past their row's position)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (j < 2 * nsteps) dma_key_tile(tks[j], tss[j], kb, ksb, j * KEY_TILE, L, dl, wv, lane);
+        if (j < 2 * nsteps) dma_key_tile<PAGED>(tks[j], tss[j], kb, ksb, j * KEY_TILE, L, dl, wv, lane, pt, g.b);
 
       for (int base = 0; base <= nsteps; base += 3) {
 #pragma unroll
@@ -473,8 +481,10 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_idx_topk_kernel(
             if (st < nsteps) {
               if (st + 2 < nsteps) {  // into the pair of step st-1, which every wave is done with
                 const int q = (pp + 2) % 3;
-                dma_key_tile(tks[2 * q], tss[2 * q], kb, ksb, (2 * st + 4) * KEY_TILE, L, dl, wv, lane);
-                dma_key_tile(tks[2 * q + 1], tss[2 * q + 1], kb, ksb, (2 * st + 5) * KEY_TILE, L, dl, wv, lane);
+                dma_key_tile<PAGED>(tks[2 * q], tss[2 * q], kb, ksb, (2 * st + 4) * KEY_TILE, L, dl, wv, lane, pt,
+                                    g.b);
+                dma_key_tile<PAGED>(tks[2 * q + 1], tss[2 * q + 1], kb, ksb, (2 * st + 5) * KEY_TILE, L, dl, wv,
+                                    lane, pt, g.b);
               }
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
@@ -599,10 +609,10 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t st) {
     const int64_t g_end = a.B * ((a.n_q - 1 - row_lo) / 4 + 1);
     const int64_t n_groups = g_end - g_begin;
     const int64_t blocks = n_groups < n_cu ? n_groups : n_cu;
-    hipLaunchKernelGGL(prefill_idx_topk_kernel, dim3((unsigned)blocks), dim3(PF_WAVES * 64), 0, st, a.q8, a.qs,
-                       a.k8, a.ks, a.w, a.q_pos, (int)a.B, (int)a.n_q, (int)a.n_k,
-                       a.k_bstride ? a.k_bstride : a.n_k, (int)row_lo, (int)row_end, a.k, (int)g_begin,
-                       (int)g_end, a.idx, a.redo);
+    hipLaunchKernelGGL(a.pages.table ? prefill_idx_topk_kernel<true> : prefill_idx_topk_kernel<false>,
+                       dim3((unsigned)blocks), dim3(PF_WAVES * 64), 0, st, a.q8, a.qs, a.k8, a.ks, a.w, a.q_pos,
+                       (int)a.B, (int)a.n_q, (int)a.n_k, a.k_bstride ? a.k_bstride : a.n_k, (int)row_lo,
+                       (int)row_end, a.k, (int)g_begin, (int)g_end, a.idx, a.redo, a.pages);
   }
   return hipGetLastError();
 }

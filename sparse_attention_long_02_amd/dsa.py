@@ -48,6 +48,9 @@ _SIGNATURES = {
     "dsa_forward_decode_paged": (ctypes.c_int, [_i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
                                                 _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                                 _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dsa_forward_chunk_paged": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
+                                               _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                               _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dsa_forward_chunk": (ctypes.c_int, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
                                          _vp, _i64, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -297,6 +300,17 @@ def forward_decode(ctx_len, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cac
     return idx, out, lse
 
 
+def _pools(k_pool, k_pool_scale, kv_pool, block_table, d_I):
+    """Check the page pools and the block table; returns the number of whole pages."""
+    if not (k_pool.is_cuda and k_pool_scale.is_cuda and kv_pool.is_cuda and block_table.is_cuda):
+        raise ValueError("libdsa takes device tensors")
+    if k_pool.dim() != 2 or k_pool.stride(1) != 1 or k_pool.stride(0) != d_I or k_pool_scale.stride(-1) != 1:
+        raise ValueError("the indexer key pool is [rows, d_I] with dense rows")
+    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.dtype != torch.int32:
+        raise ValueError("block_table is [B, pages] int32 with contiguous rows")
+    return min(k_pool.shape[0], k_pool_scale.shape[0], kv_pool.shape[0]) // DSA_PAGE_ROWS
+
+
 def forward_decode_paged(ctx_len, q_idx, q_scale, w, k_pool, k_pool_scale, q, kv_pool, block_table, n_k_max: int,
                          k: int, sm_scale: float, d_v: int, idx=None, out=None, lse=None, ws=None):
     """forward_decode over paged caches -> (idx [B, k], out, lse).  Pools of n_pages pages of
@@ -307,11 +321,7 @@ def forward_decode_paged(ctx_len, q_idx, q_scale, w, k_pool, k_pool_scale, q, kv
     _, H, d_qk = q.shape
     it, at = _idx_dtype(q_idx), _attn_dtype(q)
     dev = q.device
-    if k_pool.dim() != 2 or k_pool.stride(1) != 1 or k_pool.stride(0) != d_I or k_pool_scale.stride(-1) != 1:
-        raise ValueError("the indexer key pool is [rows, d_I] with dense rows")
-    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.dtype != torch.int32:
-        raise ValueError("block_table is [B, pages] int32 with contiguous rows")
-    n_pages = min(k_pool.shape[0], k_pool_scale.shape[0], kv_pool.shape[0]) // DSA_PAGE_ROWS
+    n_pages = _pools(k_pool, k_pool_scale, kv_pool, block_table, d_I)
     idx = torch.empty((B, k), dtype=torch.int32, device=dev) if idx is None else idx
     out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev) if out is None else out
     lse = torch.empty((B, H), dtype=torch.float32, device=dev) if lse is None else lse
@@ -375,6 +385,30 @@ def forward_chunk(q_pos, q_idx, q_scale, w, k_cache, k_cache_scale, q, kv_cache,
                                    v_p, ld_v, bs_v, H_I, d_I, H, d_qk, d_v, k, float(sm_scale), it, at,
                                    _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream()))
+    return idx, out, lse
+
+
+def forward_chunk_paged(q_pos, q_idx, q_scale, w, k_pool, k_pool_scale, q, kv_pool, block_table, n_k_max: int,
+                        k: int, sm_scale: float, d_v: int, idx=None, out=None, lse=None, ws=None):
+    """forward_chunk over paged caches (pools and block table as forward_decode_paged)
+    -> (idx [B, n_q, k], out [B, n_q, H, d_v], lse [B, n_q, H])."""
+    B, n_q, H_I, d_I = q_idx.shape
+    _, _, H, d_qk = q.shape
+    it, at = _idx_dtype(q_idx), _attn_dtype(q)
+    dev = q.device
+    n_pages = _pools(k_pool, k_pool_scale, kv_pool, block_table, d_I)
+    idx = torch.empty((B, n_q, k), dtype=torch.int32, device=dev) if idx is None else idx
+    out = torch.empty((B, n_q, H, d_v), dtype=q.dtype, device=dev) if out is None else out
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    if ws is None:
+        ws = _workspace(workspace_size(DSA_OP_CHUNK, B, n_q, n_k_max, H, d_v, k, at), dev)
+    q_p, ld_q = _rows(q, 3)
+    kv_p, ld_kv = _rows(kv_pool, 1)
+    _check(lib().dsa_forward_chunk_paged(B, n_q, _ptr(q_pos), n_k_max, _ptr(q_idx), _ptr(q_scale), _ptr(w),
+                                         k_pool.data_ptr(), k_pool_scale.data_ptr(), q_p, ld_q, kv_p, ld_kv,
+                                         block_table.data_ptr(), block_table.stride(0), n_pages, H_I, d_I, H,
+                                         d_qk, d_v, k, float(sm_scale), it, at, _ptr(idx), _ptr(out), _ptr(lse),
+                                         _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return idx, out, lse
 
 

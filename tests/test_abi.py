@@ -27,7 +27,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = declared_symbols()
-    assert len(syms) == 19
+    assert len(syms) == 20
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(dsa._SIGNATURES)
@@ -163,6 +163,27 @@ def test_paged_decode_validation(L):
     assert call(bts=n, ldkv=640, ldq=1024) == dsa.DSA_ERR_WORKSPACE   # a longer table and padded rows pass
     assert call() == dsa.DSA_ERR_WORKSPACE
     need = L.dsa_workspace_size(dsa.DSA_OP_DECODE, 64, 1, n, 128, 512, 2048, dsa.DSA_BF16)
+    assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG   # misaligned workspace
+
+
+def test_paged_chunk_validation(L):
+    """dsa_forward_chunk_paged: the same host-side refusals; no call here gets past them."""
+    n = 131072
+    pg = dict(B=1, nq=8192, qpos=FAKE, nkm=n, qi=FAKE, qs=FAKE, w=FAKE, kp=FAKE, kps=FAKE, q=FAKE, ldq=576, kv=FAKE,
+              ldkv=576, bt=FAKE, bts=n // dsa.DSA_PAGE_ROWS, npg=n, H_I=64, d_I=128, H=128, dqk=576, dv=512,
+              k=2048, sm=0.04, it=dsa.DSA_FP8_E4M3, at=dsa.DSA_BF16, idx=FAKE, out=FAKE, lse=None, ws=None,
+              wsb=0, st=None)
+    order = list(pg)
+    call = lambda **kw: L.dsa_forward_chunk_paged(*[kw.get(n, pg[n]) for n in order])
+    assert call(qpos=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(bts=n // dsa.DSA_PAGE_ROWS - 1) == dsa.DSA_ERR_INVALID_ARG
+    assert b"bt_stride" in L.dsa_last_error()
+    assert call(npg=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(it=dsa.DSA_F32, at=dsa.DSA_F32) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(q=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG
+    assert call() == dsa.DSA_ERR_WORKSPACE
+    need = L.dsa_workspace_size(dsa.DSA_OP_CHUNK, 1, 8192, n, 128, 512, 2048, dsa.DSA_BF16)
     assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG   # misaligned workspace
 
 

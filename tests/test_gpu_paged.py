@@ -70,3 +70,45 @@ def test_paged_decode_matches_contiguous(B, L, ctx_l, zero_q, seed):
         assert torch.equal(g_lse, r_lse), f"page order {rep}: lse differs"
     if zero_q:  # an all-zero query ties every key: the lowest k indices win
         assert np.array_equal(g_idx[zero_q[0]].cpu().numpy(), np.arange(cfg.k))
+
+
+def _chunk_case(q_pos, n_q, n_k, seed0):
+    """Per-sequence prefill inputs: the chunk's query rows (positions q_pos[b] .. + n_q - 1,
+    clipped into the sequence for the data) and whole caches, stacked over sequences."""
+    cfg = S.CONFIGS["prefill_8k"].with_(L=n_k)
+    inps = [S.make_prefill(cfg.with_(seed=seed0 + b)) for b in range(len(q_pos))]
+    rows = [np.clip(np.arange(p, p + n_q), 0, n_k - 1) for p in q_pos]
+    qi = dev_u8(np.stack([inp.qi[r] for inp, r in zip(inps, rows)]))
+    qs = dev_f32(np.stack([inp.q_scale[r] for inp, r in zip(inps, rows)]))
+    w = dev_f32(np.stack([inp.w[r] for inp, r in zip(inps, rows)]))
+    q = dev_bf16(np.stack([inp.q[r] for inp, r in zip(inps, rows)]))
+    kc = dev_u8(np.stack([inp.ki for inp in inps]))
+    kcs = dev_f32(np.stack([inp.k_scale for inp in inps]))
+    kv = dev_bf16(np.stack([inp.kv for inp in inps]))
+    return cfg, qi, qs, w, q, kc, kcs, kv
+
+
+@pytest.mark.parametrize("case", ["plain", "sample_low"])
+def test_paged_chunk_matches_contiguous(case):
+    """dsa_forward_chunk_paged against dsa_forward_chunk on the contiguous caches: B = 4
+    sequences of 4200 rows against 12288 cached keys (two selection passes per sequence,
+    sampled thresholds past 6144 keys), offsets -100 .. 10000.  "sample_low" zeroes every
+    32nd key, so that rows past 6144 keys overflow their candidate lists and go to the exact
+    re-selection, which then reads the keys through the table too."""
+    q_pos, n_q, n_k = [-100, 3000, 8000, 10000], 4200, 12288
+    _say(f"[paged chunk] {case}: B=4, n_q={n_q}, n_k_max={n_k}")
+    cfg, qi, qs, w, q, kc, kcs, kv = _chunk_case(q_pos, n_q, n_k, 61)
+    if case == "sample_low":
+        kc = kc.clone()
+        kc[:, ::32] = 0
+    pos = torch.tensor(q_pos, dtype=torch.int32, device="cuda")
+    r_idx, r_out, r_lse = dsa.forward_chunk(pos, qi, qs, w, kc, kcs, q, kv, cfg.k, cfg.sm_scale, cfg.d_v)
+    # every sequence's cache is complete up to n_k (the chunk rows included)
+    k_pool, ks_pool, kv_pool, table = _paged_pools(kc, kcs, kv, [n_k] * len(q_pos), np.random.default_rng(62))
+    g_idx, g_out, g_lse = dsa.forward_chunk_paged(pos, qi, qs, w, k_pool, ks_pool, q, kv_pool, table, n_k, cfg.k,
+                                                  cfg.sm_scale, cfg.d_v)
+    torch.cuda.synchronize()
+    bad = (g_idx != r_idx).any(dim=2).nonzero().tolist()
+    assert not bad, f"{len(bad)} rows select differently, first {bad[:5]}"
+    assert torch.equal(g_out.view(torch.int16), r_out.view(torch.int16))
+    assert torch.equal(g_lse, r_lse)
