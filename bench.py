@@ -452,7 +452,41 @@ def main():
         decode = {"workload": dcfg.name, "us_per_step": t_dec * 1e6, "us_median": t_dec_med * 1e6,
                   "us_min": t_dec_min * 1e6, "steps": max(args.steps, 10), "batch": dcfg.batch, "ctx": dcfg.L,
                   "index_cache_bytes": icache, "index_cache_hbm_frac": icache / t_dec / PEAK_HBM}
-        del ctx, dqi, dqs, dw, kc, kcs, dq, kvc, ws_d, didx, dout, dlse
+
+        # the same step over paged caches: the caches' 64-token pages copied into pools in a
+        # seeded random order, read through the block table
+        P = dsa.DSA_PAGE_ROWS
+        pps = (dcfg.L + P - 1) // P
+        n_pages = dcfg.batch * pps
+        perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(7)).view(dcfg.batch, pps)
+        table = perm.to(torch.int32).cuda()
+        s_idx = torch.arange(dcfg.L)
+        rows = (perm[:, s_idx // P] * P + s_idx % P).reshape(-1).cuda()
+        kp = torch.empty((n_pages * P, dcfg.d_I), dtype=kc.dtype, device="cuda")
+        ksp = torch.empty((n_pages * P,), dtype=kcs.dtype, device="cuda")
+        kvp = torch.empty((n_pages * P, dcfg.d_qk), dtype=kvc.dtype, device="cuda")
+        kp[rows] = kc.reshape(-1, dcfg.d_I)
+        ksp[rows] = kcs.reshape(-1)
+        kvp[rows] = kvc.reshape(-1, dcfg.d_qk)
+        del rows
+        ref_out = dout.clone()
+        pidx = torch.empty_like(didx)
+        pout = torch.empty_like(dout)
+        plse = torch.empty_like(dlse)
+
+        def pstep():
+            dsa.forward_decode_paged(ctx, dqi, dqs, dw, kp, ksp, dq, kvp, table, dcfg.L, dcfg.k, dcfg.sm_scale,
+                                     dcfg.d_v, idx=pidx, out=pout, lse=plse, ws=ws_d)
+        for _ in range(args.warmup):
+            pstep()
+        t_pg, t_pg_med, t_pg_min = time_each(torch, pstep, max(args.steps, 10))
+        same = bool(torch.equal(pout.view(torch.int16), ref_out.view(torch.int16)))
+        log(f"[bench] paged decode {t_pg * 1e6:.1f} us/step (median {t_pg_med * 1e6:.1f}); output equal to "
+            f"the contiguous decode: {same}")
+        decode["paged"] = {"us_per_step": t_pg * 1e6, "us_median": t_pg_med * 1e6, "us_min": t_pg_min * 1e6,
+                           "page_rows": P, "output_equal_to_contiguous": same}
+        del ctx, dqi, dqs, dw, kc, kcs, dq, kvc, ws_d, didx, dout, dlse, kp, ksp, kvp, table, pidx, pout, plse
+        del ref_out
         torch.cuda.empty_cache()
 
     others = []
