@@ -60,6 +60,16 @@ __device__ __forceinline__ int64_t paged_row(const PageTable& pt, int b, int64_t
   p = p < 0 ? 0 : p >= pt.n_pages ? pt.n_pages - 1 : p;
   return p * PAGE_ROWS + (j & (PAGE_ROWS - 1));
 }
+// A 64-key tile of consecutive tokens starting at key0 (a multiple of 64) whose keys are
+// clamped to `last`: every key it reads lies on one page, found with one table lookup.
+// Returns the pool row of token `first` = min(key0, start of last's page); token j of the
+// tile (j in [first, first + 64)) is then at that row + (j - first).
+__device__ __forceinline__ int64_t paged_tile_base(const PageTable& pt, int b, int64_t key0, int64_t last,
+                                                   int64_t& first) {
+  const int64_t last_page0 = last & ~(int64_t)(PAGE_ROWS - 1);
+  first = key0 < last_page0 ? key0 : last_page0;
+  return paged_row(pt, b, first);
+}
 
 struct SplitIdxArgs {
   const uint8_t* q8;

@@ -70,16 +70,25 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_rows(
 // Key fragment f of the tile at launch key key0 and the scale of launch key `key` (clamped to
 // n_keys - 1; launch key j is cache token j * stride of sequence b), from the contiguous
 // per-sequence cache (kbs rows apart) or, PAGED, through the page table.
+// Paged: with stride 1 a 64-key tile (key0 a multiple of 64) is one page, whose first pool
+// row `row0` the caller looks up once per tile; strided keys look up their own pages.
+template <bool PAGED>
+__device__ __forceinline__ int64_t split_key_row(const PageTable& pt, int b, int64_t key, int64_t key0,
+                                                 int64_t row0, int stride) {
+  return stride == 1 ? row0 + (key - key0) : paged_row(pt, b, key * stride);
+}
 template <bool PAGED>
 __device__ __forceinline__ v8i split_key_fragment(const uint8_t* __restrict__ k8, const PageTable& pt, int b,
-                                                  int64_t kbs, int64_t key0, int f, int64_t n_keys, int stride) {
+                                                  int64_t kbs, int64_t key0, int f, int64_t n_keys, int stride,
+                                                  int64_t row0) {
   if constexpr (!PAGED) {
     return global_key_fragment(k8 + (int64_t)b * kbs * IDX_DIM, key0, f, n_keys, stride);
   } else {
     const int l = lane_id();
     int64_t key = key0 + 16 * f + (l & 15);
     key = key < n_keys ? key : n_keys - 1;
-    const v4i* p = reinterpret_cast<const v4i*>(k8 + paged_row(pt, b, key * stride) * IDX_DIM + 32 * (l >> 4));
+    const v4i* p = reinterpret_cast<const v4i*>(k8 + split_key_row<PAGED>(pt, b, key, key0, row0, stride) * IDX_DIM +
+                                                32 * (l >> 4));
     const v4i lo = p[0];
     const v4i hi = p[1];
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -87,10 +96,17 @@ __device__ __forceinline__ v8i split_key_fragment(const uint8_t* __restrict__ k8
 }
 template <bool PAGED>
 __device__ __forceinline__ float split_key_scale(const float* __restrict__ ks, const PageTable& pt, int b,
-                                                 int64_t kbs, int64_t key, int64_t n_keys, int stride) {
+                                                 int64_t kbs, int64_t key, int64_t key0, int64_t n_keys, int stride,
+                                                 int64_t row0) {
   key = key < n_keys ? key : n_keys - 1;
   if constexpr (!PAGED) return ks[(int64_t)b * kbs + key * stride];
-  else return ks[paged_row(pt, b, key * stride)];
+  else return ks[split_key_row<PAGED>(pt, b, key, key0, row0, stride)];
+}
+// pool row of the first key of the tile at key0 (stride 1), looked up once per tile
+template <bool PAGED>
+__device__ __forceinline__ int64_t split_tile_row(const PageTable& pt, int b, int64_t key0, int stride) {
+  if constexpr (!PAGED) return 0;
+  else return stride == 1 ? paged_row(pt, b, key0) : 0;
 }
 
 // grid: x = key splits of SPLIT_TILES tiles, y = row, z = sequence.
@@ -156,9 +172,11 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
   float ksc;
   {
     const int64_t key0 = t * KEY_TILE, key = key0 + lane;
+    const int64_t row0 = split_tile_row<PAGED>(pt, b, key0, key_stride);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) bf[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride);
-    ksc = split_key_scale<PAGED>(ks, pt, b, kbs, key, n_keys, key_stride);
+    for (int f = 0; f < 4; ++f)
+      bf[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride, row0);
+    ksc = split_key_scale<PAGED>(ks, pt, b, kbs, key, key0, n_keys, key_stride, row0);
   }
   for (; t < t_vis; t += 4) {
     const int64_t tn = t + 4;
@@ -166,9 +184,11 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     float kn = ksc;
     if (tn < t_vis) {
       const int64_t key0 = tn * KEY_TILE, key = key0 + lane;
+      const int64_t row0 = split_tile_row<PAGED>(pt, b, key0, key_stride);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) bn[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride);
-      kn = split_key_scale<PAGED>(ks, pt, b, kbs, key, n_keys, key_stride);
+      for (int f = 0; f < 4; ++f)
+        bn[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride, row0);
+      kn = split_key_scale<PAGED>(ks, pt, b, kbs, key, key0, n_keys, key_stride, row0);
     }
     const int64_t key = t * KEY_TILE + lane;
     const float sc = score_tile64(Q, bf, ksc);

@@ -63,17 +63,23 @@ __device__ __forceinline__ void dense_tile_load(uint32_t slot, const uint8_t* __
                                                 const float* __restrict__ ksb, int64_t key0, int64_t n_keys,
                                                 int64_t stride, const DenseDma& d, int wv, int lane,
                                                 const PageTable& pt, int b) {
+  // paged, stride 1: the tile is one page, looked up once (strided keys look up their own)
+  int64_t first = 0, base = 0;
+  if (PAGED && stride == 1) base = paged_tile_base(pt, b, key0, n_keys - 1, first);
+  auto row_of = [&](int64_t kc) -> int64_t {
+    if constexpr (!PAGED) return kc;
+    else return stride == 1 ? base + (kc - first) : paged_row(pt, b, kc);
+  };
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int64_t key = key0 + (d.off[i] >> 7);
     const int64_t kc = (key < n_keys ? key : n_keys - 1) * stride;
-    const int64_t row = PAGED ? paged_row(pt, b, kc) : kc;
-    dma16_all(kb + row * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
+    dma16_all(kb + row_of(kc) * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
   }
   if (wv == 3) {
     const int64_t key = key0 + lane;
     const int64_t kc = (key < n_keys ? key : n_keys - 1) * stride;
-    dma4_vaddr(ksb + (PAGED ? paged_row(pt, b, kc) : kc), slot + DN_TILE_BYTES);
+    dma4_vaddr(ksb + row_of(kc), slot + DN_TILE_BYTES);
   }
 }
 

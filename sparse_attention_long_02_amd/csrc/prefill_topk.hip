@@ -283,10 +283,12 @@ __device__ __forceinline__ void dma_key_tile(uint8_t* tk, float* ts, const uint8
     const uint32_t key = (uint32_t)min(key0 + d.krow, L - 1);
     __builtin_amdgcn_global_load_lds(k8 + (key * IDX_DIM + d.koff), tk + 1024 * wv, 16, 0, 0);
     if (wv == 0) __builtin_amdgcn_global_load_lds(ks + (uint32_t)min(key0 + lane, L - 1), ts, 4, 0, 0);
-  } else {  // k8 / ks are the page pools
-    const int64_t row = paged_row(pt, b, min(key0 + d.krow, L - 1));
+  } else {  // k8 / ks are the page pools; the tile's keys lie on one page (one lookup)
+    int64_t first = 0;
+    const int64_t base = paged_tile_base(pt, b, key0, L - 1, first);
+    const int64_t row = base + (min(key0 + d.krow, L - 1) - first);
     __builtin_amdgcn_global_load_lds(k8 + row * IDX_DIM + d.koff, tk + 1024 * wv, 16, 0, 0);
-    if (wv == 0) __builtin_amdgcn_global_load_lds(ks + paged_row(pt, b, min(key0 + lane, L - 1)), ts, 4, 0, 0);
+    if (wv == 0) __builtin_amdgcn_global_load_lds(ks + base + (min(key0 + lane, L - 1) - first), ts, 4, 0, 0);
   }
 }
 
