@@ -159,15 +159,7 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     if (FILTER && lane == 0) cnt[seg] = 0u;
     return;
   }
-  IdxRow Q;
-  load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
-  float T = 0.f;
-  uint2* crow = nullptr;
-  uint32_t ccount = 0;  // wave-uniform
-  if (FILTER) {
-    T = thr[rid];
-    crow = cand + seg * DEC_SEG;
-  }
+  // the first tile's loads go out before the query row's, so both are in flight at once
   v8i bf[4];
   float ksc;
   {
@@ -177,6 +169,15 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     for (int f = 0; f < 4; ++f)
       bf[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride, row0);
     ksc = split_key_scale<PAGED>(ks, pt, b, kbs, key, key0, n_keys, key_stride, row0);
+  }
+  IdxRow Q;
+  load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
+  float T = 0.f;
+  uint2* crow = nullptr;
+  uint32_t ccount = 0;  // wave-uniform
+  if (FILTER) {
+    T = thr[rid];
+    crow = cand + seg * DEC_SEG;
   }
   for (; t < t_vis; t += 4) {
     const int64_t tn = t + 4;

@@ -138,34 +138,64 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
   v8h_t W[2][4];
   float cmx = 0.f;
   int64_t lim = -1;
+  auto row_of = [&](int j) {
+    const int64_t i = i0 + 4 * wv + j;
+    return (int64_t)b * n_q + row_begin + (i < n_rows ? i : n_rows - 1);
+  };
+  // every load first (A operands, the four rows' normaliser inputs, and the weights and
+  // scales of this lane's row rq), then the arithmetic: the empty asm in head_weight_f16()
+  // keeps loads from moving above it, so loads placed between the conversions would each
+  // wait out their own latency
+  float wl[4], sl[4], wh[2][8], sh[2][8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t i = i0 + 4 * wv + j;
-    const int64_t qrow = (int64_t)b * n_q + row_begin + (i < n_rows ? i : n_rows - 1);
-    const uint8_t* qr = q8 + qrow * IDX_HEADS * IDX_DIM;
-    const float* qsr = qs + qrow * IDX_HEADS;
-    const float* wr = w + qrow * IDX_HEADS;
+    const int64_t qrow = row_of(j);
+    wl[j] = w[qrow * IDX_HEADS + lane];
+    sl[j] = qs[qrow * IDX_HEADS + lane];
+  }
+  {
+    const int64_t qrow = row_of(rq);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wh[hh][e] = w[qrow * IDX_HEADS + slot_head(hh, e, lane)];
+        sh[hh][e] = qs[qrow * IDX_HEADS + slot_head(hh, e, lane)];
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint8_t* qr = q8 + row_of(j) * IDX_HEADS * IDX_DIM;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       const v4i* p = reinterpret_cast<const v4i*>(qr + (16 * hb + c) * IDX_DIM + 32 * g);
       const v4i lo = p[0], hi = p[1];
       A[j][hb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    const float cm = row_cmax(qsr, wr);
-    const float inv = cm > 0.f ? 1.f / cm : 0.f;
+  }
+  float cm_own = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int h = 32 * hh + 16 * (e >> 2) + 4 * g + (e & 3);
-        W[hh][j][e] = rq == j ? head_weight_f16(wr[h], qsr[h], inv) : (_Float16)0.f;
-      }
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = i0 + 4 * wv + j;
+    const float cm = row_cmax_of(wl[j], sl[j]);
+    if (rq == j) cm_own = cm;
     if (g == j) {
       cmx = __fmul_rn(cm, UNSCALE);
       const int64_t p = pos0 + i;
       const int64_t lk = p < n_k - 1 ? p : n_k - 1;
       lim = lk >= 0 ? lk / stride : -1;
     }
+  }
+  {
+    const float inv = cm_own > 0.f ? 1.f / cm_own : 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 wt = head_weight_f16(wh[hh][e], sh[hh][e], inv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) W[hh][j][e] = rq == j ? wt : (_Float16)0.f;
+      }
   }
   const int64_t my_row = (int64_t)b * 16 * n_grp + i0 + 4 * wv + g;
   float* srow = scores + my_row * ld + 4 * c;

@@ -54,13 +54,17 @@ struct IdxHalf {
   v8h wa;
 };
 
-// Per-row weight normaliser: cs = max_j |w_j q_scale_j| * 2^25 (0 if all weights vanish).
-__device__ __forceinline__ float row_cmax(const float* __restrict__ qs, const float* __restrict__ w) {
-  const int l = lane_id();
-  float m = fabsf(__fmul_rn(w[l], qs[l]));
+// Per-row weight normaliser: cs = max_j |w_j q_scale_j| * 2^25 (0 if all weights vanish),
+// from lane j's head weight and query scale.
+__device__ __forceinline__ float row_cmax_of(float w_l, float qs_l) {
+  float m = fabsf(__fmul_rn(w_l, qs_l));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
   return m;
+}
+__device__ __forceinline__ float row_cmax(const float* __restrict__ qs, const float* __restrict__ w) {
+  const int l = lane_id();
+  return row_cmax_of(w[l], qs[l]);
 }
 
 // f16 head weight (w * q_scale) / max|c|: rounded to fp32, then to f16.  The empty asm keeps
@@ -72,25 +76,41 @@ __device__ __forceinline__ _Float16 head_weight_f16(float w, float qs, float inv
   return (_Float16)p;
 }
 
-__device__ __forceinline__ void load_idx_half(IdxHalf& Q, const uint8_t* __restrict__ q8,
-                                              const float* __restrict__ qs, const float* __restrict__ w,
-                                              int hh, float cmax) {
+// The head whose weight lane l packs in slot e of head half hh.
+__device__ __forceinline__ int slot_head(int hh, int e, int l) {
+  return 32 * hh + 16 * (e >> 2) + 4 * (l >> 4) + (e & 3);
+}
+
+// A operands of head half hh: head blocks 2hh, 2hh+1.
+__device__ __forceinline__ void load_idx_half_a(IdxHalf& Q, const uint8_t* __restrict__ q8, int hh) {
   const int l = lane_id();
-  const int g = l >> 4;
-  const float inv = cmax > 0.f ? 1.f / cmax : 0.f;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int hb = 2 * hh + k;
     const int head = 16 * hb + (l & 15);
-    const v4i* p = reinterpret_cast<const v4i*>(q8 + head * IDX_DIM + 32 * g);
+    const v4i* p = reinterpret_cast<const v4i*>(q8 + head * IDX_DIM + 32 * (l >> 4));
     const v4i lo = p[0], hi = p[1];
     Q.a[k] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
+}
+
+// Every weight and scale a lane needs is loaded before the first is used: the empty asm in
+// head_weight_f16() keeps the scheduler from moving a later load above it, and loads
+// interleaved with the conversions would each wait out their own latency.
+__device__ __forceinline__ void load_idx_half(IdxHalf& Q, const uint8_t* __restrict__ q8,
+                                              const float* __restrict__ qs, const float* __restrict__ w,
+                                              int hh, float cmax) {
+  const int l = lane_id();
+  float wh[8], sh[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int h = 32 * hh + 16 * (e >> 2) + 4 * g + (e & 3);
-    Q.wa[e] = head_weight_f16(w[h], qs[h], inv);
+    wh[e] = w[slot_head(hh, e, l)];
+    sh[e] = qs[slot_head(hh, e, l)];
   }
+  load_idx_half_a(Q, q8, hh);
+  const float inv = cmax > 0.f ? 1.f / cmax : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) Q.wa[e] = head_weight_f16(wh[e], sh[e], inv);
 }
 
 // ReLU'd f16 B operand of the head-sum MFMA from the two FP8 MFMA results of a head half
@@ -132,11 +152,27 @@ struct IdxRow {
   float cmax;
 };
 
+// (all of the row's loads in flight at once, then the normaliser and the f16 weights)
 __device__ __forceinline__ void load_idx_row(IdxRow& R, const uint8_t* __restrict__ q8,
                                              const float* __restrict__ qs, const float* __restrict__ w) {
-  R.cmax = row_cmax(qs, w);
-  load_idx_half(R.h[0], q8, qs, w, 0, R.cmax);
-  load_idx_half(R.h[1], q8, qs, w, 1, R.cmax);
+  const int l = lane_id();
+  const float w_l = w[l], qs_l = qs[l];
+  float wh[2][8], sh[2][8];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      wh[hh][e] = w[slot_head(hh, e, l)];
+      sh[hh][e] = qs[slot_head(hh, e, l)];
+    }
+  load_idx_half_a(R.h[0], q8, 0);
+  load_idx_half_a(R.h[1], q8, 1);
+  R.cmax = row_cmax_of(w_l, qs_l);
+  const float inv = R.cmax > 0.f ? 1.f / R.cmax : 0.f;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) R.h[hh].wa[e] = head_weight_f16(wh[hh][e], sh[hh][e], inv);
 }
 
 // B operand of fragment f (keys 16f .. 16f+15) from a 64-key LDS tile stored as 64 rows of

@@ -270,25 +270,49 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     const uint16_t* qh = q + (qrow * MH + 32 * wv + (l & 31)) * ld_q + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < D_STEPS; ++ds) Qt[ds] = *reinterpret_cast<const v8bf*>(qh + 16 * ds);
-    // held in registers for the whole row (never re-read from memory)
-#pragma unroll
-    for (int ds = 0; ds < D_STEPS; ++ds) asm volatile("" : "+v"(Qt[ds]));
   }
 
-  // the row's selected ids -> LDS (pool rows for paged caches, invalid ids kept invalid);
-  // every wave then finds the last valid one, and the chunks run up to the one holding it
+  // the row's selected ids -> LDS (pool rows for paged caches, invalid ids kept invalid),
+  // their loads in flight together with the Q loads; the block's last valid id (the
+  // chunks run up to the one holding it) comes from the ids each thread staged
   const uint32_t nk_seq = (uint32_t)min(n_k, (int64_t)INT32_MAX);
   const uint32_t nk = pt.table ? (uint32_t)min(pt.n_pages * PAGE_ROWS, (int64_t)INT32_MAX) : nk_seq;
-  for (int j = tid; j < k; j += MLA_WAVES * 64) {
-    int32_t id = irow[j];
-    if (pt.table) id = (uint32_t)id < nk_seq ? (int32_t)paged_row(pt, b, id) : -1;
-    ids[j] = id;
+  constexpr int IDS_PER_THREAD = MAX_K / (MLA_WAVES * 64);
+  static_assert(MAX_K % (MLA_WAVES * 64) == 0, "the ids split evenly over the threads");
+  int32_t id[IDS_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < IDS_PER_THREAD; ++i) {
+    const int j = tid + i * MLA_WAVES * 64;
+    id[i] = j < k ? irow[j] : -1;
   }
-  __syncthreads();
+  if (pt.table) {  // every table lookup in flight at once (an invalid id looks up token 0)
+    int64_t prow[IDS_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < IDS_PER_THREAD; ++i) prow[i] = paged_row(pt, b, (uint32_t)id[i] < nk_seq ? id[i] : 0);
+#pragma unroll
+    for (int i = 0; i < IDS_PER_THREAD; ++i) id[i] = (uint32_t)id[i] < nk_seq ? (int32_t)prow[i] : -1;
+  }
   int last = -1;
-  for (int j = l; j < k; j += 64)
-    if ((uint32_t)ids[j] < nk) last = j;
-  last = __builtin_amdgcn_readfirstlane((int)wave_max((float)last));
+#pragma unroll
+  for (int i = 0; i < IDS_PER_THREAD; ++i) {
+    const int j = tid + i * MLA_WAVES * 64;
+    if (j < k) {
+      ids[j] = id[i];
+      if ((uint32_t)id[i] < nk) last = j;
+    }
+  }
+  // Q is held in registers for the whole row (never re-read from memory)
+#pragma unroll
+  for (int ds = 0; ds < D_STEPS; ++ds) asm volatile("" : "+v"(Qt[ds]));
+  // (exchanged through buffer 3, whose first chunk is gathered after the next barrier)
+  int32_t* wave_last = reinterpret_cast<int32_t*>(buf3);
+  last = (int)wave_max((float)last);
+  if (l == 0) wave_last[wv] = last;
+  __syncthreads();
+  last = wave_last[0];
+#pragma unroll
+  for (int w = 1; w < MLA_WAVES; ++w) last = max(last, wave_last[w]);
+  last = __builtin_amdgcn_readfirstlane(last);
   const int nchunks = (last + KC) / KC;
   const int c_lo = (int)((int64_t)nchunks * split / n_split);
   const int c_hi = (int)((int64_t)nchunks * (split + 1) / n_split);
