@@ -55,10 +55,18 @@ struct PageTable {
   int64_t ld = 0;       // entries between the tables of consecutive sequences
   int64_t n_pages = 0;  // pages in the pool
 };
-__device__ __forceinline__ int64_t paged_row(const PageTable& pt, int b, int64_t j) {
-  int64_t p = pt.table[(int64_t)b * pt.ld + (j >> 6)];
+// The table entry of the page holding token j of sequence b, as stored, and the pool row of
+// token j given that entry (clamped into the pool).  Split so that a kernel can load an entry
+// early and use it later.
+__device__ __forceinline__ int32_t page_entry(const PageTable& pt, int b, int64_t j) {
+  return pt.table[(int64_t)b * pt.ld + (j >> 6)];
+}
+__device__ __forceinline__ int64_t page_entry_row(const PageTable& pt, int64_t p, int64_t j) {
   p = p < 0 ? 0 : p >= pt.n_pages ? pt.n_pages - 1 : p;
   return p * PAGE_ROWS + (j & (PAGE_ROWS - 1));
+}
+__device__ __forceinline__ int64_t paged_row(const PageTable& pt, int b, int64_t j) {
+  return page_entry_row(pt, page_entry(pt, b, j), j);
 }
 // A 64-key tile of consecutive tokens starting at key0 (a multiple of 64) whose keys are
 // clamped to `last`: every key it reads lies on one page, found with one table lookup.

@@ -108,6 +108,19 @@ __device__ __forceinline__ int64_t split_tile_row(const PageTable& pt, int b, in
   if constexpr (!PAGED) return 0;
   else return stride == 1 ? paged_row(pt, b, key0) : 0;
 }
+// The same in two steps: the table entry of the tile at key0 (clamped to the last key, so the
+// load stays inside the table whatever key0 is), and later the tile's first pool row from it.
+template <bool PAGED>
+__device__ __forceinline__ int32_t split_tile_entry(const PageTable& pt, int b, int64_t key0, int64_t n_keys,
+                                                    int stride) {
+  if constexpr (!PAGED) return 0;
+  else return stride == 1 ? page_entry(pt, b, key0 < n_keys ? key0 : n_keys - 1) : 0;
+}
+template <bool PAGED>
+__device__ __forceinline__ int64_t split_entry_row(const PageTable& pt, int32_t entry, int64_t key0, int stride) {
+  if constexpr (!PAGED) return 0;
+  else return stride == 1 ? page_entry_row(pt, entry, key0) : 0;
+}
 
 // grid: x = key splits of SPLIT_TILES tiles, y = row, z = sequence.
 // Store mode: the row's scores of keys 0, S, 2S, ... (S = key_stride) go to columns 0, 1,
@@ -124,7 +137,7 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, const float* __restrict__ w, int64_t n_q, int64_t n_k, int64_t kbs,
     const int32_t* __restrict__ q_pos, int64_t pos_offset, int64_t row_begin, int64_t n_rows,
-    float* __restrict__ scores, int64_t ld, int key_stride, const float* __restrict__ thr,
+    float* __restrict__ scores, int64_t ld, int key_stride_arg, const float* __restrict__ thr,
     uint2* __restrict__ cand, uint32_t* __restrict__ cnt, const uint8_t* __restrict__ redo, PageTable pt) {
   const int b = blockIdx.z;
   const int64_t i = blockIdx.y;
@@ -136,6 +149,10 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
   const int64_t qrow = (int64_t)b * n_q + row;
   float* srow = scores + rid * ld;
   const int64_t t0 = (int64_t)blockIdx.x * SPLIT_TILES;
+  // the filter always runs over every key: a compile-time stride of 1 leaves one load path
+  // in its loop (with the strided path beside it the compiler drains every tile's loads
+  // before the previous tile is scored, which defeats the read-ahead)
+  const int key_stride = FILTER ? 1 : key_stride_arg;
   // launch keys: key j is cache row j * key_stride; the row sees those at or below pos
   const int64_t n_keys = (n_k + key_stride - 1) / key_stride;
   int64_t lim = pos < n_k - 1 ? pos : n_k - 1;
@@ -152,24 +169,41 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     }
   }
   // visible tiles of this wave: t0 + wv, t0 + wv + 4, ...; each tile's key fragments are
-  // loaded one tile ahead, while the previous tile is scored
+  // loaded one tile ahead, while the previous tile is scored.  The two tiles in flight live
+  // in two register buffers used in turn (the loop is unrolled by two): copying a tile's
+  // registers from one buffer to the other would make the wave wait for its loads at the
+  // copy, which is what the read-ahead exists to avoid.
   int64_t t = t0 + wv;
   const int64_t seg = rid * (4 * (int64_t)gridDim.x) + 4 * blockIdx.x + wv;
   if (t >= t_vis) {
     if (FILTER && lane == 0) cnt[seg] = 0u;
     return;
   }
-  // the first tile's loads go out before the query row's, so both are in flight at once
-  v8i bf[4];
-  float ksc;
-  {
-    const int64_t key0 = t * KEY_TILE, key = key0 + lane;
-    const int64_t row0 = split_tile_row<PAGED>(pt, b, key0, key_stride);
+  struct TileBuf {
+    v8i b[4];
+    float ks;
+  };
+  // paged, stride 1: the page entries of the tiles to be loaded, also two in turn; a tile's
+  // entry is loaded one step before its fragments, ahead of that step's loads, so that no
+  // load waits for a lookup (the memory counter drains in order)
+  auto load_tile = [&](TileBuf& B, int64_t tile, int32_t entry) {
+    const int64_t key0 = tile * KEY_TILE, key = key0 + lane;
+    const int64_t row0 = split_entry_row<PAGED>(pt, entry, key0, key_stride);
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      bf[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride, row0);
-    ksc = split_key_scale<PAGED>(ks, pt, b, kbs, key, key0, n_keys, key_stride, row0);
-  }
+    for (int f = 0; f < 4; ++f) B.b[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride, row0);
+    B.ks = split_key_scale<PAGED>(ks, pt, b, kbs, key, key0, n_keys, key_stride, row0);
+  };
+  // Every step issues the same loads: past the last visible tile the next tile is the last
+  // one again (a re-read from cache, never scored).  With the loads conditional, the compiler
+  // sizes each wait for the path that issued none and so waits for the tile just issued.
+  auto clamp_tile = [&](int64_t x) { return x < t_vis ? x : t_vis - 1; };
+  auto entry_of = [&](int64_t x) {
+    return split_tile_entry<PAGED>(pt, b, clamp_tile(x) * KEY_TILE, n_keys, key_stride);
+  };
+  // the first tile's loads go out before the query row's, so both are in flight at once
+  TileBuf A, B;
+  load_tile(A, t, entry_of(t));
+  int32_t e0 = 0, e1 = entry_of(t + 4);
   IdxRow Q;
   load_idx_row(Q, q8 + qrow * IDX_HEADS * IDX_DIM, qs + qrow * IDX_HEADS, w + qrow * IDX_HEADS);
   float T = 0.f;
@@ -179,20 +213,13 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     T = thr[rid];
     crow = cand + seg * DEC_SEG;
   }
-  for (; t < t_vis; t += 4) {
-    const int64_t tn = t + 4;
-    v8i bn[4] = {bf[0], bf[1], bf[2], bf[3]};
-    float kn = ksc;
-    if (tn < t_vis) {
-      const int64_t key0 = tn * KEY_TILE, key = key0 + lane;
-      const int64_t row0 = split_tile_row<PAGED>(pt, b, key0, key_stride);
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-        bn[f] = split_key_fragment<PAGED>(k8, pt, b, kbs, key0, f, n_keys, key_stride, row0);
-      kn = split_key_scale<PAGED>(ks, pt, b, kbs, key, key0, n_keys, key_stride, row0);
-    }
-    const int64_t key = t * KEY_TILE + lane;
-    const float sc = score_tile64(Q, bf, ksc);
+  // the query's operands have landed before the loop: otherwise the compiler, merging the
+  // loop's entry with its back edge, takes them as still in flight in every iteration and
+  // makes each tile's first MFMAs wait for the loads issued just before them
+  idx_row_landed(Q);
+  auto score = [&](const TileBuf& C, int64_t tile) {
+    const int64_t key = tile * KEY_TILE + lane;
+    const float sc = score_tile64(Q, C.b, C.ks);
     if (FILTER) {
       const bool pass = key < n_vis && sc > T;
       const uint64_t m = ballot(pass);
@@ -202,9 +229,18 @@ __global__ __launch_bounds__(256) void idx_scores_fp8_split(
     } else if (key < n_keys) {
       srow[key] = key < n_vis ? sc : -INFINITY;
     }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) bf[f] = bn[f];
-    ksc = kn;
+  };
+  for (;;) {
+    e0 = entry_of(t + 8);
+    load_tile(B, clamp_tile(t + 4), e1);
+    score(A, t);
+    t += 4;
+    if (t >= t_vis) break;
+    e1 = entry_of(t + 8);
+    load_tile(A, clamp_tile(t + 4), e0);
+    score(B, t);
+    t += 4;
+    if (t >= t_vis) break;
   }
   if (FILTER && lane == 0) cnt[seg] = ccount;
 }

@@ -175,6 +175,14 @@ __device__ __forceinline__ void load_idx_row(IdxRow& R, const uint8_t* __restric
     for (int e = 0; e < 8; ++e) R.h[hh].wa[e] = head_weight_f16(wh[hh][e], sh[hh][e], inv);
 }
 
+// Waits (here, once) until a query row's operand loads have landed.
+__device__ __forceinline__ void idx_row_landed(IdxRow& R) {
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) asm volatile("" : "+v"(R.h[hh].a[k]));
+}
+
 // B operand of fragment f (keys 16f .. 16f+15) from a 64-key LDS tile stored as 64 rows of
 // 128 bytes whose 16-byte units are XOR-swizzled by (row & 7).
 __device__ __forceinline__ v8i lds_key_fragment(const uint8_t* tile, int f) {

@@ -401,6 +401,7 @@ __device__ void write_from_candidates(const uint32_t* ckey, Pos pos, uint32_t nc
 // recomputed by the streaming exact selection, so the result never depends on the sample.
 // ---------------------------------------------------------------------------------------
 constexpr int TH_THREADS = 256;
+constexpr int LOAD_BATCH = 8;  // loads per thread in flight while a list is staged in LDS
 constexpr int TH_MAX = (int)(TOPK_MAX_N / SEL_SAMPLE_STRIDE);
 
 // The row's sample keys live in dynamic LDS of ceil(n_k / SEL_SAMPLE_STRIDE) words (16 KB at
@@ -431,7 +432,20 @@ __global__ __launch_bounds__(NT) void sel_threshold_kernel(const float* __restri
   int r = (int)ceilf(m + 5.f * sqrtf(m) + 5.f);
   r = r < ns ? r : ns;
   const float* srow = samp + ((int64_t)b * rows_pad + i) * ld_s;
-  for (int j = tid; j < ns; j += NT) keys[j] = score_key(srow[j]);
+  // the samples -> LDS, LOAD_BATCH loads per thread in flight before any is stored
+  for (int j0 = 0; j0 < ns; j0 += LOAD_BATCH * NT) {
+    float v[LOAD_BATCH];
+#pragma unroll
+    for (int q = 0; q < LOAD_BATCH; ++q) {
+      const int j = j0 + q * NT + tid;
+      v[q] = j < ns ? srow[j] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < LOAD_BATCH; ++q) {
+      const int j = j0 + q * NT + tid;
+      if (j < ns) keys[j] = score_key(v[q]);
+    }
+  }
   __syncthreads();
   uint32_t rem;
   const uint32_t T = select_lds<NT>(keys, ns, (uint32_t)r, hist, wtot, &s_digit, &s_above, rem);
@@ -470,11 +484,23 @@ __global__ __launch_bounds__(TO_THREADS) void sel_candidates_kernel(
     if (tid == 0) redo[orow] = 1;
     return;
   }
+  // the list -> LDS, every load of a thread in flight before any is stored
   const uint2* cr = cand + r * SEL_CAND_PITCH;
-  for (uint32_t j = tid; j < c; j += TO_THREADS) {
-    const uint2 e = cr[j];
-    ckey[j] = score_key(__uint_as_float(e.x));
-    cidx[j] = (int32_t)e.y;
+  constexpr int PER = SEL_CAND_CAP / TO_THREADS;
+  static_assert(SEL_CAND_CAP % TO_THREADS == 0, "the list splits evenly over the threads");
+  uint2 e[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const uint32_t j = (uint32_t)(q * TO_THREADS + tid);
+    e[q] = j < c ? cr[j] : make_uint2(0u, 0u);
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const uint32_t j = (uint32_t)(q * TO_THREADS + tid);
+    if (j < c) {
+      ckey[j] = score_key(__uint_as_float(e[q].x));
+      cidx[j] = (int32_t)e[q].y;
+    }
   }
   __syncthreads();
   uint32_t rem;
@@ -531,15 +557,27 @@ __global__ __launch_bounds__(DC_THREADS) void dec_cand_topk_kernel(
     if (tid == 0) redo[rid] = 1;
     return;
   }
+  // the segments -> LDS, packed; LOAD_BATCH loads per thread in flight before any is stored
   const uint2* cr = cand + rid * n_segs * DEC_SEG;
-  for (int64_t sgi = tid / DEC_SEG; sgi < n_segs; sgi += DC_THREADS / DEC_SEG) {
-    const uint32_t j = (uint32_t)(tid % DEC_SEG);
-    const uint32_t o = soff[sgi];
-    if (j < soff[sgi + 1] - o) {
-      const uint2 e = cr[sgi * DEC_SEG + j];
-      ckey[o + j] = score_key(__uint_as_float(e.x));
-      cpos[o + j] = (int32_t)e.y;
+  constexpr int SEG_STEP = DC_THREADS / DEC_SEG;
+  const uint32_t j = (uint32_t)(tid % DEC_SEG);
+  for (int64_t sg0 = tid / DEC_SEG; sg0 < n_segs; sg0 += (int64_t)LOAD_BATCH * SEG_STEP) {
+    uint2 e[LOAD_BATCH];
+    uint32_t o[LOAD_BATCH];
+    bool have[LOAD_BATCH];
+#pragma unroll
+    for (int q = 0; q < LOAD_BATCH; ++q) {
+      const int64_t sgi = sg0 + (int64_t)q * SEG_STEP;
+      o[q] = sgi < n_segs ? soff[sgi] : 0u;
+      have[q] = sgi < n_segs && j < soff[sgi + 1] - o[q];
+      e[q] = have[q] ? cr[sgi * DEC_SEG + j] : make_uint2(0u, 0u);
     }
+#pragma unroll
+    for (int q = 0; q < LOAD_BATCH; ++q)
+      if (have[q]) {
+        ckey[o[q] + j] = score_key(__uint_as_float(e[q].x));
+        cpos[o[q] + j] = (int32_t)e[q].y;
+      }
   }
   const int64_t nw = (n + 31) / 32;
   for (int64_t j = tid; j < nw; j += DC_THREADS) {
