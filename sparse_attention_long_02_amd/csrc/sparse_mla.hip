@@ -473,42 +473,53 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
   }
 }
 
-// merge the splits of one (query, head): O = sum_s e^{lse_s - lse} O_s
+// merge the NS splits of one (query, head): O = sum_s e^{lse_s - lse} O_s.  NS is a template
+// argument so that every load is unconditional (a load on one path only makes the compiler
+// copy its result between registers, and the copy waits for the load).
+constexpr int MLA_MAX_SPLIT = 16;
+template <int NS>
 __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse, int n_split,
-                                                          int H, int d_v, uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse) {
-  constexpr int MAX_SPLIT = 16, PER = MDV / 128;  // the bf16 path: d_v = 512
+                                                          const float* __restrict__ part_lse, int H, int d_v,
+                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int PER = MDV / 128;  // the bf16 path: d_v = 512
+  static_assert(PER == 4, "a thread merges four adjacent values");
   const int64_t qh = blockIdx.x;  // qrow * H + head
-  const int64_t qrow = qh / H;
-  const int head = (int)(qh % H);
-  // the splits' weights first, then every partial value this thread needs, all loads issued
-  // before any is used
-  float ls[MAX_SPLIT];
+  const int64_t qrow = blockIdx.x / (uint32_t)H;
+  const int head = (int)(blockIdx.x % (uint32_t)H);
+  // every partial value this thread needs (values 4t .. 4t+3 of each split, one 16-byte load
+  // per split) and the splits' weights, all loads issued before any is used
+  v4f po[NS];
 #pragma unroll
-  for (int s = 0; s < MAX_SPLIT; ++s) ls[s] = s < n_split ? part_lse[(qrow * n_split + s) * H + head] : -INFINITY;
-  float po[MAX_SPLIT][PER];
+  for (int s = 0; s < NS; ++s)
+    po[s] = *reinterpret_cast<const v4f*>(part_o + ((qrow * NS + s) * H + head) * d_v + PER * threadIdx.x);
+  float ls[NS];
 #pragma unroll
-  for (int s = 0; s < MAX_SPLIT; ++s)
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      po[s][j] = s < n_split ? part_o[((qrow * n_split + s) * H + head) * d_v + threadIdx.x + 128 * j] : 0.f;
+  for (int s = 0; s < NS; ++s) ls[s] = part_lse[(qrow * NS + s) * H + head];
   float mx = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < MAX_SPLIT; ++s) mx = fmaxf(mx, ls[s]);
+  for (int s = 0; s < NS; ++s) mx = fmaxf(mx, ls[s]);
   float den = 0.f, acc[PER] = {};
 #pragma unroll
-  for (int s = 0; s < MAX_SPLIT; ++s) {
-    const float wgt = (s < n_split && mx != -INFINITY) ? exp2f((ls[s] - mx) * LOG2E) : 0.f;
+  for (int s = 0; s < NS; ++s) {
+    const float wgt = mx != -INFINITY ? exp2f((ls[s] - mx) * LOG2E) : 0.f;
     den += wgt;
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] += wgt * po[s][j];
   }
+  uint16_t o[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    out[qh * d_v + threadIdx.x + 128 * j] = f32_to_bf16_bits(den > 0.f ? acc[j] / den : 0.f);
+  for (int j = 0; j < PER; ++j) o[j] = f32_to_bf16_bits(den > 0.f ? acc[j] / den : 0.f);
+  *reinterpret_cast<uint2*>(out + qh * d_v + PER * threadIdx.x) =
+      make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
   if (lse && threadIdx.x == 0) lse[qh] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
+
+template <int... NS>
+struct CombineTable {
+  static constexpr decltype(&mla_combine_kernel<2>) fn[] = {mla_combine_kernel<NS>...};
+};
+using Combines = CombineTable<2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>;
+static_assert(MLA_MAX_SPLIT == 16, "one combine instantiation per split count 2 .. MLA_MAX_SPLIT");
 
 // fp32 attention (any H, d_qk, d_v <= 256, k <= 4096): one wave per (query, head),
 // exact two-pass softmax over the selected keys.
@@ -565,7 +576,7 @@ int sparse_mla_splits(int64_t B, int64_t n_q, int32_t k, int32_t dtype) {
   const int64_t chunks = (k + KC - 1) / KC;
   int64_t s = (256 + blocks - 1) / blocks;
   if (s > chunks / 4) s = chunks / 4;  // at least 4 chunks per split
-  if (s > 16) s = 16;
+  if (s > MLA_MAX_SPLIT) s = MLA_MAX_SPLIT;
   return s < 1 ? 1 : (int)s;
 }
 
@@ -601,8 +612,8 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
                      (const uint16_t*)a.kv, a.idx, a.n_q, a.n_k, ld_q, ld_kv, bs_kv, a.k, a.sm_scale * LOG2E, s,
                      (uint16_t*)a.out, a.lse, part_o, part_lse, a.pages);
   if (s > 1)
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(a.B * a.n_q * a.H)), dim3(128), 0, st, part_o,
-                       part_lse, s, a.H, a.d_v, (uint16_t*)a.out, a.lse);
+    hipLaunchKernelGGL(Combines::fn[s - 2], dim3((unsigned)(a.B * a.n_q * a.H)), dim3(128), 0, st, part_o,
+                       part_lse, a.H, a.d_v, (uint16_t*)a.out, a.lse);
   return hipGetLastError();
 }
 
