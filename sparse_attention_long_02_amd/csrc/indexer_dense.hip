@@ -249,6 +249,7 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
     float v[4];
     // each fragment's B operand is read from LDS one fragment ahead
     v8i bnext = dense_fragment(tile, 0, lane);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const v8i bf = bnext;
@@ -267,6 +268,7 @@ __global__ __launch_bounds__(DN_WAVES * 64, 2) void idx_dense_fp8_kernel(
       if constexpr (FILTER)
         if (f == 0) append_tile(psc, phit, (uint32_t)(4 * c + (t - 1) * KEY_TILE));
     }
+    __builtin_amdgcn_s_setprio(0);
     typedef __attribute__((address_space(3))) const v4f lds_v4f;
     const v4f kscale = *(lds_v4f*)((__attribute__((address_space(3))) const uint8_t*)tile + DN_TILE_BYTES + 16 * c);
     const int64_t key = (int64_t)t * KEY_TILE + 4 * c;
