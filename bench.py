@@ -423,8 +423,9 @@ def main():
     f_bwd = kept * cfg.H * 2 * (3 * cfg.d_qk + 2 * cfg.d_v)
     stages["sparse_mla_backward"] = {
         "ms": t_bwd * 1e3, "bf16_flop": f_bwd, "mfma_frac": f_bwd / t_bwd / PEAK_BF16,
-        "gather_bytes": g_bytes, "dkv_atomic_bytes": kept * cfg.d_qk * 4,
-        "note": "dq and dkv (fp32 atomics) of the step's attention for seeded output gradients"}
+        "gather_bytes": g_bytes, "dkv_contribution_bytes": kept * cfg.d_qk * 4,
+        "note": "dq and dkv of the step's attention for seeded output gradients; dkv from fp32 "
+                "per-pair contribution rows (written once, read once) summed per key"}
     log(f"[bench] sparse MLA backward: {t_bwd * 1e3:.3f} ms ({f_bwd / t_bwd / 1e12:.0f} TFLOP/s bf16)")
     del dout, ws_b
     torch.cuda.empty_cache()

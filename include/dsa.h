@@ -183,7 +183,10 @@ int dsa_sparse_mla(const void* q, int64_t ld_q, const void* kv, int64_t ld_kv, c
  * dtype DSA_BF16 (H = 128, d_qk = 576, d_v = 512, V inside kv, k a multiple of 32 up to
  * 2048) or DSA_F32 (small shapes).  Workspace: dsa_workspace_size(DSA_OP_MLA_BWD, B, n_q,
  * n_k, H, d_v, k, dtype) (bf16: the transposed q and dO and the bf16 P and dZ of up to
- * 4096 queries at a time).  Order of the dkv sums is not fixed (atomics): d_kv is
+ * 4096 queries at a time, then for up to 2048 queries at a time the fp32 d_kv
+ * contributions of every (query, selected key) pair (k * 576 * 4 bytes per query), those
+ * pairs' lists by key and the lists' offsets over the keys of the sequences those queries
+ * belong to).  The order in which a key's contributions are summed is not fixed: d_kv is
  * reproducible to rounding, not bit for bit.
  */
 int dsa_sparse_mla_backward(const void* q, const void* kv, const void* v, const int32_t* idx,

@@ -287,7 +287,7 @@ size_t dsa_workspace_size(int32_t op, int64_t B, int64_t n_q, int64_t n_k, int32
       return dec_sel_bytes(B, n_k, dtype == DSA_BF16 ? DSA_FP8_E4M3 : DSA_F32) +
              dsa::sparse_mla_ws_bytes(B, 1, H, d_v, k, dtype);
     case DSA_OP_MLA_BWD:
-      return dsa::sparse_mla_bwd_ws_bytes(B, n_q, k, dtype);
+      return dsa::sparse_mla_bwd_ws_bytes(B, n_q, n_k, k, dtype);
     case DSA_OP_CHUNK:
       return chunk_scores_bytes(B, n_q, n_k, dtype) + dsa::sparse_mla_ws_bytes(B, n_q, H, d_v, k, dtype);
     case DSA_OP_KL_DENSE:
@@ -855,7 +855,7 @@ int dsa_sparse_mla_backward(const void* q, const void* kv, const void* v, const 
     REQUIRE(aligned16(q) && aligned16(kv) && aligned16(out) && aligned16(d_out) && aligned16(d_q) &&
                 aligned16(idx) && aligned16(d_kv),
             "bf16 backward operands must be 16-byte aligned");
-    const size_t need = dsa::sparse_mla_bwd_ws_bytes(B, n_q, k, dtype);
+    const size_t need = dsa::sparse_mla_bwd_ws_bytes(B, n_q, n_k, k, dtype);
     if (!ws || ws_bytes < need)
       return fail(DSA_ERR_WORKSPACE, "dsa_sparse_mla_backward needs %zu workspace bytes (got %zu)", need, ws_bytes);
     REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");

@@ -282,7 +282,7 @@ struct MlaBwdArgs {
   void* ws;
 };
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, hipStream_t st);
-size_t sparse_mla_bwd_ws_bytes(int64_t B, int64_t n_q, int32_t k, int32_t dtype);
+size_t sparse_mla_bwd_ws_bytes(int64_t B, int64_t n_q, int64_t n_k, int32_t k, int32_t dtype);
 
 // index scores at the keys listed in idx [B, n_q, k] (-inf for ids outside [0, n_k))
 struct ScoresAtArgs {

@@ -20,25 +20,54 @@
 //      operand), then P and dZ on the VALU, and accumulates dq^T += K^T dZ^T (K^T by
 //      transposing LDS reads; each lane's dZ values are already the B operand).  P and dZ
 //      go to the workspace in bf16 ([query][slot][head]);
-//   3. mla_bwd_dkv_kernel: one block of 4 waves per query; wave w owns the 32-column output
-//      tiles w, w+4, .. of the 576; per chunk it contracts over all 128 heads (dZ^T q and
-//      P^T dO, 32x32x16 MFMAs) and adds each value to dkv with a hardware fp32 atomic.
+//   3. dkv, in sub-passes of at most DKV_ROWS queries, without atomics on the rows:
+//      a. the (query, slot) pairs of the sub-pass are grouped by key id on the GPU (a CSR:
+//         per-key counts, an exclusive scan, then each pair's position in its key's list);
+//      b. mla_bwd_dkv_kernel: one block of 4 waves per query; wave w owns the 32-column
+//         output tiles w, w+4, .. of the 576; per chunk it contracts over all 128 heads
+//         (dZ^T q and P^T dO, 32x32x16 MFMAs) and stores each selected key's fp32 row of
+//         contributions (576 values) to the workspace, at the pair's (query, slot) place;
+//      c. mla_bwd_dkv_reduce: one wave per key sums the rows its list names and adds the
+//         sum to dkv (the only writer of that row in the sub-pass).
+//      The contributions are the same fp32 values the per-pair atomic adds carried before;
+//      only the order of the additions differs (the atomics' order was not fixed either).
 #include "dsa_kernels.h"
 #include "mla_gather.h"
 
 namespace dsa {
 
 constexpr int BWD_ROWS = 4096;  // queries per pass (bounds the workspace)
+constexpr int DKV_ROWS = 2048;  // queries per dkv sub-pass (bounds the contribution rows)
 
 // bf16 workspace elements per query of a pass: q^T and dO^T, then P and dZ per slot
 __host__ __device__ constexpr int64_t bwd_ws_elems_per_row(int k) {
   return (int64_t)MDQK * MH + (int64_t)MDV * MH + 2 * (int64_t)k * MH;
 }
 
-size_t sparse_mla_bwd_ws_bytes(int64_t B, int64_t n_q, int32_t k, int32_t dtype) {
-  if (dtype != DSA_BF16) return 0;
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the bf16 path, in order: the pass's q^T, dO^T, P and dZ (bf16); the dkv
+// sub-pass's fp32 contribution rows [rows][k][576], its pair lists [rows * k] (int32) and
+// the per-key list offsets [keys + 1] (uint32) over the sequences a sub-pass can span.
+struct BwdWs {
+  size_t contrib, perm, off, total;
+};
+static BwdWs bwd_ws_layout(int64_t B, int64_t n_q, int64_t n_k, int32_t k) {
   const int64_t rows = B * n_q < BWD_ROWS ? B * n_q : BWD_ROWS;
-  return (size_t)rows * bwd_ws_elems_per_row(k) * sizeof(uint16_t);
+  const int64_t rs = rows < DKV_ROWS ? rows : DKV_ROWS;
+  int64_t seqs = (rs + n_q - 1) / n_q + 1;
+  seqs = seqs < B ? seqs : B;
+  BwdWs w;
+  w.contrib = align256((size_t)rows * bwd_ws_elems_per_row(k) * sizeof(uint16_t));
+  w.perm = w.contrib + align256((size_t)rs * k * MDQK * sizeof(float));
+  w.off = w.perm + align256((size_t)rs * k * sizeof(int32_t));
+  w.total = w.off + align256((size_t)(seqs * n_k + 1) * sizeof(uint32_t));
+  return w;
+}
+
+size_t sparse_mla_bwd_ws_bytes(int64_t B, int64_t n_q, int64_t n_k, int32_t k, int32_t dtype) {
+  if (dtype != DSA_BF16) return 0;
+  return bwd_ws_layout(B, n_q, n_k, k).total;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -314,18 +343,73 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void mla_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// 3. dkv by atomics
+// 3. dkv: pair lists by key, contribution rows, per-key sums
 // ---------------------------------------------------------------------------------------
 constexpr int DKV_WAVES = 4;
 constexpr int DKV_TILES = MDQK / 32;  // 18 column tiles; tiles < 16 also take the V part
 constexpr int DKV_MAXT = (DKV_TILES + DKV_WAVES - 1) / DKV_WAVES;  // 5
 
-// grid.x = rows of the pass, 256 threads; wave w owns column tiles w, w+4, .., < 18 (one
-// wave per SIMD: its q^T and dO^T operands take up to 288 registers).
+// 3a. Pair lists.  Row r of the sub-pass is query g0 + r (sequence b = (g0 + r) / n_q); its
+// valid slot j names key b * n_k + idx - kbase of the sub-pass's key range.  Count: one
+// atomic increment of that key's counter per pair.  Fill (after the scan turned the counters
+// into list starts): each pair takes the next place of its key's list, which leaves off[key]
+// at the start of the next key's list, i.e. at the end of its own.
+template <bool FILL>
+__global__ __launch_bounds__(256) void mla_bwd_pairs(const int32_t* __restrict__ idx, int64_t n_q, int64_t n_k,
+                                                     int k, int64_t g0, int64_t kbase, uint32_t* __restrict__ off,
+                                                     int32_t* __restrict__ perm) {
+  const int64_t r = blockIdx.x;
+  const int64_t g = g0 + r;
+  const int64_t kb = (g / n_q) * n_k - kbase;
+  const int32_t* irow = idx + g * k;
+  for (int j = threadIdx.x; j < k; j += 256) {
+    const int32_t id = irow[j];
+    if (id < 0 || (int64_t)id >= n_k) continue;
+    if constexpr (FILL) perm[atomicAdd(&off[kb + id], 1u)] = (int32_t)(r * k + j);
+    else atomicAdd(&off[kb + id], 1u);
+  }
+}
+
+// 3a. Exclusive prefix sum of off[0 .. n) in place, one block of 1024 threads, 4096 entries
+// per step (4 consecutive per thread), the running total carried between steps.
+__global__ __launch_bounds__(1024) void mla_bwd_scan(uint32_t* __restrict__ off, int64_t n) {
+  __shared__ uint32_t wtot[16];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  uint32_t carry = 0;
+  for (int64_t base = 0; base < n; base += 4096) {
+    const int64_t i0 = base + 4 * tid;
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = i0 + e < n ? off[i0 + e] : 0u;
+    const uint32_t own = v[0] + v[1] + v[2] + v[3];
+    const uint32_t incl = wave_incl_scan(own);
+    if (lane == WAVE - 1) wtot[wv] = incl;
+    __syncthreads();
+    uint32_t before = carry, step = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t t = wtot[i];
+      before += i < wv ? t : 0u;
+      step += t;
+    }
+    __syncthreads();
+    uint32_t run = before + incl - own;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i0 + e < n) off[i0 + e] = run;
+      run += v[e];
+    }
+    carry += step;
+  }
+}
+
+// 3b. grid.x = rows of the sub-pass, 256 threads; wave w owns column tiles w, w+4, .., < 18
+// (one wave per SIMD: its q^T and dO^T operands take up to 288 registers).  The fp32
+// contributions of row gl's slot j go to contrib[(gl * k + j) * 576 ..] (valid slots only).
 __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
     const uint16_t* __restrict__ qT, const uint16_t* __restrict__ doT, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ wsp, const uint16_t* __restrict__ wsz, int64_t n_q, int64_t n_k, int k,
-    int64_t g0, float* __restrict__ dkv) {
+    int64_t g0, float* __restrict__ contrib) {
   __shared__ __align__(16) uint16_t pz[2][2][KC][MH];  // [buffer][P, dZ][slot][head]
   __shared__ int32_t sid[2][KC];
 
@@ -333,7 +417,6 @@ __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t gl = xcd_contiguous(blockIdx.x, gridDim.x);
   const int64_t g = g0 + gl;
-  const int64_t b = g / n_q;
   const int32_t* irow = idx + g * k;
   const int n = bwd_chunks(irow, k, n_k, l);
   if (n == 0) return;  // uniform over the block
@@ -355,7 +438,7 @@ __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
 
   const uint16_t* prow = wsp + gl * (int64_t)k * MH;
   const uint16_t* zrow = wsz + gl * (int64_t)k * MH;
-  float* dkvb = dkv + b * n_k * MDQK;
+  float* crow = contrib + gl * (int64_t)k * MDQK;
   // chunk staging: thread t moves 64 bytes (32 heads) of P (t < 128) or dZ: slot (t%128)/4,
   // heads 32 (t%4) .. +31; the next chunk is loaded into registers while this one is used
   const int which = tid >> 7, u = tid & 127, srow = u >> 2, hcol = 32 * (u & 3);
@@ -395,17 +478,67 @@ __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
           acc = mfma_bf16_32x32x16(ap, Dt[t][s], acc);
         }
       }
-      // lane: column 32j + l%32, rows (slots) 8(r/4) + 4G + r%4; 32-bit element offsets
-      // from the sequence's base (n_k * 576 < 2^32, checked by the entry point)
-      const uint32_t col = 32 * j + (l & 31);
+      // lane: column 32j + l%32, rows (slots) 8(r/4) + 4G + r%4 of chunk c; each store
+      // instruction writes two 128-byte runs (one slot per half-wave)
+      const int col = 32 * j + (l & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int32_t id = sid[bi][8 * (r >> 2) + 4 * G + (r & 3)];
-        if (id >= 0 && (int64_t)id < n_k) unsafeAtomicAdd(dkvb + ((uint32_t)id * MDQK + col), acc[r]);
+        const int slot = 8 * (r >> 2) + 4 * G + (r & 3);
+        const int32_t id = sid[bi][slot];
+        if (id >= 0 && (int64_t)id < n_k) crow[(int64_t)(c * KC + slot) * MDQK + col] = acc[r];
       }
     }
     if (c + 1 < n) stage_store(bi ^ 1);
   }
+}
+
+// 3c. One wave per key of the sub-pass's range (4 per block): the sum of the contribution
+// rows its list names, added to dkv[kbase + key].  Lane l holds values 4l .. 4l+3,
+// 256 + 4l .. +3 and, for l < 16, 512 + 4l .. +3 of the 576; four rows are loaded at once.
+__global__ __launch_bounds__(256) void mla_bwd_dkv_reduce(const float* __restrict__ contrib,
+                                                          const int32_t* __restrict__ perm,
+                                                          const uint32_t* __restrict__ off, int64_t n_keys,
+                                                          int64_t kbase, float* __restrict__ dkv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t key = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (key >= n_keys) return;
+  const uint32_t lo = key ? off[key - 1] : 0u, hi = off[key];
+  if (lo == hi) return;
+  const bool third = lane < 16;
+  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+  for (uint32_t e0 = lo; e0 < hi; e0 += WAVE) {
+    const uint32_t m = hi - e0 < (uint32_t)WAVE ? hi - e0 : (uint32_t)WAVE;
+    const int32_t pl = (uint32_t)lane < m ? perm[e0 + lane] : 0;
+    uint32_t j = 0;
+    for (; j + 4 <= m; j += 4) {
+      v4f x0[4], x1[4], x2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t p = __builtin_amdgcn_readlane(pl, (int)(j + u));
+        const v4f* row = reinterpret_cast<const v4f*>(contrib + p * MDQK);
+        x0[u] = row[lane];
+        x1[u] = row[64 + lane];
+        x2[u] = third ? row[128 + lane] : v4f{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a0 += x0[u];
+        a1 += x1[u];
+        a2 += x2[u];
+      }
+    }
+    for (; j < m; ++j) {
+      const int64_t p = __builtin_amdgcn_readlane(pl, (int)j);
+      const v4f* row = reinterpret_cast<const v4f*>(contrib + p * MDQK);
+      a0 += row[lane];
+      a1 += row[64 + lane];
+      if (third) a2 += row[128 + lane];
+    }
+  }
+  v4f* d = reinterpret_cast<v4f*>(dkv + (kbase + key) * MDQK);
+  d[lane] += a0;
+  d[64 + lane] += a1;
+  if (third) d[128 + lane] += a2;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_f32(float* __restrict__ x, int64_t n) {
@@ -479,6 +612,10 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   uint16_t* ws = (uint16_t*)a.ws;
+  const BwdWs wl = bwd_ws_layout(a.B, a.n_q, a.n_k, a.k);
+  float* contrib = (float*)((char*)a.ws + wl.contrib);
+  int32_t* perm = (int32_t*)((char*)a.ws + wl.perm);
+  uint32_t* off = (uint32_t*)((char*)a.ws + wl.off);
   for (int64_t g0 = 0; g0 < rows; g0 += BWD_ROWS) {
     const int64_t R = rows - g0 < BWD_ROWS ? rows - g0 : BWD_ROWS;
     uint16_t* qT = ws;
@@ -493,8 +630,26 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, hipStream_t st) {
                        (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (const uint16_t*)a.out, a.lse,
                        (const uint16_t*)a.dout, a.n_q, a.n_k, a.k, a.sm_scale * LOG2E, a.sm_scale, g0,
                        (uint16_t*)a.dq, wp, wz);
-    hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3((unsigned)R), dim3(DKV_WAVES * 64), 0, st, qT, dT, a.idx, wp, wz,
-                       a.n_q, a.n_k, a.k, g0, a.dkv);
+    for (int64_t s0 = 0; s0 < R; s0 += DKV_ROWS) {
+      const int64_t Rs = R - s0 < DKV_ROWS ? R - s0 : DKV_ROWS;
+      const int64_t gs = g0 + s0;
+      // keys of the sequences rows gs .. gs + Rs - 1 belong to
+      const int64_t b_lo = gs / a.n_q, b_hi = (gs + Rs - 1) / a.n_q;
+      const int64_t kbase = b_lo * a.n_k, n_keys = (b_hi - b_lo + 1) * a.n_k;
+      hipLaunchKernelGGL(fill_zero_f32, dim3((unsigned)((n_keys + 1 + 255) / 256 < 65536 ? (n_keys + 1 + 255) / 256
+                                                                                           : 65536)),
+                         dim3(256), 0, st, (float*)off, n_keys + 1);
+      hipLaunchKernelGGL(mla_bwd_pairs<false>, dim3((unsigned)Rs), dim3(256), 0, st, a.idx, a.n_q, a.n_k, a.k, gs,
+                         kbase, off, perm);
+      hipLaunchKernelGGL(mla_bwd_scan, dim3(1), dim3(1024), 0, st, off, n_keys + 1);
+      hipLaunchKernelGGL(mla_bwd_pairs<true>, dim3((unsigned)Rs), dim3(256), 0, st, a.idx, a.n_q, a.n_k, a.k, gs,
+                         kbase, off, perm);
+      hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3((unsigned)Rs), dim3(DKV_WAVES * 64), 0, st,
+                         qT + s0 * (int64_t)MDQK * MH, dT + s0 * (int64_t)MDV * MH, a.idx, wp + s0 * (int64_t)a.k * MH,
+                         wz + s0 * (int64_t)a.k * MH, a.n_q, a.n_k, a.k, gs, contrib);
+      hipLaunchKernelGGL(mla_bwd_dkv_reduce, dim3((unsigned)((n_keys + 3) / 4)), dim3(256), 0, st, contrib, perm, off,
+                         n_keys, kbase, a.dkv);
+    }
   }
   return hipGetLastError();
 }

@@ -254,15 +254,29 @@ def test_training_stage_validation(L):
     assert call(do=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(out=None) == dsa.DSA_ERR_INVALID_ARG            # bf16 path needs the forward output
     assert call(v=FAKE) == dsa.DSA_ERR_UNSUPPORTED              # bf16 path: V inside kv
+    def bwd_ws(B, n_q, n_k, k):
+        # the documented layout: per pass of <= 4096 queries their q^T, dO^T, P and dZ (bf16);
+        # per dkv sub-pass of <= 2048 queries the fp32 contribution rows, the pair lists and
+        # the per-key list offsets over the sequences such a sub-pass can span
+        a256 = lambda x: (x + 255) // 256 * 256
+        rows = min(B * n_q, 4096)
+        rs = min(rows, 2048)
+        seqs = min(B, -(-rs // n_q) + 1)
+        return (a256(rows * (576 * 128 + 512 * 128 + 2 * k * 128) * 2) + a256(rs * k * 576 * 4)
+                + a256(rs * k * 4) + a256((seqs * n_k + 1) * 4))
     need = L.dsa_workspace_size(dsa.DSA_OP_MLA_BWD, 1, 4096, 4096, 128, 512, 2048, dsa.DSA_BF16)
-    assert need == 4096 * (576 * 128 + 512 * 128 + 2 * 2048 * 128) * 2
+    assert need == bwd_ws(1, 4096, 4096, 2048)
+    assert L.dsa_workspace_size(dsa.DSA_OP_MLA_BWD, 3, 1000, 5000, 128, 512, 256, dsa.DSA_BF16) == \
+        bwd_ws(3, 1000, 5000, 256)
     assert call() == dsa.DSA_ERR_WORKSPACE
     assert call(ws=FAKE + 8, wsb=need) == dsa.DSA_ERR_INVALID_ARG
     assert call(nk=1 << 23, ws=FAKE, wsb=need) == dsa.DSA_ERR_UNSUPPORTED   # 32-bit dkv offsets
     f32 = dict(dt=dsa.DSA_F32, H=4, dqk=64, dv=64, k=64, v=FAKE, out=None)
     assert call(**f32) == dsa.DSA_ERR_INVALID_ARG                # separate V needs d_v_out
-    # passes of at most 4096 queries bound the workspace
-    assert L.dsa_workspace_size(dsa.DSA_OP_MLA_BWD, 1, 131072, 131072, 128, 512, 2048, dsa.DSA_BF16) == need
+    # passes of at most 4096 queries (dkv sub-passes of at most 2048) bound the workspace;
+    # only the per-key offsets grow with the key count
+    assert L.dsa_workspace_size(dsa.DSA_OP_MLA_BWD, 1, 131072, 131072, 128, 512, 2048, dsa.DSA_BF16) == \
+        bwd_ws(1, 131072, 131072, 2048) == need + (131072 - 4096) * 4
 
 
 def test_dense_kl_validation(L):
