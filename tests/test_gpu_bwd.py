@@ -126,6 +126,14 @@ def test_backward_bf16_two_passes_and_batch():
     _bf16_case(2, 96, 1500, 128, seed=63)
 
 
+def test_backward_bf16_dkv_subpasses_across_sequences():
+    """B = 5 sequences of 900 queries: the key-gradient sub-passes of at most 2048 queries
+    (rows 0-2047, 2048-4095, then the second pass's 404) each span three sequences and
+    start or end inside one, so their key ranges and pair lists cover several sequences."""
+    _say("[sparse MLA backward, bf16] B=5, n_q=900, n_k=1200, k=32")
+    _bf16_case(5, 900, 1200, 32, seed=68)
+
+
 def test_backward_bf16_k2048_across_a_pass_boundary():
     """k = 2048 (the workload's k: 64 chunks per row, every iteration of the row scan, the
     full P / dZ workspace) over 4100 queries, so the second pass of at most 4096 queries
