@@ -461,6 +461,8 @@ __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
     const int bi = c & 1;
     if (c + 1 < n) stage_load(c + 1);
     __syncthreads();  // chunk c staged; chunk c-1's buffer free
+    const int32_t sid_l = sid[bi][l & 31];
+    const bool sok = sid_l >= 0 && (int64_t)sid_l < n_k;  // this lane's slot holds a valid key
 #pragma unroll
     for (int t = 0; t < DKV_MAXT; ++t) {
       const int j = wv + DKV_WAVES * t;
@@ -469,23 +471,24 @@ __global__ __launch_bounds__(DKV_WAVES * 64, 1) void mla_bwd_dkv_kernel(
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const v8bf az = *reinterpret_cast<const v8bf*>(&pz[bi][1][l & 31][16 * s + 8 * G]);
-        acc = mfma_bf16_32x32x16(az, Qt[t][s], acc);
+        acc = mfma_bf16_32x32x16(Qt[t][s], az, acc);
       }
       if (t < DKV_MAXT - 1) {  // j < 16: the V part
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const v8bf ap = *reinterpret_cast<const v8bf*>(&pz[bi][0][l & 31][16 * s + 8 * G]);
-          acc = mfma_bf16_32x32x16(ap, Dt[t][s], acc);
+          acc = mfma_bf16_32x32x16(Dt[t][s], ap, acc);
         }
       }
-      // lane: column 32j + l%32, rows (slots) 8(r/4) + 4G + r%4 of chunk c; each store
-      // instruction writes two 128-byte runs (one slot per half-wave)
-      const int col = 32 * j + (l & 31);
+      // The columns are the product's rows and the slots its columns (q^T / dO^T as the A
+      // operand, dZ / P as B; both operands have the same per-lane layout): lane l holds
+      // slot l%32 of chunk c at columns 32j + 8(r/4) + 4G + r%4, so each register quad is
+      // four consecutive columns, written with one 16-byte store.
+      if (sok) {
+        float* dst = crow + (int64_t)(c * KC + (l & 31)) * MDQK + 32 * j + 4 * G;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int slot = 8 * (r >> 2) + 4 * G + (r & 3);
-        const int32_t id = sid[bi][slot];
-        if (id >= 0 && (int64_t)id < n_k) crow[(int64_t)(c * KC + slot) * MDQK + col] = acc[r];
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<v4f*>(dst + 8 * q) = v4f{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
       }
     }
     if (c + 1 < n) stage_store(bi ^ 1);
