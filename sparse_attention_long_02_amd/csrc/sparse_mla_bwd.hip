@@ -29,8 +29,8 @@
 //         contributions (576 values) to the workspace, at the pair's (query, slot) place;
 //      c. mla_bwd_dkv_reduce: one wave per key sums the rows its list names and adds the
 //         sum to dkv (the only writer of that row in the sub-pass).
-//      The contributions are the same fp32 values the per-pair atomic adds carried before;
-//      only the order of the additions differs (the atomics' order was not fixed either).
+//      The contributions are exactly the fp32 values per-pair atomic adds into dkv would
+//      carry; only the order of the additions differs (and atomics fix no order either).
 #include "dsa_kernels.h"
 #include "mla_gather.h"
 
@@ -174,7 +174,8 @@ __device__ __forceinline__ int row_quad_off(int r, int j, int qq) {
 // Blocks are dispatched to the 8 XCDs round robin (block i on XCD i % 8).  This maps block
 // i to a logical index so that each XCD takes one contiguous eighth of [0, n): neighbouring
 // queries, which select many of the same keys, then share that XCD's L2 (for the gathered
-// rows and for the dkv lines the atomics update).  Identity when n is not a multiple of 8.
+// rows, and the q^T / dO^T rows of neighbouring queries).  Identity when n is not a
+// multiple of 8.
 __device__ __forceinline__ int64_t xcd_contiguous(int64_t i, int64_t n) {
   return (n & 7) ? i : (i & 7) * (n >> 3) + (i >> 3);
 }
