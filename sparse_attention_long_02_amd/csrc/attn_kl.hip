@@ -135,7 +135,7 @@ __device__ __forceinline__ void kl_gather(uint32_t buf, const uint16_t* __restri
               __builtin_amdgcn_readlane(id.lat, 6), __builtin_amdgcn_readlane(id.lat, 7)};
   ci.rope = id.rope;
 #pragma unroll
-  for (int j = 0; j < LOADS_PER_CHUNK; ++j) gather_load(j, ci, buf, kvb, n_k, wv, lane, ~0ull);
+  for (int j = 0; j < LOADS_PER_CHUNK; ++j) gather_load(j, ci, buf, kvb, n_k, wv, lane);
 }
 
 // grid.x = n_q, grid.y = B.  Chunk loop (c = 0 .. n-1, n = chunks up to the last valid id):

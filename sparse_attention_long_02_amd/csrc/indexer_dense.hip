@@ -74,7 +74,7 @@ __device__ __forceinline__ void dense_tile_load(uint32_t slot, const uint8_t* __
   for (int i = 0; i < 2; ++i) {
     const int64_t key = key0 + (d.off[i] >> 7);
     const int64_t kc = (key < n_keys ? key : n_keys - 1) * stride;
-    dma16_all(kb + row_of(kc) * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
+    dma16_vaddr(kb + row_of(kc) * IDX_DIM + (d.off[i] & 127u), slot + 2048 * wv + 1024 * i);
   }
   if (wv == 3) {
     const int64_t key = key0 + lane;

@@ -26,38 +26,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // lds + 16 i (a direct load the compiler can see would force every LDS wait behind it to
 // zero).  No register is written; one wait state separates the M0 write from the load that
 // reads it.  M0 holds nothing else in the kernels that use these loads, so clobbering it is
-// safe.  The exec mask is narrowed for the load and restored; the AND sets SCC, which is
-// therefore clobbered too.
+// safe.  Every active lane loads: a kernel that has nothing left to gather re-loads rows it
+// already has into a buffer no later read uses, which costs less than narrowing the exec
+// mask around each load.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16_saddr(const void* gbase, uint32_t voff, uint32_t lds, uint64_t on) {
-  uint64_t sv;
+__device__ __forceinline__ void dma16_saddr(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile(
-      "s_mov_b64 %0, exec\n\t"
-      "s_and_b64 exec, exec, %1\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %4\n\t"
-      "s_mov_b64 exec, %0"
-      : "=&s"(sv)
-      : "s"(on), "s"(lds), "v"(voff), "s"(gbase)
-      : "memory", "m0", "scc");
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds), "v"(voff), "s"(gbase)
+      : "memory", "m0");
 }
-__device__ __forceinline__ void dma16_vaddr(const void* gaddr, uint32_t lds, uint64_t on) {
-  uint64_t sv;
-  asm volatile(
-      "s_mov_b64 %0, exec\n\t"
-      "s_and_b64 exec, exec, %1\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, off\n\t"
-      "s_mov_b64 exec, %0"
-      : "=&s"(sv)
-      : "s"(on), "s"(lds), "v"(gaddr)
-      : "memory", "m0", "scc");
-}
-// The same for every active lane, without the exec mask.
-__device__ __forceinline__ void dma16_all(const void* gaddr, uint32_t lds) {
+__device__ __forceinline__ void dma16_vaddr(const void* gaddr, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"

@@ -70,28 +70,27 @@ __device__ __forceinline__ ChunkIds chunk_ids(const int32_t* ids, int c, int wv,
 // latent half as one wave-wide 1 KB load from a scalar row address, and their rope parts
 // as one instruction whose lane L loads unit (L%8) ^ swz of row 8w + L/8.
 // Load number j (0..7: latent half of row 8w + j; 8: the rope parts of rows 8w .. 8w+7)
-// of this wave's share of a chunk into the buffer at LDS address `buf`; `on` = 0 issues
-// nothing (no lanes active).
+// of this wave's share of a chunk into the buffer at LDS address `buf`.
 // Rows are `ld` elements apart (ld >= 576, a multiple of 8).
 __device__ __forceinline__ void gather_load(int j, const ChunkIds& ci, uint32_t buf, const uint16_t* __restrict__ kvb,
-                                            uint32_t n_k, int wv, int lane, uint64_t on, int64_t ld = MDQK) {
+                                            uint32_t n_k, int wv, int lane, int64_t ld = MDQK) {
   if (j < 8) {
     const int32_t id = j == 0 ? ci.a.x : j == 1 ? ci.a.y : j == 2 ? ci.a.z : j == 3 ? ci.a.w
                      : j == 4 ? ci.b.x : j == 5 ? ci.b.y : j == 6 ? ci.b.z : ci.b.w;
     const int r = 8 * wv + j;
     const uint32_t row = safe_row(__builtin_amdgcn_readfirstlane(id), n_k);
-    dma16_saddr(kvb + (size_t)row * ld, 16 * (lane ^ lat_swz(r)), buf + r * LAT_PITCH, on);
+    dma16_saddr(kvb + (size_t)row * ld, 16 * (lane ^ lat_swz(r)), buf + r * LAT_PITCH);
   } else {
     const int r = 8 * wv + (lane >> 3);
     const uint32_t row = safe_row(ci.rope, n_k);
-    dma16_vaddr(kvb + (size_t)row * ld + 512 + 8 * ((lane & 7) ^ rope_swz(r)), buf + LAT_BYTES + wv * 1024, on);
+    dma16_vaddr(kvb + (size_t)row * ld + 512 + 8 * ((lane & 7) ^ rope_swz(r)), buf + LAT_BYTES + wv * 1024);
   }
 }
 __device__ __forceinline__ void gather_chunk(uint32_t buf, const uint16_t* __restrict__ kvb, const int32_t* ids,
                                              int c, uint32_t n_k, int wv, int lane, int64_t ld = MDQK) {
   const ChunkIds ci = chunk_ids(ids, c, wv, lane);
 #pragma unroll
-  for (int j = 0; j < LOADS_PER_CHUNK; ++j) gather_load(j, ci, buf, kvb, n_k, wv, lane, ~0ull, ld);
+  for (int j = 0; j < LOADS_PER_CHUNK; ++j) gather_load(j, ci, buf, kvb, n_k, wv, lane, ld);
 }
 
 // A operand of S^T for d-step ds (values 16ds .. 16ds+15): row = key r = l%32, elements

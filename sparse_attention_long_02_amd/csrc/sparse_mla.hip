@@ -349,11 +349,10 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
         VMCNT(0);
         LGKM0();
         block_barrier();
-        // chunk c+2's loads go out one every four logit MFMAs (none past the last chunk)
+        // chunk c+2's loads go out one every four logit MFMAs; past the last chunk they load
+        // the last chunk's rows again into the buffer chunk c+2 would take, which no later
+        // step reads (cheaper than narrowing the exec mask around every load)
         const ChunkIds gi = chunk_ids(ids, c_lo + min(c + 2, n - 1), wv, l);
-        // (through a vector register and back, so that it is formed in scalar registers)
-        const uint32_t gon32 = __builtin_amdgcn_readfirstlane(opaque(c + 2 < n ? -1 : 0));
-        const uint64_t gon = ((uint64_t)gon32 << 32) | gon32;
         const uint32_t gbuf = lds_addr(bufs[(j + 2) % NBUF]);
         // online softmax of chunk c (base 2, lazily rescaled) interleaved with the logits
         // of chunk c+1 (formed from a stale buffer on the last chunk, and then unused):
@@ -377,7 +376,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
         for (int ds = 0; ds < PART1; ++ds) {
           S_next = mfma_bf16_32x32x16(kf[ds % KRING], Qt[ds], S_next);
           kf[ds % KRING] = k_frag(bn, k_off(ko, ds + KRING));
-          if (ds % 4 == 1) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon, ld_kv);
+          if (ds % 4 == 1) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, ld_kv);
         }
         float mx = fmaxf(fmaxf(S_cur[0], S_cur[1]), S_cur[2]);
 #pragma unroll
@@ -427,7 +426,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
         for (int ds = PART1; ds < D_STEPS; ++ds) {
           S_next = mfma_bf16_32x32x16(kf[ds % KRING], Qt[ds], S_next);
           if (ds + KRING < D_STEPS) kf[ds % KRING] = k_frag(bn, k_off(ko, ds + KRING));
-          if (ds % 4 == 1 && ds / 4 < LOADS_PER_CHUNK) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, gon, ld_kv);
+          if (ds % 4 == 1 && ds / 4 < LOADS_PER_CHUNK) gather_load(ds / 4, gi, gbuf, kvb, nk, wv, l, ld_kv);
         }
         const uint32_t bc = lds_addr(bufs[j]);
         pv_chunk(O, P0, P1, bc + opaque(vt_lane_offset(0)), bc + opaque(vt_lane_offset(1)));
@@ -436,6 +435,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void sparse_mla_bf16_kernel(
     }
   }
 
+  VMCNT(0);  // the loads issued past the last chunk have landed before the block ends
   // ---- epilogue: lane holds head 32w + l%32, values 32t + 8(r/4) + 4g + r%4
   o_guard(O);
   const int le = opaque(l);

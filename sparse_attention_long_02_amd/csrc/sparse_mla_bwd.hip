@@ -141,7 +141,7 @@ __device__ __forceinline__ void bwd_gather(uint32_t buf, const uint16_t* __restr
               __builtin_amdgcn_readlane(id.lat, 6), __builtin_amdgcn_readlane(id.lat, 7)};
   ci.rope = id.rope;
 #pragma unroll
-  for (int j = 0; j < LOADS_PER_CHUNK; ++j) gather_load(j, ci, buf, kvb, n_k, wv, lane, ~0ull);
+  for (int j = 0; j < LOADS_PER_CHUNK; ++j) gather_load(j, ci, buf, kvb, n_k, wv, lane);
 }
 
 __device__ __forceinline__ v8bf lds_v8bf(const uint8_t* buf, int off) {
